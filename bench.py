@@ -1,0 +1,293 @@
+"""Throughput of the fused LoRA linear forward and the pristine merge on one
+MI355X, with roofline fractions and the fp64 oracle timed on the host.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--only NAME]
+
+One step = one fused forward (tiled MFMA kernel) on the headline workload,
+bf16 X[4096,1024] (4 x 1024 tokens), W[1024,1024], A[16,1024], B[1024,16],
+r = 16, alpha = 32, fp32 accumulate, bf16 output; inputs resident in HBM.
+Printed: one JSON line (rank 0).  Besides the headline, "workloads" reports
+the other shapes of the same path measured in the same run: transformer
+projections (8192 tokens, hidden 2560, r = 32), the 16384 x 8192 x 8192
+square at r in {8, 16, 64, 128}, decode-shaped forwards (M in {1, 8, 64},
+W[4096,4096], rotated over 16 operand sets so the 256 MB last-level cache
+cannot hold them) and the merge of 36 layers x 7 targets at r = 32.
+
+--only NAME runs just one kernel a few times (for rocprofv3); NAME is one of
+cfg1, cfg2, q, v, sq8, sq16, sq64, sq128, dec1, dec8, dec64, merge, copy.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def _kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "rank_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(name, src_files, per_launch_units=1.0):
+    """HBM bytes per launch from the committed counter runs, if they were taken
+    on the kernel source as it is now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = data.get(name)
+    if not e or e.get("source_hash") != _kernel_source_hash(src_files):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """Per-launch HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, n):
+        import torch
+        self.s = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.e = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in zip(self.s, self.e)]
+
+
+def timed_launches(fn, steps, warmup):
+    """Run fn warmup times, then `steps` times with events around each launch
+    and around the whole region.  Returns (region_ms, per_launch_ms list)."""
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    t = Timer(steps)
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for i in range(steps):
+        t.s[i].record()
+        fn(i)
+        t.e[i].record()
+    r1.record()
+    torch.cuda.synchronize()
+    return r0.elapsed_time(r1), t.ms()
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+# ------------------------------------------------------------------ workloads
+
+def run_fwd_case(rg, c, steps, warmup, rotate=1, variant="auto"):
+    import torch
+    import synth
+    sets = [synth.fwd_case_on_device(
+        synth.FwdCase(c.name, c.cfg, c.case + 100 * i, c.M, c.N, c.K, c.r, c.alpha, c.dtype,
+                      var_b=c.var_b) if i else c) for i in range(rotate)]
+    outs = [torch.empty((c.M, c.N), dtype=sets[0]["X"].dtype, device="cuda") for _ in sets]
+
+    def fn(i):
+        s = sets[i % rotate]
+        rg.fwd(s["X"], s["W"], s["A"], s["B"], c.scale, out=outs[i % rotate], variant=variant)
+
+    region, per = timed_launches(fn, steps, warmup)
+    k_ms = sum(per) / len(per)
+    return {
+        "workload": c.name,
+        "variant": variant if variant != "auto" else ("decode" if rg.fwd_pick(
+            rg.LORA_BF16, c.M, c.N, c.K, c.r) == 2 else "tiled"),
+        "kernel_us_mean": round(k_ms * 1e3, 3),
+        "kernel_us_median": round(median(per) * 1e3, 3),
+        "tflops": round(c.flops() / (k_ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * c.flops() / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "gbs": round(c.bytes() / (k_ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * c.bytes() / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "operand_sets": rotate,
+    }
+
+
+def run_merge_pass(rg, steps, warmup, layers=36):
+    """All 36 x 7 targets, back to back on one stream; one pass = 252 launches."""
+    import torch
+    import synth
+    tg = synth.merge_targets(layers)
+    w0, a, b, wi = [], [], [], []
+    for t in tg:
+        w0.append(synth.device_normal(t.cfg, t.case, synth.TW, (t.N, t.K), t.var_w0, "bf16"))
+        a.append(synth.device_normal(t.cfg, t.case, synth.TA, (t.r, t.K), 1.0 / t.K, "bf16"))
+        b.append(synth.device_normal(t.cfg, t.case, synth.TB, (t.N, t.r), t.var_b, "bf16"))
+        wi.append(torch.empty_like(w0[-1]))
+
+    def one_pass(_):
+        for i, t in enumerate(tg):
+            rg.merge(w0[i], b[i], a[i], t.scale, out=wi[i])
+
+    region, per = timed_launches(one_pass, steps, warmup)
+    pass_ms = sum(per) / len(per)
+    total_bytes = sum(t.bytes() for t in tg)
+    # per-target-shape kernel times from a separate event-per-launch pass
+    shape_ms = {}
+    torch.cuda.synchronize()
+    for i, t in enumerate(tg[:7]):
+        _, ms = timed_launches(lambda _i, i=i, t=t: rg.merge(w0[i], b[i], a[i], t.scale, out=wi[i]),
+                               20, 3)
+        shape_ms[t.name.split(".")[1]] = {
+            "shape": [t.N, t.K], "kernel_us_mean": round(sum(ms) / len(ms) * 1e3, 2),
+            "gbs": round(t.bytes() / (sum(ms) / len(ms) * 1e-3) / 1e9, 1)}
+    return {
+        "workload": f"merge_from_pristine_{layers}x7_targets_r32",
+        "pass_ms_mean": round(pass_ms, 4),
+        "gbs": round(total_bytes / (pass_ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * total_bytes / (pass_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "bytes_per_pass": int(total_bytes),
+        "per_target_shape": shape_ms,
+    }
+
+
+def cpu_baseline(c, budget_s=10.0):
+    """The fp64 oracle, as it is, on the host cores: full passes of the
+    headline workload until the budget is spent."""
+    import oracle
+    t = c.make()
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    n, t0 = 0, time.time()
+    while True:
+        oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)
+        n += 1
+        if time.time() - t0 >= budget_s:
+            break
+    dt = time.time() - t0
+    return {"value": round(n * c.flops() / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} full fp64 oracle pass(es) of {c.name} ({c.flops() / 1e9:.3f} GFLOP "
+                      f"each) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--only", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_gemm_amd as rg
+    import synth
+
+    torch.cuda.set_device(0)
+    rg.lib()
+
+    if args.only:
+        return only(rg, args.only, args.steps, args.warmup)
+
+    head = synth.CFG2
+    t = head.make()
+
+    def dev(a):
+        import numpy as np
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    X, W, A, B = (dev(t[k]) for k in "XWAB")
+    Y = torch.empty((head.M, head.N), dtype=torch.bfloat16, device="cuda")
+
+    def step(_):
+        rg.fwd(X, W, A, B, head.scale, out=Y)
+
+    region_ms, per = timed_launches(step, args.steps, args.warmup)
+    ms_per_step = region_ms / args.steps
+    k_ms = sum(per) / len(per)
+    value = head.flops() / (ms_per_step * 1e-3) / 1e12
+    achieved = head.flops() / (k_ms * 1e-3) / 1e12
+    traffic = _traffic("fwd_tiled_cfg2", ["fwd_tiled.hip", "common.h"])
+
+    line = {
+        "metric": "fused LoRA fwd TFLOP/s (% bf16 MFMA peak); merge/decode GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs)",
+        "config": {"workload": head.name, "M": head.M, "N": head.N, "K": head.K, "r": head.r,
+                   "alpha": head.alpha, "accumulate": "fp32", "output": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_us_mean": round(k_ms * 1e3, 3),
+                     "algorithmic_flop_per_launch": head.flops()},
+    }
+
+    if not args.quick:
+        work = []
+        for c in (synth.CFG3_Q, synth.CFG3_V):
+            work.append(run_fwd_case(rg, c, 30, 5))
+        for c in synth.CFG3_SQ:
+            work.append(run_fwd_case(rg, c, 10, 2))
+        for c in synth.CFG4:
+            work.append(run_fwd_case(rg, c, 256, 32, rotate=16))
+        work.append(run_merge_pass(rg, 5, 1))
+        line["workloads"] = work
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(head)
+    print(json.dumps(line), flush=True)
+
+
+def only(rg, name, steps, warmup):
+    """One kernel, a few launches, for profiler runs."""
+    import torch
+    import synth
+    table = {"cfg1": synth.CFG1, "cfg2": synth.CFG2, "q": synth.CFG3_Q, "v": synth.CFG3_V,
+             "sq8": synth.CFG3_SQ[0], "sq16": synth.CFG3_SQ[1], "sq64": synth.CFG3_SQ[2],
+             "sq128": synth.CFG3_SQ[3], "dec1": synth.CFG4[0], "dec8": synth.CFG4[1],
+             "dec64": synth.CFG4[2]}
+    if name in table:
+        c = table[name]
+        rot = 16 if name.startswith("dec") else 1
+        res = run_fwd_case(rg, c, steps, warmup, rotate=rot)
+    elif name == "merge":
+        res = run_merge_pass(rg, steps, warmup)
+    elif name == "copy":
+        # Plain device copy of a known size: the reference for counter scaling.
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        region, per = timed_launches(lambda _: dst.copy_(src), steps, warmup)
+        res = {"workload": f"copy_{n}_bytes", "kernel_us_mean": sum(per) / len(per) * 1e3,
+               "gbs": 2 * n / (sum(per) / len(per) * 1e-3) / 1e9}
+    else:
+        raise SystemExit(f"unknown --only {name}")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

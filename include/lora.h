@@ -1,0 +1,146 @@
+/*
+ * lora.h -- C ABI of liblora.so: a fused LoRA linear forward and the merge of
+ * a LoRA adapter into a pristine copy of the base weight, on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Definitions (page titles as published):
+ *   [fastaf]  "fastaf: Minimal LoRA fine-tuning with hand-written Triton
+ *             kernels", section "FWD kernel speedup": one LoRA layer computes
+ *             out = X W^T + ((X A^T) B^T) * scale, scale = alpha / r, and the
+ *             fused kernel keeps the [tokens, r] intermediate X A^T on chip.
+ *   [unsloth] unsloth commit log for scripts/benchmarks/qwen3_flex_inference.py,
+ *             the entry that replaces copy+merge_adapter by one
+ *             addmm(pristine, B, A, alpha=scaling, out=W_inf) per layer: the
+ *             pristine weight is only read, W_inf is rewritten, accumulation
+ *             is fp32; rsLoRA folds alpha/sqrt(r) into the same scaling.
+ *
+ * Conventions shared by every entry point:
+ *   - Layouts follow nn.Linear: X[M,K] (tokens x d_in), W[N,K] (d_out x d_in),
+ *     A[r,K], B[N,r], Y[M,N]; row-major, unit inner stride, leading dimension
+ *     (ld*) in elements, ld >= row length.
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no memory and keeps no state between calls; it is reentrant.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued there and the call returns without synchronising:
+ *     LORA_OK means "validated and launched", not "finished".
+ *   - Every argument is validated on the host before any HIP call; on error
+ *     nothing is launched and nothing is written.
+ *   - One element type for all operands and the result (lora_dtype).
+ *     Accumulation is fp32; the result is rounded once, to nearest-even.
+ *   - LORA_BF16: pointers 16-byte aligned; K and the ld of X, W, A, W0 and
+ *     W_inf multiples of 8.  LORA_F32: pointers 16-byte aligned; K and those
+ *     ld multiples of 4.  N, r, ldb and ldy are unrestricted.
+ *   - Outputs must not overlap any input (LORA_ERR_ALIAS).
+ *   - NaN and Inf in the inputs propagate as IEEE arithmetic makes them.
+ */
+#ifndef LORA_H
+#define LORA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+
+typedef enum lora_status {
+    LORA_OK = 0,
+    LORA_ERR_NULL = 1,        /* a required pointer is NULL */
+    LORA_ERR_SHAPE = 2,       /* negative size, or r < 1 */
+    LORA_ERR_STRIDE = 3,      /* a leading dimension is smaller than its row */
+    LORA_ERR_ALIGN = 4,       /* pointer / K / ld alignment rule broken */
+    LORA_ERR_DTYPE = 5,       /* unknown lora_dtype */
+    LORA_ERR_ALIAS = 6,       /* an output overlaps an input */
+    LORA_ERR_UNSUPPORTED = 7, /* r > LORA_MAX_RANK, or a forced variant that
+                                 cannot run this shape */
+    LORA_ERR_HIP = 8          /* the HIP runtime reported a launch error */
+} lora_status;
+
+typedef enum lora_dtype {
+    LORA_F32 = 0,
+    LORA_BF16 = 1
+} lora_dtype;
+
+/* Forward variants.  AUTO picks DECODE for bf16 with M <= LORA_DECODE_MAX_M,
+ * TILED otherwise.  Forcing one is for tests and measurement. */
+typedef enum lora_variant {
+    LORA_VARIANT_AUTO = 0,
+    LORA_VARIANT_TILED = 1,   /* MFMA-tiled fused forward, any M */
+    LORA_VARIANT_DECODE = 2   /* weight-streaming forward, bf16, M <= 64 */
+} lora_variant;
+
+#define LORA_MAX_RANK 256
+#define LORA_DECODE_MAX_M 64
+
+/*
+ * lora_fwd -- fused LoRA linear forward   [fastaf], "FWD kernel speedup".
+ *
+ *   Y[m,n] = round( sum_k X[m,k] W[n,k] + scale * sum_j T[m,j] B[n,j] ),
+ *   T[m,j] = sum_k X[m,k] A[j,k]   (kept on chip, never stored to memory).
+ *
+ *   dtype         LORA_F32 or LORA_BF16 (operands and Y).
+ *   M, N, K, r    tokens, d_out, d_in, rank.  M == 0 or N == 0: no-op, LORA_OK.
+ *                 K == 0: Y = 0.  1 <= r <= LORA_MAX_RANK.
+ *   X, ldx        [M,K] activations.
+ *   W, ldw        [N,K] base weight.
+ *   A, lda        [r,K] down-projection (lora_A).
+ *   B, ldb        [N,r] up-projection (lora_B).
+ *   scale         alpha / r (or alpha / sqrt(r) for rsLoRA), used as given.
+ *   Y, ldy        [M,N] output, fully overwritten; must not overlap X/W/A/B.
+ *   stream        hipStream_t as void*.
+ * Returns a lora_status.
+ */
+int lora_fwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r,
+             const void *X, int64_t ldx, const void *W, int64_t ldw,
+             const void *A, int64_t lda, const void *B, int64_t ldb,
+             float scale, void *Y, int64_t ldy, void *stream);
+
+/*
+ * lora_fwd_variant -- lora_fwd with an explicit kernel choice (lora_variant).
+ * Same arguments, layouts and errors as lora_fwd; DECODE with dtype != bf16 or
+ * M > LORA_DECODE_MAX_M returns LORA_ERR_UNSUPPORTED.
+ */
+int lora_fwd_variant(int variant, int dtype, int64_t M, int64_t N, int64_t K, int64_t r,
+                     const void *X, int64_t ldx, const void *W, int64_t ldw,
+                     const void *A, int64_t lda, const void *B, int64_t ldb,
+                     float scale, void *Y, int64_t ldy, void *stream);
+
+/*
+ * lora_merge -- merge from pristine   [unsloth], addmm refresh entry.
+ *
+ *   W_inf[n,k] = round( W0[n,k] + scale * sum_j B[n,j] A[j,k] ),
+ *
+ * one pass: W0 is read once and never written, W_inf is written once and its
+ * previous content never read.  Repeated calls with the same inputs give
+ * bitwise-identical W_inf (no atomics, fixed summation order).
+ *
+ *   dtype         LORA_F32 or LORA_BF16 (all of W0, B, A, W_inf).
+ *   N, K, r       d_out, d_in, rank.  N == 0 or K == 0: no-op.  1 <= r <= 256.
+ *   W0, ldw0      [N,K] pristine base weight (read only).
+ *   B, ldb        [N,r] lora_B.
+ *   A, lda        [r,K] lora_A.
+ *   scale         the adapter's scaling, used as given.
+ *   W_inf, ldwi   [N,K] merged weight; must not overlap W0, B or A.
+ *   stream        hipStream_t as void*.
+ * Returns a lora_status.
+ */
+int lora_merge(int dtype, int64_t N, int64_t K, int64_t r,
+               const void *W0, int64_t ldw0, const void *B, int64_t ldb,
+               const void *A, int64_t lda, float scale,
+               void *W_inf, int64_t ldwi, void *stream);
+
+/* Static, NUL-terminated description of a lora_status value. */
+const char *lora_status_str(int status);
+
+/* LORA_ABI_VERSION of the loaded library. */
+int lora_abi_version(void);
+
+/* Variant lora_fwd would run for these sizes (a lora_variant, never AUTO). */
+int lora_fwd_pick(int dtype, int64_t M, int64_t N, int64_t K, int64_t r);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_H */

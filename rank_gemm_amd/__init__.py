@@ -1,0 +1,195 @@
+"""rank_gemm_amd -- Python binding of liblora.so, the MI355X (gfx950) fused
+LoRA linear forward and pristine merge.
+
+The binding only marshals arguments: every step of the computation runs in
+the library's HIP kernels.  There is no CPU fallback; if the library cannot be
+loaded, the first call raises.
+
+    Y = fwd(X, W, A, B, scale)          # X W^T + scale * (X A^T) B^T
+    merge(W0, B, A, scale, out=W_inf)   # W_inf = W0 + scale * B A, W0 untouched
+
+Tensors are torch tensors on the current HIP device, all bfloat16 or all
+float32, 2-D with unit inner stride (rows may be padded: the leading
+dimension is passed through).  Work is enqueued on torch's current stream.
+The C entry points of the same names are declared in include/lora.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+from . import build as _build
+
+LIB_PATH = _build.LIB
+
+LORA_OK = 0
+LORA_ERR_NULL = 1
+LORA_ERR_SHAPE = 2
+LORA_ERR_STRIDE = 3
+LORA_ERR_ALIGN = 4
+LORA_ERR_DTYPE = 5
+LORA_ERR_ALIAS = 6
+LORA_ERR_UNSUPPORTED = 7
+LORA_ERR_HIP = 8
+LORA_F32 = 0
+LORA_BF16 = 1
+VARIANTS = {"auto": 0, "tiled": 1, "decode": 2}
+MAX_RANK = 256
+DECODE_MAX_M = 64
+
+EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_status_str",
+           "lora_abi_version", "lora_fwd_pick")
+
+_lib = None
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded liblora.so (built in place first if it is not there)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        _build.build()
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    L.lora_fwd.argtypes = [i32, i64, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, f32, vp,
+                           i64, vp]
+    L.lora_fwd.restype = i32
+    L.lora_fwd_variant.argtypes = [i32] + L.lora_fwd.argtypes
+    L.lora_fwd_variant.restype = i32
+    L.lora_merge.argtypes = [i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, vp, i64, vp]
+    L.lora_merge.restype = i32
+    L.lora_status_str.argtypes = [i32]
+    L.lora_status_str.restype = ctypes.c_char_p
+    L.lora_abi_version.argtypes = []
+    L.lora_abi_version.restype = i32
+    L.lora_fwd_pick.argtypes = [i32, i64, i64, i64, i64]
+    L.lora_fwd_pick.restype = i32
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().lora_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().lora_abi_version())
+
+
+def fwd_pick(dtype: int, M: int, N: int, K: int, r: int) -> int:
+    return int(lib().lora_fwd_pick(dtype, M, N, K, r))
+
+
+def _check(status: int, what: str) -> None:
+    if status != LORA_OK:
+        raise LoraError(status, f"{what}: {status_str(status)}")
+
+
+# ---------------------------------------------------------------- raw ABI
+
+def fwd_raw(variant: int, dtype: int, M: int, N: int, K: int, r: int, X: int, ldx: int, W: int,
+            ldw: int, A: int, lda: int, B: int, ldb: int, scale: float, Y: int, ldy: int,
+            stream: int = 0) -> int:
+    """lora_fwd_variant with integer addresses; returns the lora_status."""
+    return int(lib().lora_fwd_variant(variant, dtype, M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb,
+                                      scale, Y, ldy, stream or None))
+
+
+def merge_raw(dtype: int, N: int, K: int, r: int, W0: int, ldw0: int, B: int, ldb: int, A: int,
+              lda: int, scale: float, Wi: int, ldwi: int, stream: int = 0) -> int:
+    """lora_merge with integer addresses; returns the lora_status."""
+    return int(lib().lora_merge(dtype, N, K, r, W0, ldw0, B, ldb, A, lda, scale, Wi, ldwi,
+                                stream or None))
+
+
+# ------------------------------------------------------------ torch-facing
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LORA_BF16
+    if t.dtype == torch.float32:
+        return LORA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _mat(t, name: str):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit inner stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    return t.data_ptr(), max(t.stride(0), t.shape[1], 1)
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd(X, W, A, B, scale: float, out=None, variant: str = "auto"):
+    """Fused LoRA forward ``Y = X W^T + scale * (X A^T) B^T`` on the GPU.
+
+    X[M,K], W[N,K], A[r,K], B[N,r]; returns Y[M,N] (``out`` if given).
+    """
+    import torch
+    M, K = X.shape
+    N = W.shape[0]
+    r = A.shape[0]
+    if W.shape[1] != K or A.shape[1] != K or tuple(B.shape) != (N, r):
+        raise ValueError(f"shape mismatch X{tuple(X.shape)} W{tuple(W.shape)} "
+                         f"A{tuple(A.shape)} B{tuple(B.shape)}")
+    dt = _dtype_code(X)
+    for t, nm in ((W, "W"), (A, "A"), (B, "B")):
+        if t.dtype != X.dtype or t.device != X.device:
+            raise ValueError(f"{nm} must match X in dtype and device")
+    if out is None:
+        out = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    elif tuple(out.shape) != (M, N) or out.dtype != X.dtype or out.device != X.device:
+        raise ValueError("out must be [M, N] with X's dtype and device")
+    px, ldx = _mat(X, "X")
+    pw, ldw = _mat(W, "W")
+    pa, lda = _mat(A, "A")
+    pb, ldb = _mat(B, "B")
+    py, ldy = _mat(out, "out")
+    st = fwd_raw(VARIANTS[variant], dt, M, N, K, r, px, ldx, pw, ldw, pa, lda, pb, ldb,
+                 float(scale), py, ldy, _stream(X.device))
+    _check(st, "lora_fwd")
+    return out
+
+
+def merge(W0, B, A, scale: float, out=None):
+    """Merge from pristine ``W_inf = W0 + scale * B A`` (W0 is never written).
+
+    W0[N,K], B[N,r], A[r,K]; returns W_inf[N,K] (``out`` if given).
+    """
+    import torch
+    N, K = W0.shape
+    r = A.shape[0]
+    if A.shape[1] != K or tuple(B.shape) != (N, r):
+        raise ValueError(f"shape mismatch W0{tuple(W0.shape)} B{tuple(B.shape)} A{tuple(A.shape)}")
+    dt = _dtype_code(W0)
+    for t, nm in ((B, "B"), (A, "A")):
+        if t.dtype != W0.dtype or t.device != W0.device:
+            raise ValueError(f"{nm} must match W0 in dtype and device")
+    if out is None:
+        out = torch.empty_like(W0)
+    elif tuple(out.shape) != (N, K) or out.dtype != W0.dtype or out.device != W0.device:
+        raise ValueError("out must be [N, K] with W0's dtype and device")
+    p0, ld0 = _mat(W0, "W0")
+    pb, ldb = _mat(B, "B")
+    pa, lda = _mat(A, "A")
+    po, ldo = _mat(out, "out")
+    st = merge_raw(dt, N, K, r, p0, ld0, pb, ldb, pa, lda, float(scale), po, ldo,
+                   _stream(W0.device))
+    _check(st, "lora_merge")
+    return out

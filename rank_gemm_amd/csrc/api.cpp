@@ -1,0 +1,155 @@
+// api.cpp -- the C ABI of liblora.so (declared in include/lora.h).
+//
+// Every entry point validates all of its arguments on the host and returns an
+// error before touching the HIP runtime; only then does it choose a kernel and
+// launch it on the caller's stream.  The library holds no device memory and no
+// state besides per-kernel launch attributes.
+#include "lora.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Byte range [lo, hi) touched by a row-major matrix of `rows` rows of `cols`
+// elements with leading dimension ld.
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t esz) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  if (rows <= 0 || cols <= 0) return {lo, lo};
+  return {lo, lo + static_cast<uintptr_t>(((rows - 1) * ld + cols) * esz)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+int esize(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
+
+// Checks shared by lora_fwd / lora_fwd_variant.
+int check_fwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void* X, int64_t ldx,
+              const void* W, int64_t ldw, const void* A, int64_t lda, const void* B, int64_t ldb,
+              void* Y, int64_t ldy) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || r < 1) return LORA_ERR_SHAPE;
+  if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
+  // Kernel index arithmetic is 32-bit per dimension.
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return LORA_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return LORA_OK;
+  if (Y == nullptr || B == nullptr) return LORA_ERR_NULL;
+  if (K > 0 && (X == nullptr || W == nullptr || A == nullptr)) return LORA_ERR_NULL;
+  if (ldx < K || ldw < K || lda < K || ldb < r || ldy < N) return LORA_ERR_STRIDE;
+  const int64_t e = esize(dtype);
+  const int64_t kal = dtype == LORA_BF16 ? 8 : 4;
+  if (K > 0) {
+    if (!aligned16(X) || !aligned16(W) || !aligned16(A)) return LORA_ERR_ALIGN;
+    if (K % kal || ldx % kal || ldw % kal || lda % kal) return LORA_ERR_ALIGN;
+  }
+  if ((reinterpret_cast<uintptr_t>(B) % e) || (reinterpret_cast<uintptr_t>(Y) % e))
+    return LORA_ERR_ALIGN;
+  const Range y = span(Y, M, N, ldy, e);
+  if (overlap(y, span(X, M, K, ldx, e)) || overlap(y, span(W, N, K, ldw, e)) ||
+      overlap(y, span(A, r, K, lda, e)) || overlap(y, span(B, N, r, ldb, e)))
+    return LORA_ERR_ALIAS;
+  return LORA_OK;
+}
+
+int pick(int dtype, int64_t M, int64_t r) {
+  if (dtype == LORA_BF16 && M <= LORA_DECODE_MAX_M && r <= lora::kDecodeMaxRank)
+    return LORA_VARIANT_DECODE;
+  return LORA_VARIANT_TILED;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+const char* lora_status_str(int s) {
+  switch (s) {
+    case LORA_OK: return "LORA_OK: validated and launched";
+    case LORA_ERR_NULL: return "LORA_ERR_NULL: a required pointer is NULL";
+    case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: negative size or rank < 1";
+    case LORA_ERR_STRIDE: return "LORA_ERR_STRIDE: leading dimension smaller than the row";
+    case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN: pointer, K or leading-dimension alignment";
+    case LORA_ERR_DTYPE: return "LORA_ERR_DTYPE: unknown element type";
+    case LORA_ERR_ALIAS: return "LORA_ERR_ALIAS: output overlaps an input";
+    case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED: rank or variant not supported";
+    case LORA_ERR_HIP: return "LORA_ERR_HIP: HIP launch error";
+    default: return "unknown lora_status";
+  }
+}
+
+int lora_fwd_pick(int dtype, int64_t M, int64_t N, int64_t K, int64_t r) {
+  (void)N;
+  (void)K;
+  return pick(dtype, M, r);
+}
+
+int lora_fwd_variant(int variant, int dtype, int64_t M, int64_t N, int64_t K, int64_t r,
+                     const void* X, int64_t ldx, const void* W, int64_t ldw, const void* A,
+                     int64_t lda, const void* B, int64_t ldb, float scale, void* Y, int64_t ldy,
+                     void* stream) {
+  if (variant != LORA_VARIANT_AUTO && variant != LORA_VARIANT_TILED &&
+      variant != LORA_VARIANT_DECODE)
+    return LORA_ERR_UNSUPPORTED;
+  const int st = check_fwd(dtype, M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, Y, ldy);
+  if (st != LORA_OK) return st;
+  if (variant == LORA_VARIANT_DECODE &&
+      (dtype != LORA_BF16 || M > LORA_DECODE_MAX_M || r > lora::kDecodeMaxRank))
+    return LORA_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return LORA_OK;
+  if (variant == LORA_VARIANT_AUTO) variant = pick(dtype, M, r);
+  const lora::FwdArgs a{M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, scale, Y, ldy};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == LORA_F32)
+    e = lora::launch_fwd_tiled_f32(a, s);
+  else if (variant == LORA_VARIANT_DECODE)
+    e = lora::launch_fwd_decode_bf16(a, s);
+  else
+    e = lora::launch_fwd_tiled_bf16(a, s);
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+int lora_fwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void* X, int64_t ldx,
+             const void* W, int64_t ldw, const void* A, int64_t lda, const void* B, int64_t ldb,
+             float scale, void* Y, int64_t ldy, void* stream) {
+  return lora_fwd_variant(LORA_VARIANT_AUTO, dtype, M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb,
+                          scale, Y, ldy, stream);
+}
+
+int lora_merge(int dtype, int64_t N, int64_t K, int64_t r, const void* W0, int64_t ldw0,
+               const void* B, int64_t ldb, const void* A, int64_t lda, float scale, void* W_inf,
+               int64_t ldwi, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (N < 0 || K < 0 || r < 1) return LORA_ERR_SHAPE;
+  if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
+  if (N > INT32_MAX / 2 || K > INT32_MAX / 2) return LORA_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return LORA_OK;
+  if (W0 == nullptr || B == nullptr || A == nullptr || W_inf == nullptr) return LORA_ERR_NULL;
+  if (ldw0 < K || ldwi < K || lda < K || ldb < r) return LORA_ERR_STRIDE;
+  const int64_t e = esize(dtype);
+  const int64_t kal = dtype == LORA_BF16 ? 8 : 4;
+  if (!aligned16(W0) || !aligned16(A) || !aligned16(W_inf)) return LORA_ERR_ALIGN;
+  if (K % kal || ldw0 % kal || ldwi % kal || lda % kal) return LORA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(B) % e) return LORA_ERR_ALIGN;
+  const Range wi = span(W_inf, N, K, ldwi, e);
+  if (overlap(wi, span(W0, N, K, ldw0, e)) || overlap(wi, span(A, r, K, lda, e)) ||
+      overlap(wi, span(B, N, r, ldb, e)))
+    return LORA_ERR_ALIAS;
+  const lora::MergeArgs a{N, K, r, W0, ldw0, B, ldb, A, lda, scale, W_inf, ldwi};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err =
+      dtype == LORA_BF16 ? lora::launch_merge_bf16(a, s) : lora::launch_merge_f32(a, s);
+  return err == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+}  // extern "C"

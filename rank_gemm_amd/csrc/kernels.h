@@ -1,0 +1,44 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (C++ linkage, internal
+// to liblora.so).  Arguments are validated by the C ABI layer before any of
+// these is called; the launchers only pick a tile configuration and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+struct FwdArgs {
+  int64_t M, N, K, r;
+  const void* X; int64_t ldx;
+  const void* W; int64_t ldw;
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  float scale;
+  void* Y; int64_t ldy;
+};
+
+struct MergeArgs {
+  int64_t N, K, r;
+  const void* W0; int64_t ldw0;
+  const void* B; int64_t ldb;
+  const void* A; int64_t lda;
+  float scale;
+  void* Wi; int64_t ldwi;
+};
+
+// Rank padded to the MFMA-friendly size the kernels are instantiated for.
+inline int pad_rank(int64_t r) {
+  return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : r <= 128 ? 128 : 256;
+}
+
+hipError_t launch_fwd_tiled_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_tiled_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_merge_bf16(const MergeArgs& a, hipStream_t s);
+hipError_t launch_merge_f32(const MergeArgs& a, hipStream_t s);
+
+// Largest rank the decode kernel is instantiated for.
+constexpr int kDecodeMaxRank = 32;
+
+}  // namespace lora

@@ -187,3 +187,38 @@ def merge_targets(layers: int = MERGE_LAYERS) -> List[MergeTarget]:
 
 
 FWD_CASES: List[FwdCase] = [CFG1, CFG2, CFG3_Q, CFG3_V, *CFG3_SQ, *CFG4]
+
+
+# ---------------------------------------------------------------------------
+# Device-side generation for throughput runs whose inputs are too large to
+# draw on the host in reasonable time (the 7.3 GB merge set, the square sweep).
+# Same distributions, a different generator: torch's Philox stream on the
+# device, seeded from (cfg, case, tensor).  Parity tests use the numpy recipe.
+# ---------------------------------------------------------------------------
+
+def device_seed(cfg: int, case: int, tensor: int) -> int:
+    return int(np.random.SeedSequence([cfg, case, tensor]).generate_state(1, np.uint64)[0]
+               & 0x7FFFFFFFFFFFFFFF)
+
+
+def device_normal(cfg: int, case: int, tensor: int, shape, var: float, dtype: str,
+                  device="cuda"):
+    """N(0, var) drawn on the device, fp32 then narrowed (bf16: nearest-even)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(cfg, case, tensor))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    x.mul_(math.sqrt(var))
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def fwd_case_on_device(c: FwdCase, device="cuda"):
+    vw = c.var_w if c.var_w is not None else 1.0 / c.K
+    va = c.var_a if c.var_a is not None else 1.0 / c.K
+    xc = c.x_from if c.x_from is not None else (c.cfg, c.case)
+    return {
+        "X": device_normal(xc[0], xc[1], TX, (c.M, c.K), c.var_x, c.dtype, device),
+        "W": device_normal(c.cfg, c.case, TW, (c.N, c.K), vw, c.dtype, device),
+        "A": device_normal(c.cfg, c.case, TA, (c.r, c.K), va, c.dtype, device),
+        "B": device_normal(c.cfg, c.case, TB, (c.N, c.r), c.var_b, c.dtype, device),
+    }

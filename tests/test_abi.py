@@ -1,0 +1,140 @@
+"""The C ABI library on the host: it loads, exports what include/lora.h
+declares, and rejects every invalid argument before any HIP call.
+
+No call here reaches a kernel launch: each one either fails validation or is
+an empty-shape no-op, so these tests run without a GPU.
+"""
+import os
+import re
+
+import pytest
+
+import rank_gemm_amd as rg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+# Fake, never dereferenced device addresses (16-byte aligned, far apart).
+PX, PW, PA, PB, PY = (0x10000000 * (i + 1) for i in range(5))
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(lora_\w+)\s*\(", src))
+
+
+def test_header_exports_match_library():
+    declared = _declared()
+    assert declared == set(rg.EXPORTS)
+    out = os.popen(f"nm -D --defined-only {rg.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT\s+(lora_\w+)", out))
+    assert declared <= exported, declared - exported
+
+
+def test_version_and_status_strings():
+    assert rg.abi_version() == 1
+    for s in range(9):
+        assert rg.status_str(s).startswith("LORA_")
+    assert "unknown" in rg.status_str(99)
+
+
+def test_variant_pick():
+    assert rg.fwd_pick(rg.LORA_BF16, 1, 4096, 4096, 16) == 2
+    assert rg.fwd_pick(rg.LORA_BF16, 64, 4096, 4096, 16) == 2
+    assert rg.fwd_pick(rg.LORA_BF16, 65, 4096, 4096, 16) == 1
+    assert rg.fwd_pick(rg.LORA_BF16, 8, 4096, 4096, 64) == 1      # rank above the decode kernel's
+    assert rg.fwd_pick(rg.LORA_F32, 8, 512, 512, 16) == 1
+
+
+def _fwd(**kw):
+    a = dict(variant=0, dtype=rg.LORA_BF16, M=64, N=64, K=64, r=16, X=PX, ldx=64, W=PW, ldw=64,
+             A=PA, lda=64, B=PB, ldb=16, scale=2.0, Y=PY, ldy=64)
+    a.update(kw)
+    return rg.fwd_raw(a["variant"], a["dtype"], a["M"], a["N"], a["K"], a["r"], a["X"], a["ldx"],
+                      a["W"], a["ldw"], a["A"], a["lda"], a["B"], a["ldb"], a["scale"], a["Y"],
+                      a["ldy"])
+
+
+def _merge(**kw):
+    a = dict(dtype=rg.LORA_BF16, N=64, K=64, r=16, W0=PW, ldw0=64, B=PB, ldb=16, A=PA, lda=64,
+             scale=2.0, Wi=PY, ldwi=64)
+    a.update(kw)
+    return rg.merge_raw(a["dtype"], a["N"], a["K"], a["r"], a["W0"], a["ldw0"], a["B"], a["ldb"],
+                        a["A"], a["lda"], a["scale"], a["Wi"], a["ldwi"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=7), rg.LORA_ERR_DTYPE),
+    (dict(M=-1), rg.LORA_ERR_SHAPE),
+    (dict(K=-8), rg.LORA_ERR_SHAPE),
+    (dict(r=0), rg.LORA_ERR_SHAPE),
+    (dict(r=257, ldb=257), rg.LORA_ERR_UNSUPPORTED),
+    (dict(variant=9), rg.LORA_ERR_UNSUPPORTED),
+    (dict(variant=2, M=65), rg.LORA_ERR_UNSUPPORTED),
+    (dict(variant=2, dtype=rg.LORA_F32), rg.LORA_ERR_UNSUPPORTED),
+    (dict(variant=2, r=33, ldb=33), rg.LORA_ERR_UNSUPPORTED),
+    (dict(X=0), rg.LORA_ERR_NULL),
+    (dict(W=0), rg.LORA_ERR_NULL),
+    (dict(A=0), rg.LORA_ERR_NULL),
+    (dict(B=0), rg.LORA_ERR_NULL),
+    (dict(Y=0), rg.LORA_ERR_NULL),
+    (dict(ldx=56), rg.LORA_ERR_STRIDE),
+    (dict(ldw=8), rg.LORA_ERR_STRIDE),
+    (dict(lda=63), rg.LORA_ERR_STRIDE),
+    (dict(ldb=15), rg.LORA_ERR_STRIDE),
+    (dict(ldy=63), rg.LORA_ERR_STRIDE),
+    (dict(K=60, ldx=64, ldw=64, lda=64), rg.LORA_ERR_ALIGN),        # bf16 needs K % 8 == 0
+    (dict(ldx=68), rg.LORA_ERR_ALIGN),
+    (dict(X=PX + 2), rg.LORA_ERR_ALIGN),
+    (dict(W=PW + 8), rg.LORA_ERR_ALIGN),
+    (dict(Y=PY + 1), rg.LORA_ERR_ALIGN),
+    (dict(dtype=rg.LORA_F32, K=62, ldx=64, ldw=64, lda=64), rg.LORA_ERR_ALIGN),
+    (dict(Y=PX), rg.LORA_ERR_ALIAS),
+    (dict(Y=PW + 64 * 63 * 2), rg.LORA_ERR_ALIAS),                 # overlaps W's last row
+    (dict(Y=PB - 64 * 63 * 2), rg.LORA_ERR_ALIAS),                 # Y's tail runs into B
+])
+def test_fwd_rejects_before_any_hip_call(kw, want):
+    assert _fwd(**kw) == want
+
+
+@pytest.mark.parametrize("kw", [dict(M=0), dict(N=0), dict(M=0, X=0, Y=0), dict(N=0, W=0, B=0)])
+def test_fwd_empty_is_noop(kw):
+    assert _fwd(**kw) == rg.LORA_OK
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=3), rg.LORA_ERR_DTYPE),
+    (dict(N=-1), rg.LORA_ERR_SHAPE),
+    (dict(r=0), rg.LORA_ERR_SHAPE),
+    (dict(r=300, ldb=300), rg.LORA_ERR_UNSUPPORTED),
+    (dict(W0=0), rg.LORA_ERR_NULL),
+    (dict(Wi=0), rg.LORA_ERR_NULL),
+    (dict(ldw0=32), rg.LORA_ERR_STRIDE),
+    (dict(ldwi=32), rg.LORA_ERR_STRIDE),
+    (dict(ldb=8), rg.LORA_ERR_STRIDE),
+    (dict(W0=PW + 2), rg.LORA_ERR_ALIGN),
+    (dict(Wi=PY + 4), rg.LORA_ERR_ALIGN),
+    (dict(K=12, ldw0=64, lda=64, ldwi=64), rg.LORA_ERR_ALIGN),
+    (dict(Wi=PW), rg.LORA_ERR_ALIAS),                                # in-place merge refused
+    (dict(Wi=PA + 64), rg.LORA_ERR_ALIAS),
+    (dict(Wi=PB - 96), rg.LORA_ERR_ALIAS),
+])
+def test_merge_rejects_before_any_hip_call(kw, want):
+    assert _merge(**kw) == want
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(K=0)])
+def test_merge_empty_is_noop(kw):
+    assert _merge(**kw) == rg.LORA_OK
+
+
+def test_torch_wrapper_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    X = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rg.fwd(X, torch.zeros(8, 8, dtype=torch.bfloat16), torch.zeros(2, 8, dtype=torch.bfloat16),
+               torch.zeros(8, 2, dtype=torch.bfloat16), 1.0)
+    with pytest.raises(TypeError):
+        rg.fwd(X.half(), torch.zeros(8, 8).half(), torch.zeros(2, 8).half(),
+               torch.zeros(8, 2).half(), 1.0)

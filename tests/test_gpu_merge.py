@@ -1,0 +1,169 @@
+"""Parity and invariants of the HIP merge from pristine against the fp64
+oracle, through the C ABI, on seeded inputs.
+
+Bar (bf16): relative Frobenius error <= 1e-2, and every element equal to the
+bf16 rounding of a value within the fp32-accumulation error bound of the
+exact result (|got - exact| <= ulp/2 + (r+2) 2^-24 (|W0| + |s| sum|B||A|)).
+That is the meaning of "within 1 bf16 ULP of an fp32-accumulating path" at
+weight magnitude; where W0 + s B A nearly cancels, the result is tiny and the
+same absolute error spans more ULPs of it, so the ULP distance to the
+correctly rounded value is reported (max, exact-match fraction) and bounded
+by 1 only away from such cancellation.  W0 bit-identical after 10
+perturb+merge cycles; re-merging the cycle-0 adapter reproduces the cycle-0
+W_inf bitwise; B = 0 or scale = 0 reproduce W0 bitwise.  fp32: relative
+Frobenius error <= 1e-5.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import (TOL, as_f64, merge_within_fp32_bound, rel_fro, to_dev, to_host,
+                     ulp_bf16_of, ulp_distance_bf16)
+
+pytestmark = pytest.mark.gpu
+
+LAYER0 = synth.merge_targets(1)
+
+
+def _merge(rg, W0, A, B, s, out=None):
+    import torch
+    Wi = rg.merge(W0, B, A, s, out=out)
+    torch.cuda.synchronize()
+    return Wi
+
+
+@pytest.mark.parametrize("tgt", LAYER0, ids=lambda t: t.name)
+def test_layer0_targets_parity(gpu_lib, tgt):
+    W0 = tgt.make_w0()
+    A, B = tgt.make_ab(0)
+    got = to_host(_merge(gpu_lib, to_dev(W0), to_dev(A), to_dev(B), tgt.scale))
+    Wd, Wb = oracle.merge(W0, B, A, tgt.scale)
+    _check_bf16_merge(got, Wd, Wb, W0, B, A, tgt.scale, tgt.r, tgt.name)
+
+
+def _check_bf16_merge(got, Wd, Wb, W0, B, A, s, r, name):
+    err = rel_fro(as_f64(got), Wd)
+    ulp = ulp_distance_bf16(got, Wb)
+    ok, delta = merge_within_fp32_bound(got, Wd, W0, B, A, s, r)
+    # away from cancellation (fp32 error below a quarter ulp) at most 1 ulp
+    calm = delta < 0.25 * ulp_bf16_of(Wd)
+    print(f"{name}: rel_fro={err:.3e} max_ulp={int(ulp.max())} "
+          f"max_ulp_away_from_cancellation={int(ulp[calm].max())} "
+          f"exact={float((ulp == 0).mean()):.6f} bound_ok={bool(ok.all())}")
+    assert err <= TOL["bf16"]
+    assert ok.all()
+    assert int(ulp[calm].max()) <= 1
+
+
+def test_ten_cycles_pristine_and_remerge(gpu_lib):
+    """Perturb+merge cycles with fresh adapters: W0 stays bit-identical, and
+    merging the cycle-0 adapter again reproduces cycle 0's W_inf bitwise."""
+    import torch
+    tg = LAYER0
+    w0_host = [t.make_w0() for t in tg]
+    w0_dev = [to_dev(w) for w in w0_host]
+    wi_dev = [torch.empty_like(w) for w in w0_dev]
+    first = None
+    for cycle in range(10):
+        for t, w0, wi in zip(tg, w0_dev, wi_dev):
+            A, B = t.make_ab(cycle)
+            gpu_lib.merge(w0, to_dev(B), to_dev(A), t.scale, out=wi)
+        torch.cuda.synchronize()
+        if cycle == 0:
+            first = [to_host(w) for w in wi_dev]
+    for w_host, w in zip(w0_host, w0_dev):
+        assert to_host(w).tobytes() == w_host.tobytes()
+    for t, w0, wi, ref in zip(tg, w0_dev, wi_dev, first):
+        A, B = t.make_ab(0)
+        gpu_lib.merge(w0, to_dev(B), to_dev(A), t.scale, out=wi)
+        torch.cuda.synchronize()
+        assert to_host(wi).tobytes() == ref.tobytes(), t.name
+
+
+@pytest.mark.parametrize("which", ["B0", "s0"])
+def test_zero_adapter_reproduces_pristine(gpu_lib, which):
+    t = LAYER0[1]
+    W0 = t.make_w0()
+    A, B = t.make_ab(0)
+    if which == "B0":
+        B = np.zeros_like(B)
+    s = 0.0 if which == "s0" else t.scale
+    got = to_host(_merge(gpu_lib, to_dev(W0), to_dev(A), to_dev(B), s))
+    assert got.tobytes() == W0.tobytes()
+
+
+RAGGED = [
+    # N, K, r, dtype
+    (1, 8, 1, "bf16"),
+    (37, 264, 7, "bf16"),
+    (100, 520, 32, "bf16"),
+    (33, 1000, 33, "bf16"),
+    (300, 256, 64, "bf16"),
+    (64, 776, 100, "bf16"),
+    (17, 272, 128, "bf16"),
+    (70, 520, 200, "bf16"),
+    (40, 264, 256, "bf16"),
+    (1024, 4096, 32, "bf16"),
+    (33, 100, 5, "f32"),
+    (64, 1028, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,K,r,dtype", RAGGED)
+def test_ragged_shapes(gpu_lib, N, K, r, dtype):
+    t = synth.MergeTarget(f"m{N}x{K}r{r}", 91, N * 3 + r, N, K, r, 2.0 * r, dtype)
+    W0 = t.make_w0()
+    A, B = t.make_ab(0)
+    got = to_host(_merge(gpu_lib, to_dev(W0), to_dev(A), to_dev(B), t.scale))
+    Wd, Wb = oracle.merge(W0, B, A, t.scale, want_bf16=(dtype == "bf16"))
+    if dtype == "bf16":
+        _check_bf16_merge(got, Wd, Wb, W0, B, A, t.scale, r, f"N{N} K{K} r{r}")
+    else:
+        err = rel_fro(as_f64(got), Wd)
+        print(f"N{N} K{K} r{r} {dtype}: rel_fro={err:.3e}")
+        assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_padded_leading_dimensions(gpu_lib, dtype):
+    import torch
+    N, K, r = 48, 264, 20
+    t = synth.MergeTarget("pad", 92, 0, N, K, r, 40.0, dtype)
+    W0 = t.make_w0()
+    A, B = t.make_ab(0)
+
+    def padded(a, p):
+        d = to_dev(a)
+        big = torch.zeros((d.shape[0], d.shape[1] + p), dtype=d.dtype, device=d.device)
+        big[:, : d.shape[1]] = d
+        return big[:, : d.shape[1]]
+
+    w0, a, b = padded(W0, 16), padded(A, 8), padded(B, 5)
+    big = torch.full((N, K + 8), float("nan"), dtype=w0.dtype, device=w0.device)
+    _merge(gpu_lib, w0, a, b, t.scale, out=big[:, :K])
+    got = to_host(big)
+    Wd, _ = oracle.merge(W0, B, A, t.scale, want_bf16=False)
+    assert rel_fro(as_f64(got[:, :K]), Wd) <= TOL[dtype]
+    assert np.isnan(as_f64(got[:, K:])).all()
+
+
+def test_deterministic(gpu_lib):
+    t = LAYER0[4]
+    W0 = t.make_w0()
+    A, B = t.make_ab(3)
+    w0, a, b = to_dev(W0), to_dev(A), to_dev(B)
+    x = to_host(_merge(gpu_lib, w0, a, b, t.scale))
+    y = to_host(_merge(gpu_lib, w0, a, b, t.scale))
+    assert x.tobytes() == y.tobytes()
+
+
+def test_rslora_scale_passed_through(gpu_lib):
+    """rsLoRA folds alpha / sqrt(r) into the scaling; the merge uses it as given."""
+    t = LAYER0[0]
+    W0 = t.make_w0()
+    A, B = t.make_ab(0)
+    s = 64.0 / np.sqrt(32.0)
+    got = to_host(_merge(gpu_lib, to_dev(W0), to_dev(A), to_dev(B), s))
+    Wd, Wb = oracle.merge(W0, B, A, s)
+    _check_bf16_merge(got, Wd, Wb, W0, B, A, s, t.r, "rslora")
