@@ -6,14 +6,17 @@
 // kernel speedup") in ONE launch: the base product, the rank-r
 // down-projection, the up-projection, the scale and the add all happen in one
 // workgroup per output tile, and the [tokens, r] intermediate never leaves the
-// chip (registers, then LDS for the operand re-layout).
+// chip (accumulator registers, then LDS for the operand re-layout).
 //
-// Per workgroup (BM x BN output tile, WM x WN waves, each wave TM x TN blocks
-// of 16 x 16):
-//   K loop (BK = 64, two LDS stages, register prefetch of the next stage):
-//     X[BM x 64], W[BN x 64], A[RP x 64] staged in LDS, rows of 128 B with the
-//     16-B chunks XOR-swizzled by (row & 7) so MFMA operand reads are free of
-//     bank conflicts;
+// Per workgroup (BM x BN output tile, WM x WN waves, each wave a grid of
+// 16 x 16 MFMA blocks):
+//   K loop, BK = 32 per stage, STAGES-deep ring of LDS stages:
+//     X[BM x 32], W[BN x 32] and A[RP x 32] go straight from global memory to
+//     LDS (buffer_load ... lds, 16 B per lane, no register staging).  Each
+//     buffer resource starts at the tile's first row and ends at the last
+//     valid row, so rows past M, N or r and the K tail read as zeros.
+//     Rows are 64 B; 16-B chunks are XOR-swizzled so that MFMA operand reads
+//     (16 rows x one chunk per instruction) hit distinct banks.
 //     acc[BM x BN] += X W^T          (MFMA)
 //     T[BM x RP]   += X A^T          (MFMA, reusing the X operand registers)
 //   epilogue:
@@ -26,112 +29,143 @@
 namespace lora {
 namespace {
 
-template <int WM_, int WN_, int TM_, int TN_, int RP_>
-struct Tiled {
-  static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, RP = RP_;
-  static constexpr int kThreads = WM * WN * kWave;
-  static constexpr int BM = WM * TM * 16;
-  static constexpr int BN = WN * TN * 16;
-  static constexpr int BK = 64;
-  static constexpr int RB = RP / 16;                 // 16-wide rank blocks
-  static constexpr int kRowB = BK * 2;               // bytes per staged row
-  static constexpr int kStageB = (BM + BN + RP) * kRowB;
-  static constexpr int kTS = RP + 8;                 // epilogue row stride (elements)
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int BK = 32;          // k per LDS stage
+constexpr int kRowB = BK * 2;   // bytes per staged row
+// Buffer offset for a lane that must read zeros: past every valid range.
+__device__ __forceinline__ uint32_t off_or_oob(bool in, uint32_t off) { return in ? off : 0x80000000u; }
+
+// 16-B chunk swizzle within a 64-B row.  For the 16 rows one operand read
+// touches, (row * 4 + chunk) takes 16 distinct values mod 16 and 8 distinct
+// values mod 8 within each half, so it is conflict-free whether the LDS
+// serves 8 lanes per 128 B or 16 lanes per 256 B.
+// Depends on row & 15 only, so a 1-KiB load (16 rows) can apply it from the
+// lane index alone.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row >> 3) & 1)) & 3; }
+__device__ __forceinline__ int stage_off(int row, int chunk) {
+  return row * kRowB + ((chunk ^ swz(row)) << 4);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_;
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = NW * kWave;
+  static constexpr int TM = BM / WM / 16;
+  static constexpr int TN = BN / WN / 16;
+  static constexpr int RB = RP / 16;
+  static constexpr int ROWS = BM + BN + RP;         // staged rows per stage
+  static constexpr int kStageB = ROWS * kRowB;
+  static constexpr int kXL = BM / 16 / NW;           // X loads (1 KiB each) per wave per stage
+  static constexpr int kWL = BN / 16 / NW;           // W loads per wave per stage
+  static constexpr int kAL = (RP / 16 + NW - 1) / NW;  // A load slots per wave per stage
+  static constexpr int kLoadsMin = kXL + kWL + (RP / 16) / NW;  // fewest any wave issues
+  static constexpr int kTS = RP + 8;                // epilogue T / B row stride (elements)
   static constexpr int kEpiB = (BM + BN) * kTS * 2;
-  static constexpr int kYS = BN + 8;                 // output staging row stride
+  static constexpr int kYS = BN + 8;                // output staging row stride (elements)
   static constexpr int kYB = BM * kYS * 2;
-  static constexpr int kLds = (2 * kStageB > kEpiB ? (2 * kStageB > kYB ? 2 * kStageB : kYB)
-                                                   : (kEpiB > kYB ? kEpiB : kYB));
-  static constexpr int kRowsPerPass = kThreads / 8;  // rows covered by one chunk pass
-  static constexpr int kXPass = BM / kRowsPerPass;
-  static constexpr int kWPass = BN / kRowsPerPass;
-  static constexpr int kAPass = (RP + kRowsPerPass - 1) / kRowsPerPass;
-  static constexpr int kTTiles = TM * RB;            // T tiles per wave row group
-  static constexpr int kTSlots = (kTTiles + WN - 1) / WN;
-  static_assert(BM % kRowsPerPass == 0 && BN % kRowsPerPass == 0, "tile rows per pass");
+  static constexpr int kLds = cmax(STAGES * kStageB, cmax(kEpiB, kYB));
+  static constexpr int kTSlots = (TM * RB + WN - 1) / WN;
+  static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiling");
+  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "X/W loads split evenly over waves");
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2, "ring depth");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// Issue one stage of direct-to-LDS loads for this wave: its X slots, its W
+// slots and (waves below RP / 16) its A slot.  Lanes whose 16-B chunk lies
+// past K read zeros.
+template <class C>
+__device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0, int K, int wave,
+                                            int lchunk, __amdgpu_buffer_rsrc_t rx,
+                                            __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
+                                            const uint32_t (&voffx)[C::kXL],
+                                            const uint32_t (&voffw)[C::kWL],
+                                            const uint32_t (&voffa)[C::kAL]) {
+  const bool kin = k0 + lchunk * 8 < K;
+  const uint32_t kb = (uint32_t)k0 * 2;
+  unsigned char* base = smem + buf * C::kStageB;
+#pragma unroll
+  for (int s = 0; s < C::kXL; ++s)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(base + (wave + s * C::NW) * 1024), 16,
+                                             off_or_oob(kin, voffx[s] + kb), 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < C::kWL; ++s)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rw, (lds_void*)(base + C::BM * kRowB + (wave + s * C::NW) * 1024), 16,
+        off_or_oob(kin, voffw[s] + kb), 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < C::kAL; ++s)
+    if (wave + s * C::NW < C::RP / 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_void*)(base + (C::BM + C::BN) * kRowB + (wave + s * C::NW) * 1024), 16,
+          off_or_oob(kin, voffa[s] + kb), 0, 0, 0);
+}
 
 template <class C>
-__global__ __launch_bounds__(C::kThreads) void fwd_tiled_bf16_kernel(
+__global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
     int64_t ldy, int tiles_m, int tiles_n, int y_vec) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int BM = C::BM, BN = C::BN, RP = C::RP, RB = C::RB, TM = C::TM, TN = C::TN;
-  constexpr int WN = C::WN;
+  constexpr int WN = C::WN, NW = C::NW, STAGES = C::STAGES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave / WN;
   const int wn = wave % WN;
+  const int lrow = lane & 15;
+  const int lk = lane >> 4;
 
   // ---- tile id: XCD-contiguous, then grouped along M for L2 reuse of W.
   const int total = tiles_m * tiles_n;
-  int pid = xcd_contiguous_id(blockIdx.x, total);
+  const int pid = xcd_contiguous_id(blockIdx.x, total);
   constexpr int kGroup = 8;
   const int group = pid / (kGroup * tiles_n);
   const int first_m = group * kGroup;
   const int gsize = min(tiles_m - first_m, kGroup);
-  const int tile_m = first_m + (pid % (kGroup * tiles_n)) % gsize;
-  const int tile_n = (pid % (kGroup * tiles_n)) / gsize;
-  const int m0 = tile_m * BM;
-  const int n0 = tile_n * BN;
+  const int local = pid % (kGroup * tiles_n);
+  const int m0 = (first_m + local % gsize) * BM;
+  const int n0 = (local / gsize) * BN;
 
-  // ---- per-thread global chunk sources (row clamped; K tail zero-filled).
-  const int crow = tid >> 3;  // row within a pass
-  const int cchk = tid & 7;   // 16-B chunk within the 64-wide k slab
-  const uint16_t* xsrc[C::kXPass];
-  const uint16_t* wsrc[C::kWPass];
-  const uint16_t* asrc[C::kAPass];
-#pragma unroll
-  for (int p = 0; p < C::kXPass; ++p) {
-    const int row = min(m0 + crow + p * C::kRowsPerPass, M - 1);
-    xsrc[p] = X + (int64_t)row * ldx + cchk * 8;
-  }
-#pragma unroll
-  for (int p = 0; p < C::kWPass; ++p) {
-    const int row = min(n0 + crow + p * C::kRowsPerPass, N - 1);
-    wsrc[p] = W + (int64_t)row * ldw + cchk * 8;
-  }
-#pragma unroll
-  for (int p = 0; p < C::kAPass; ++p) {
-    const int row = min(crow + p * C::kRowsPerPass, r - 1);
-    asrc[p] = A + (int64_t)row * lda + cchk * 8;
-  }
+  // ---- buffer resources from the tile's first row to its last valid row.
+  const int xrows = min(BM, M - m0);
+  const int wrows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + (int64_t)m0 * ldx), 0, (int)(xrows * ldx * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * ldw), 0, (int)(wrows * ldw * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)A, 0, (int)(r * lda * 2), 0x00020000);
 
-  u32x4 px[C::kXPass], pw[C::kWPass], pa[C::kAPass];
-  auto load_stage = [&](int k0) {
-    const bool kin = k0 + cchk * 8 < K;
+  // Lane i of a 1-KiB load writes staged row (16q + i/4), physical chunk
+  // i%4, so it fetches logical chunk (i%4) ^ swz(row).  Wave w issues X loads
+  // q = w, w + NW, ..., the same for W, and A load q = w when w < RP / 16.
+  const int lrow_in_load = lane >> 2;
+  const int lchunk = (lane & 3) ^ swz(lrow_in_load);
+  uint32_t voffx[C::kXL], voffw[C::kWL], voffa[C::kAL];
 #pragma unroll
-    for (int p = 0; p < C::kXPass; ++p)
-      px[p] = kin ? *reinterpret_cast<const u32x4*>(xsrc[p] + k0) : u32x4{0, 0, 0, 0};
+  for (int s = 0; s < C::kXL; ++s)
+    voffx[s] = (uint32_t)(((wave + s * NW) * 16 + lrow_in_load) * ldx * 2 + lchunk * 16);
 #pragma unroll
-    for (int p = 0; p < C::kWPass; ++p)
-      pw[p] = kin ? *reinterpret_cast<const u32x4*>(wsrc[p] + k0) : u32x4{0, 0, 0, 0};
+  for (int s = 0; s < C::kWL; ++s)
+    voffw[s] = (uint32_t)(((wave + s * NW) * 16 + lrow_in_load) * ldw * 2 + lchunk * 16);
 #pragma unroll
-    for (int p = 0; p < C::kAPass; ++p) {
-      const bool in = kin && (crow + p * C::kRowsPerPass < RP);
-      pa[p] = in ? *reinterpret_cast<const u32x4*>(asrc[p] + k0) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_stage = [&](int buf) {
-    unsigned char* base = smem + buf * C::kStageB;
-#pragma unroll
-    for (int p = 0; p < C::kXPass; ++p)
-      *reinterpret_cast<u32x4*>(base + swz(crow + p * C::kRowsPerPass, cchk)) = px[p];
-#pragma unroll
-    for (int p = 0; p < C::kWPass; ++p)
-      *reinterpret_cast<u32x4*>(base + BM * 128 + swz(crow + p * C::kRowsPerPass, cchk)) = pw[p];
-#pragma unroll
-    for (int p = 0; p < C::kAPass; ++p) {
-      const int row = crow + p * C::kRowsPerPass;
-      if (row < RP) *reinterpret_cast<u32x4*>(base + (BM + BN) * 128 + swz(row, cchk)) = pa[p];
-    }
-  };
+  for (int s = 0; s < C::kAL; ++s)
+    voffa[s] = (uint32_t)(((wave + s * NW) * 16 + lrow_in_load) * lda * 2 + lchunk * 16);
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -142,8 +176,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_tiled_bf16_kernel(
 #pragma unroll
   for (int s = 0; s < C::kTSlots; ++s) tacc[s] = zero4();
 
-  // Which rank blocks this wave works on (T tile (i, tj) belongs to wave
-  // (i * RB + tj) % WN of its wave row).
+  // T tile (i, tj) belongs to wave (i * RB + tj) % WN of its wave row.
   bool uses_tj[RB];
 #pragma unroll
   for (int tj = 0; tj < RB; ++tj) {
@@ -153,49 +186,58 @@ __global__ __launch_bounds__(C::kThreads) void fwd_tiled_bf16_kernel(
     uses_tj[tj] = u;
   }
 
-  const int nk = (K + C::BK - 1) / C::BK;
-  if (nk > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
-  __syncthreads();
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue_stage<C>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, voffx, voffw, voffa);
 
-  const int lrow = lane & 15;
-  const int lk = lane >> 4;
+  int buf = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load_stage((kt + 1) * C::BK);
-    const unsigned char* xs = smem + (kt & 1) * C::kStageB;
-    const unsigned char* ws = xs + BM * 128;
-    const unsigned char* as = ws + BN * 128;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int cc = kk * 4 + lk;
-      u32x4 a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(xs + swz(wm * TM * 16 + i * 16 + lrow, cc));
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(ws + swz(wn * TN * 16 + j * 16 + lrow, cc));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-#pragma unroll
-      for (int tj = 0; tj < RB; ++tj) {
-        if (!uses_tj[tj]) continue;
-        const u32x4 bt = *reinterpret_cast<const u32x4*>(as + swz(tj * 16 + lrow, cc));
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int idx = i * RB + tj;
-          if (idx % WN == wn) tacc[idx / WN] = mfma16x16x32(a[i], bt, tacc[idx / WN]);
-        }
+    // Stage kt has landed once at most (STAGES - 2) later stages are in flight.
+    // A bare s_barrier: each wave has waited for its own loads of stage kt,
+    // and the operand reads of stage kt-1 completed before the MFMAs that
+    // consumed them, so no fence (which would drain every in-flight stage)
+    // is needed here.
+    if (kt + STAGES - 2 < nk)
+      wait_vmcnt<(STAGES - 2) * C::kLoadsMin>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    {
+      const int nxt = kt + STAGES - 1;
+      if (nxt < nk) {
+        int nb = buf + STAGES - 1;
+        if (nb >= STAGES) nb -= STAGES;
+        issue_stage<C>(smem, nb, nxt * BK, K, wave, lchunk, rx, rw, ra, voffx, voffw, voffa);
       }
     }
-    if (more) store_stage((kt + 1) & 1);
-    __syncthreads();
+    const unsigned char* xs = smem + buf * C::kStageB;
+    const unsigned char* ws = xs + BM * kRowB;
+    const unsigned char* as = ws + BN * kRowB;
+    u32x4 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      a[i] = *reinterpret_cast<const u32x4*>(xs + stage_off(wm * TM * 16 + i * 16 + lrow, lk));
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off(wn * TN * 16 + j * 16 + lrow, lk));
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+#pragma unroll
+    for (int tj = 0; tj < RB; ++tj) {
+      if (!uses_tj[tj]) continue;
+      const u32x4 bt = *reinterpret_cast<const u32x4*>(as + stage_off(tj * 16 + lrow, lk));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int idx = i * RB + tj;
+        if (idx % WN == wn) tacc[idx / WN] = mfma16x16x32(a[i], bt, tacc[idx / WN]);
+      }
+    }
+    buf = buf + 1 == STAGES ? 0 : buf + 1;
   }
+  __syncthreads();
 
   // ---- epilogue 1: scaled T (bf16) and the B tile into LDS.
   uint16_t* ts = reinterpret_cast<uint16_t*>(smem);
@@ -213,7 +255,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_tiled_bf16_kernel(
         ts[row * C::kTS + j] = j < r ? f2bf(scale * tacc[idx / WN][q]) : uint16_t(0);
       }
     }
-  for (int e = tid; e < BN * RP; e += C::kThreads) {
+  for (int e = tid; e < BN * RP; e += C::NT) {
     const int n = e / RP, j = e % RP;
     uint16_t v = 0;
     if (j < r && n0 + n < N) v = B[(int64_t)(n0 + n) * ldb + j];
@@ -267,7 +309,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_tiled_bf16_kernel(
       }
   __syncthreads();
   constexpr int kCPR = BN / 8;  // 16-B chunks per output row
-  for (int e = tid; e < BM * kCPR; e += C::kThreads) {
+  for (int e = tid; e < BM * kCPR; e += C::NT) {
     const int row = e / kCPR, c = e % kCPR;
     const int gm = m0 + row, gn = n0 + c * 8;
     if (gm >= M || gn >= N) continue;
@@ -294,17 +336,28 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(C::kThreads), C::kLds, s, (int)a.M,
-                     (int)a.N, (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.X), a.ldx,
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(C::NT), C::kLds, s, (int)a.M, (int)a.N,
+                     (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.X), a.ldx,
                      static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
                      a.lda, static_cast<const uint16_t*>(a.B), a.ldb, a.scale,
                      static_cast<uint16_t*>(a.Y), a.ldy, tiles_m, tiles_n, y_vec);
   return hipGetLastError();
 }
 
+// Tile shapes.  Large: 256 x 256, 8 waves (2 x 4), wave tile 128 x 64.
+// Medium: 128 x 128, 4 waves (2 x 2), wave tile 64 x 64.
+template <int RP>
+using Big = Cfg<256, 256, 2, 4, RP, 4>;
+template <int RP>
+using Mid = Cfg<128, 128, 2, 2, RP, 4>;
+
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
-  return launch<Tiled<2, 2, 4, 4, RP>>(a, s);
+  const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if constexpr (RP <= 64) {
+    if (big_tiles >= 256) return launch<Big<RP>>(a, s);
+  }
+  return launch<Mid<RP>>(a, s);
 }
 
 }  // namespace
