@@ -10,12 +10,12 @@
 //
 // Per workgroup (BM x BN output tile, WM x WN waves, each wave a grid of
 // 16 x 16 MFMA blocks):
-//   K loop, BK = 32 per stage, STAGES-deep ring of LDS stages:
-//     X[BM x 32], W[BN x 32] and A[RP x 32] go straight from global memory to
+//   K loop, BK (32 or 64) per stage, STAGES-deep ring of LDS stages:
+//     X[BM x BK], W[BN x BK] and A[RP x BK] go straight from global memory to
 //     LDS (buffer_load ... lds, 16 B per lane, no register staging).  Each
 //     buffer resource starts at the tile's first row and ends at the last
 //     valid row, so rows past M, N or r and the K tail read as zeros.
-//     Rows are 64 B; 16-B chunks are XOR-swizzled so that MFMA operand reads
+//     16-B chunks are XOR-swizzled per row so that MFMA operand reads
 //     (16 rows x one chunk per instruction) hit distinct banks.
 //     acc[BM x BN] += X W^T          (MFMA)
 //     T[BM x RP]   += X A^T          (MFMA, reusing the X operand registers)
@@ -31,21 +31,25 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BK = 32;          // k per LDS stage
-constexpr int kRowB = BK * 2;   // bytes per staged row
+// LDS stage rows hold BK k-values (BK = 32: 64-B rows, 4 chunks of 16 B;
+// BK = 64: 128-B rows, 8 chunks).  The 16-B chunks are XOR-swizzled per row.
+// With the MFMA operand read pattern (16 consecutive rows at one logical chunk
+// per ds_read_b128) both layouts below measured free of LDS bank conflicts on
+// gfx950 (SQ_LDS_BANK_CONFLICT = 0), where e.g. chunk ^ (row & 3) on 64-B rows
+// is 2-way conflicted.  Both depend on row & 7 only, so a 1-KiB direct load
+// (16 or 8 rows) can apply them from the lane index alone.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (BK == 32) return (row >> 1) & 3;
+  return row & 7;
+}
+template <int BK>
+__device__ __forceinline__ int stage_off(int row, int chunk) {
+  return row * (BK * 2) + ((chunk ^ swz<BK>(row)) << 4);
+}
+
 // Buffer offset for a lane that must read zeros: past every valid range.
 __device__ __forceinline__ uint32_t off_or_oob(bool in, uint32_t off) { return in ? off : 0x80000000u; }
-
-// 16-B chunk swizzle within a 64-B row.  For the 16 rows one operand read
-// touches, (row * 4 + chunk) takes 16 distinct values mod 16 and 8 distinct
-// values mod 8 within each half, so it is conflict-free whether the LDS
-// serves 8 lanes per 128 B or 16 lanes per 256 B.
-// Depends on row & 15 only, so a 1-KiB load (16 rows) can apply it from the
-// lane index alone.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row >> 3) & 1)) & 3; }
-__device__ __forceinline__ int stage_off(int row, int chunk) {
-  return row * kRowB + ((chunk ^ swz(row)) << 4);
-}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
@@ -56,9 +60,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_>
+template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_, BK = BK_;
+  static constexpr int kRowB = BK * 2;                // bytes per staged row
+  static constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one 1-KiB wave load covers
+  static constexpr int kChunks = BK / 8;              // 16-B chunks per row
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * kWave;
   static constexpr int TM = BM / WM / 16;
@@ -66,21 +73,85 @@ struct Cfg {
   static constexpr int RB = RP / 16;
   static constexpr int ROWS = BM + BN + RP;         // staged rows per stage
   static constexpr int kStageB = ROWS * kRowB;
-  static constexpr int kXL = BM / 16 / NW;           // X loads (1 KiB each) per wave per stage
-  static constexpr int kWL = BN / 16 / NW;           // W loads per wave per stage
-  static constexpr int kAL = (RP / 16 + NW - 1) / NW;  // A load slots per wave per stage
-  static constexpr int kLoadsMin = kXL + kWL + (RP / 16) / NW;  // fewest any wave issues
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static constexpr int kXL = BM / kRowsPerLoad / NW;  // X loads (1 KiB each) per wave per stage
+  static constexpr int kWL = BN / kRowsPerLoad / NW;  // W loads per wave per stage
+  static constexpr int kAN = (RP + kRowsPerLoad - 1) / kRowsPerLoad;  // A loads per stage
+  static constexpr int kAL = (kAN + NW - 1) / NW;     // A load slots per wave per stage
+  static constexpr int kLoadsMin = kXL + kWL + kAN / NW;  // fewest any wave issues
   static constexpr int kTS = RP + 8;                // epilogue T / B row stride (elements)
   static constexpr int kEpiB = (BM + BN) * kTS * 2;
   static constexpr int kYS = BN + 8;                // output staging row stride (elements)
   static constexpr int kYB = BM * kYS * 2;
   static constexpr int kLds = cmax(STAGES * kStageB, cmax(kEpiB, kYB));
-  static constexpr int kTSlots = (TM * RB + WN - 1) / WN;
+  static constexpr int kTSlots = (TM * RB + WN - 1) / WN;  // T accumulators per wave
+  // T tile (i, tj) of a wave row belongs to wave (i * RB + tj) % WN.  With RB a
+  // multiple of WN a wave owns rank blocks tj = wn + u * WN for every i and keeps
+  // RB / WN A fragments; with WN a multiple of RB it owns rows
+  // i = wn / RB + s * (WN / RB) of rank block wn % RB and keeps one.
+  static constexpr bool kTByRank = RB % WN == 0;
+  static_assert(kTByRank || WN % RB == 0, "T tile ownership");
+  static constexpr int kTF = kTByRank ? RB / WN : 1;       // A fragments per wave
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiling");
-  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "X/W loads split evenly over waves");
+  static_assert(BM % (kRowsPerLoad * NW) == 0 && BN % (kRowsPerLoad * NW) == 0,
+                "X/W loads split evenly over waves");
   static_assert(kLds <= 160 * 1024, "LDS budget");
-  static_assert(STAGES >= 2, "ring depth");
+  static_assert(STAGES >= 3, "ring: one stage computed, one read, one in flight");
+  static_assert(BK == 32, "pipelined loop reads one k32 step per stage");
 };
+
+
+// Operand fragments of one k32 stage for one wave: X rows (a), W rows (b) and
+// the A rows (t) of the rank block(s) this wave owns.
+template <class C>
+struct Frags {
+  u32x4 a[C::TM];
+  u32x4 b[C::TN];
+  u32x4 t[C::kTF];
+};
+
+// Rank block held in A fragment u of wave wn.
+template <class C>
+__device__ __forceinline__ int t_block(int wn, int u) {
+  if constexpr (C::kTByRank) return wn + u * C::WN;
+  return wn % C::RB;
+}
+
+// Row block i of T slot s (for the rank-split case this depends on wn).
+template <class C>
+__device__ __forceinline__ int t_row_block(int wn, int s) {
+  if constexpr (C::kTByRank) return s / (C::RB / C::WN);
+  return wn / C::RB + s * (C::WN / C::RB);
+}
+
+// T slots of this wave += X rows x A rows.  When the wave splits by rank the
+// rows are compile-time; otherwise the wave-uniform q = wn / RB picks which
+// of WN / RB row blocks it owns (a uniform branch, kept out of the main MFMA
+// stream).
+template <class C>
+__device__ __forceinline__ void t_update(const Frags<C>& f, f32x4 (&tacc)[C::kTSlots], int wn) {
+  if constexpr (C::kTByRank) {
+#pragma unroll
+    for (int sl = 0; sl < C::kTSlots; ++sl)
+      tacc[sl] = mfma16x16x32(f.a[sl / (C::RB / C::WN)], f.t[sl % (C::RB / C::WN)], tacc[sl]);
+  } else {
+    constexpr int G = C::WN / C::RB;
+    const int q = wn / C::RB;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (q != g) continue;
+#pragma unroll
+      for (int sl = 0; sl < C::kTSlots; ++sl)
+        tacc[sl] = mfma16x16x32(f.a[sl * G + g], f.t[0], tacc[sl]);
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ int t_frag_of_slot(int s) {
+  if constexpr (C::kTByRank) return s % (C::RB / C::WN);
+  return 0;
+}
 
 // Issue one stage of direct-to-LDS loads for this wave: its X slots, its W
 // slots and (waves below RP / 16) its A slot.  Lanes whose 16-B chunk lies
@@ -95,6 +166,7 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
   const bool kin = k0 + lchunk * 8 < K;
   const uint32_t kb = (uint32_t)k0 * 2;
   unsigned char* base = smem + buf * C::kStageB;
+  constexpr int kRowB = C::kRowB;
 #pragma unroll
   for (int s = 0; s < C::kXL; ++s)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(base + (wave + s * C::NW) * 1024), 16,
@@ -106,7 +178,7 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
         off_or_oob(kin, voffw[s] + kb), 0, 0, 0);
 #pragma unroll
   for (int s = 0; s < C::kAL; ++s)
-    if (wave + s * C::NW < C::RP / 16)
+    if (wave + s * C::NW < C::kAN)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (lds_void*)(base + (C::BM + C::BN) * kRowB + (wave + s * C::NW) * 1024), 16,
           off_or_oob(kin, voffa[s] + kb), 0, 0, 0);
@@ -151,21 +223,22 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       (void*)A, 0, (int)(r * lda * 2), 0x00020000);
 
-  // Lane i of a 1-KiB load writes staged row (16q + i/4), physical chunk
-  // i%4, so it fetches logical chunk (i%4) ^ swz(row).  Wave w issues X loads
+  // Lane i of a 1-KiB load writes staged row (q * rows_per_load + i / chunks),
+  // physical chunk i % chunks, so it fetches logical chunk (i % chunks) ^ swz(row).  Wave w issues X loads
   // q = w, w + NW, ..., the same for W, and A load q = w when w < RP / 16.
-  const int lrow_in_load = lane >> 2;
-  const int lchunk = (lane & 3) ^ swz(lrow_in_load);
+  constexpr int BK = C::BK, kRowB = C::kRowB, kRPL = C::kRowsPerLoad;
+  const int lrow_in_load = lane / C::kChunks;
+  const int lchunk = (lane % C::kChunks) ^ swz<BK>(lrow_in_load);
   uint32_t voffx[C::kXL], voffw[C::kWL], voffa[C::kAL];
 #pragma unroll
   for (int s = 0; s < C::kXL; ++s)
-    voffx[s] = (uint32_t)(((wave + s * NW) * 16 + lrow_in_load) * ldx * 2 + lchunk * 16);
+    voffx[s] = (uint32_t)(((wave + s * NW) * kRPL + lrow_in_load) * ldx * 2 + lchunk * 16);
 #pragma unroll
   for (int s = 0; s < C::kWL; ++s)
-    voffw[s] = (uint32_t)(((wave + s * NW) * 16 + lrow_in_load) * ldw * 2 + lchunk * 16);
+    voffw[s] = (uint32_t)(((wave + s * NW) * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
 #pragma unroll
   for (int s = 0; s < C::kAL; ++s)
-    voffa[s] = (uint32_t)(((wave + s * NW) * 16 + lrow_in_load) * lda * 2 + lchunk * 16);
+    voffa[s] = (uint32_t)(((wave + s * NW) * kRPL + lrow_in_load) * lda * 2 + lchunk * 16);
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -176,66 +249,90 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
   for (int s = 0; s < C::kTSlots; ++s) tacc[s] = zero4();
 
-  // T tile (i, tj) belongs to wave (i * RB + tj) % WN of its wave row.
-  bool uses_tj[RB];
-#pragma unroll
-  for (int tj = 0; tj < RB; ++tj) {
-    bool u = false;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) u |= ((i * RB + tj) % WN) == wn;
-    uses_tj[tj] = u;
-  }
-
+  // K loop, software-pipelined three ways: iteration kt multiplies stage kt
+  // from registers, reads the operand fragments of stage kt+1 from LDS into
+  // a register ring (row i of the next stage lands in a[i] as soon as the
+  // MFMAs of row i have consumed it), and loads stage kt+STAGES-1 from global
+  // memory into the LDS ring.  Loads of stages past K read zeros, so the loop
+  // body has no branches and the scheduler can interleave its three streams.
   const int nk = (K + BK - 1) / BK;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue_stage<C>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, voffx, voffw, voffa);
+    issue_stage<C>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, voffx, voffw, voffa);
 
-  int buf = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt has landed once at most (STAGES - 2) later stages are in flight.
-    // A bare s_barrier: each wave has waited for its own loads of stage kt,
-    // and the operand reads of stage kt-1 completed before the MFMAs that
-    // consumed them, so no fence (which would drain every in-flight stage)
-    // is needed here.
-    if (kt + STAGES - 2 < nk)
-      wait_vmcnt<(STAGES - 2) * C::kLoadsMin>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    {
-      const int nxt = kt + STAGES - 1;
-      if (nxt < nk) {
-        int nb = buf + STAGES - 1;
-        if (nb >= STAGES) nb -= STAGES;
-        issue_stage<C>(smem, nb, nxt * BK, K, wave, lchunk, rx, rw, ra, voffx, voffw, voffa);
-      }
-    }
-    const unsigned char* xs = smem + buf * C::kStageB;
+  const int xrow0 = wm * TM * 16 + lrow;
+  const int wrow0 = wn * TN * 16 + lrow;
+  Frags<C> cur;
+  u32x4 bn[TN], tn[C::kTF];
+  wait_vmcnt<(STAGES - 2) * C::kLoadsMin>();
+  __builtin_amdgcn_s_barrier();
+  {
+    const unsigned char* xs = smem;
     const unsigned char* ws = xs + BM * kRowB;
     const unsigned char* as = ws + BN * kRowB;
-    u32x4 a[TM], b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      a[i] = *reinterpret_cast<const u32x4*>(xs + stage_off(wm * TM * 16 + i * 16 + lrow, lk));
+      cur.a[i] = *reinterpret_cast<const u32x4*>(xs + stage_off<BK>(xrow0 + i * 16, lk));
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off(wn * TN * 16 + j * 16 + lrow, lk));
+      cur.b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, lk));
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int u = 0; u < C::kTF; ++u)
+      cur.t[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk));
+  }
+
+  int rbuf = 1 % STAGES;              // ring slot holding stage kt+1
+  int wbuf = (STAGES - 1) % STAGES;   // ring slot to refill with stage kt+STAGES-1
+  for (int kt = 0; kt < nk; ++kt) {
+    // T MFMAs of stage kt first: they keep the MFMA pipe busy across the barrier.
+    t_update<C>(cur, tacc, wn);
+    // Stage kt+1 has landed once at most STAGES-3 later stages are in flight.
+    // The barrier is a bare s_barrier: each wave has waited for its own loads,
+    // and the slot refilled below held stage kt-1, whose fragments were
+    // consumed by MFMAs issued before it; a fence would drain every stage.
+    wait_vmcnt<(STAGES - 3) * C::kLoadsMin>();
+    __builtin_amdgcn_s_barrier();
+    issue_stage<C>(smem, wbuf, (kt + STAGES - 1) * BK, K, wave, lchunk, rx, rw, ra, voffx, voffw,
+                   voffa);
+    const unsigned char* xs = smem + rbuf * C::kStageB;
+    const unsigned char* ws = xs + BM * kRowB;
+    const unsigned char* as = ws + BN * kRowB;
+    // Next stage's W and A fragments go to separate registers; X fragments
+    // refill the ring after their row's MFMAs.  On the last iteration the
+    // reads repeat the stage in the slot (harmless, never used).
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+    for (int j = 0; j < TN; ++j)
+      bn[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, lk));
 #pragma unroll
-    for (int tj = 0; tj < RB; ++tj) {
-      if (!uses_tj[tj]) continue;
-      const u32x4 bt = *reinterpret_cast<const u32x4*>(as + stage_off(tj * 16 + lrow, lk));
+    for (int u = 0; u < C::kTF; ++u)
+      tn[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk));
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int idx = i * RB + tj;
-        if (idx % WN == wn) tacc[idx / WN] = mfma16x16x32(a[i], bt, tacc[idx / WN]);
-      }
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(cur.a[i], cur.b[j], acc[i][j]);
+      cur.a[i] = *reinterpret_cast<const u32x4*>(xs + stage_off<BK>(xrow0 + i * 16, lk));
     }
-    buf = buf + 1 == STAGES ? 0 : buf + 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) cur.b[j] = bn[j];
+#pragma unroll
+    for (int u = 0; u < C::kTF; ++u) cur.t[u] = tn[u];
+    // Interleave: DMA issues and LDS reads spread between the MFMAs.
+    constexpr int kDma = C::kXL + C::kWL;
+    constexpr int kReads = TN + C::kTF + TM;
+    constexpr int kMfma = TM * TN;
+#pragma unroll
+    for (int d = 0; d < kDma; ++d) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA) issue
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+#pragma unroll
+    for (int q = 0; q < kReads; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kDma - kReads > 0 ? kMfma - kDma - kReads : 0, 0);
+    rbuf = rbuf + 1 == STAGES ? 0 : rbuf + 1;
+    wbuf = wbuf + 1 == STAGES ? 0 : wbuf + 1;
   }
   __syncthreads();
 
@@ -243,18 +340,15 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   uint16_t* ts = reinterpret_cast<uint16_t*>(smem);
   uint16_t* bs = ts + BM * C::kTS;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int sl = 0; sl < C::kTSlots; ++sl) {
+    const int i = t_row_block<C>(wn, sl);
+    const int j = t_block<C>(wn, t_frag_of_slot<C>(sl)) * 16 + lrow;
 #pragma unroll
-    for (int tj = 0; tj < RB; ++tj) {
-      const int idx = i * RB + tj;
-      if (idx % WN != wn) continue;
-      const int j = tj * 16 + lrow;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wm * TM * 16 + i * 16 + lk * 4 + q;
-        ts[row * C::kTS + j] = j < r ? f2bf(scale * tacc[idx / WN][q]) : uint16_t(0);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int row = wm * TM * 16 + i * 16 + lk * 4 + q;
+      ts[row * C::kTS + j] = j < r ? f2bf(scale * tacc[sl][q]) : uint16_t(0);
     }
+  }
   for (int e = tid; e < BN * RP; e += C::NT) {
     const int n = e / RP, j = e % RP;
     uint16_t v = 0;
@@ -347,9 +441,9 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 // Tile shapes.  Large: 256 x 256, 8 waves (2 x 4), wave tile 128 x 64.
 // Medium: 128 x 128, 4 waves (2 x 2), wave tile 64 x 64.
 template <int RP>
-using Big = Cfg<256, 256, 2, 4, RP, 4>;
+using Big = Cfg<256, 256, 2, 4, RP, 4, 32>;
 template <int RP>
-using Mid = Cfg<128, 128, 2, 2, RP, 4>;
+using Mid = Cfg<128, 128, 2, 2, RP, 4, 32>;
 
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
