@@ -78,26 +78,31 @@ struct Cfg {
   static constexpr int kWL = BN / kRowsPerLoad / NW;  // W loads per wave per stage
   static constexpr int kAN = (RP + kRowsPerLoad - 1) / kRowsPerLoad;  // A loads per stage
   static constexpr int kAL = (kAN + NW - 1) / NW;     // A load slots per wave per stage
-  static constexpr int kLoadsMin = kXL + kWL + kAN / NW;  // fewest any wave issues
+  // Loads per stage: waves below kAN % NW issue one A load more than the rest.
+  static constexpr int kLoadsLo = kXL + kWL + kAN / NW;
+  static constexpr int kLoadsHi = kLoadsLo + (kAN % NW != 0 ? 1 : 0);
   static constexpr int kTS = RP + 8;                // epilogue T / B row stride (elements)
   static constexpr int kEpiB = (BM + BN) * kTS * 2;
   static constexpr int kYS = BN + 8;                // output staging row stride (elements)
   static constexpr int kYB = BM * kYS * 2;
   static constexpr int kLds = cmax(STAGES * kStageB, cmax(kEpiB, kYB));
   static constexpr int kTSlots = (TM * RB + WN - 1) / WN;  // T accumulators per wave
+  static constexpr int kGroup = 4;         // M tiles per group (XCD-contiguous ids)
+  static constexpr int kGroupShared = 16;  // M tiles swept together by all XCDs
   // T tile (i, tj) of a wave row belongs to wave (i * RB + tj) % WN.  With RB a
   // multiple of WN a wave owns rank blocks tj = wn + u * WN for every i and keeps
   // RB / WN A fragments; with WN a multiple of RB it owns rows
   // i = wn / RB + s * (WN / RB) of rank block wn % RB and keeps one.
   static constexpr bool kTByRank = RB % WN == 0;
-  static_assert(kTByRank || WN % RB == 0, "T tile ownership");
+  static_assert(kTByRank || (WN % RB == 0 && TM % (WN / RB) == 0), "T tile ownership");
+  static_assert((TM & (TM - 1)) == 0, "ring rotation needs a power-of-two row-block count");
   static constexpr int kTF = kTByRank ? RB / WN : 1;       // A fragments per wave
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiling");
   static_assert(BM % (kRowsPerLoad * NW) == 0 && BN % (kRowsPerLoad * NW) == 0,
                 "X/W loads split evenly over waves");
   static_assert(kLds <= 160 * 1024, "LDS budget");
-  static_assert(STAGES >= 3, "ring: one stage computed, one read, one in flight");
-  static_assert(BK == 32, "pipelined loop reads one k32 step per stage");
+  static_assert(STAGES >= 2, "ring: one stage being read, at least one in flight");
+  static_assert(BK == 32 || BK == 64, "one or two k32 substeps per stage");
 };
 
 
@@ -110,59 +115,81 @@ struct Frags {
   u32x4 t[C::kTF];
 };
 
-// Rank block held in A fragment u of wave wn.
+// T tile ownership.  T tiles of a wave row are (row block i, rank block tj),
+// i < TM, tj < RB, shared by the WN waves of the row.
+//  * RB a multiple of WN: wave wn owns rank blocks tj = wn + u * WN for all
+//    i; it keeps RB / WN A fragments.
+//  * WN a multiple of RB (G = WN / RB waves per rank block): wave wn owns
+//    rank block wn % RB for row blocks [q * TM / G, (q + 1) * TM / G),
+//    q = wn / RB; it keeps one A fragment.
+// Each wave keeps its X fragments in a ring rotated by rot(wn), so that the
+// row blocks it owns T tiles for sit in ring slots 0, 1, ... : every index
+// below is compile-time and the T MFMAs need no branches.
 template <class C>
-__device__ __forceinline__ int t_block(int wn, int u) {
-  if constexpr (C::kTByRank) return wn + u * C::WN;
+__device__ __forceinline__ int ring_rot(int wn) {
+  if constexpr (C::kTByRank) return 0;
+  return (wn / C::RB) * (C::TM / (C::WN / C::RB));
+}
+
+// Row block held in ring slot k.
+template <class C>
+__device__ __forceinline__ int ring_row_block(int k, int rot) { return (k + rot) & (C::TM - 1); }
+
+// Rank block held in A fragment f of wave wn.
+template <class C>
+__device__ __forceinline__ int t_block(int wn, int f) {
+  if constexpr (C::kTByRank) return wn + f * C::WN;
   return wn % C::RB;
 }
 
-// Row block i of T slot s (for the rank-split case this depends on wn).
+// T slot sl: ring slot of its X fragment and index of its A fragment.
 template <class C>
-__device__ __forceinline__ int t_row_block(int wn, int s) {
-  if constexpr (C::kTByRank) return s / (C::RB / C::WN);
-  return wn / C::RB + s * (C::WN / C::RB);
+__device__ __forceinline__ constexpr int t_ring_slot(int sl) {
+  if constexpr (C::kTByRank) return sl / (C::RB / C::WN);
+  return sl;
 }
-
-// T slots of this wave += X rows x A rows.  When the wave splits by rank the
-// rows are compile-time; otherwise the wave-uniform q = wn / RB picks which
-// of WN / RB row blocks it owns (a uniform branch, kept out of the main MFMA
-// stream).
 template <class C>
-__device__ __forceinline__ void t_update(const Frags<C>& f, f32x4 (&tacc)[C::kTSlots], int wn) {
-  if constexpr (C::kTByRank) {
-#pragma unroll
-    for (int sl = 0; sl < C::kTSlots; ++sl)
-      tacc[sl] = mfma16x16x32(f.a[sl / (C::RB / C::WN)], f.t[sl % (C::RB / C::WN)], tacc[sl]);
-  } else {
-    constexpr int G = C::WN / C::RB;
-    const int q = wn / C::RB;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (q != g) continue;
-#pragma unroll
-      for (int sl = 0; sl < C::kTSlots; ++sl)
-        tacc[sl] = mfma16x16x32(f.a[sl * G + g], f.t[0], tacc[sl]);
-    }
-  }
-}
-
-template <class C>
-__device__ __forceinline__ int t_frag_of_slot(int s) {
-  if constexpr (C::kTByRank) return s % (C::RB / C::WN);
+__device__ __forceinline__ constexpr int t_frag(int sl) {
+  if constexpr (C::kTByRank) return sl % (C::RB / C::WN);
   return 0;
 }
 
+template <class C>
+__device__ __forceinline__ void t_update_ab(const u32x4 (&a)[C::TM], const u32x4 (&t)[C::kTF],
+                                            f32x4 (&tacc)[C::kTSlots]) {
+#pragma unroll
+  for (int sl = 0; sl < C::kTSlots; ++sl)
+    tacc[sl] = mfma16x16x32(a[t_ring_slot<C>(sl)], t[t_frag<C>(sl)], tacc[sl]);
+}
+
+// Wait until this wave's loads of all but its `Newer` most recent stages have
+// landed.  Loads complete in issue order, so the count must be this wave's
+// own per-stage load count: waves that also load an A row issue one more.
+template <class C, int Newer>
+__device__ __forceinline__ void wait_stages(int wave) {
+  if constexpr (C::kLoadsHi != C::kLoadsLo) {
+    if (wave < C::kAN % C::NW) {
+      wait_vmcnt<Newer * C::kLoadsHi>();
+      return;
+    }
+  }
+  wait_vmcnt<Newer * C::kLoadsLo>();
+}
+
+// A wave-uniform value kept in a scalar register: stops loop-invariant code
+// motion from precomputing one vector offset per load slot.
+__device__ __forceinline__ uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Issue one stage of direct-to-LDS loads for this wave: its X slots, its W
-// slots and (waves below RP / 16) its A slot.  Lanes whose 16-B chunk lies
-// past K read zeros.
+// slots and (waves below kAN) its A slot.  Slot s of a matrix is the wave's
+// slot 0 plus s * NW 1-KiB loads, i.e. a wave-uniform byte stride.  Lanes
+// whose 16-B chunk lies past K read zeros.
 template <class C>
 __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0, int K, int wave,
                                             int lchunk, __amdgpu_buffer_rsrc_t rx,
                                             __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
-                                            const uint32_t (&voffx)[C::kXL],
-                                            const uint32_t (&voffw)[C::kWL],
-                                            const uint32_t (&voffa)[C::kAL]) {
+                                            uint32_t vx, uint32_t vw, uint32_t va, uint32_t sx,
+                                            uint32_t sw, uint32_t sa) {
   const bool kin = k0 + lchunk * 8 < K;
   const uint32_t kb = (uint32_t)k0 * 2;
   unsigned char* base = smem + buf * C::kStageB;
@@ -170,18 +197,18 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
 #pragma unroll
   for (int s = 0; s < C::kXL; ++s)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(base + (wave + s * C::NW) * 1024), 16,
-                                             off_or_oob(kin, voffx[s] + kb), 0, 0, 0);
+                                             off_or_oob(kin, vx + sgpr(s * sx + kb)), 0, 0, 0);
 #pragma unroll
   for (int s = 0; s < C::kWL; ++s)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rw, (lds_void*)(base + C::BM * kRowB + (wave + s * C::NW) * 1024), 16,
-        off_or_oob(kin, voffw[s] + kb), 0, 0, 0);
+        off_or_oob(kin, vw + sgpr(s * sw + kb)), 0, 0, 0);
 #pragma unroll
   for (int s = 0; s < C::kAL; ++s)
     if (wave + s * C::NW < C::kAN)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (lds_void*)(base + (C::BM + C::BN) * kRowB + (wave + s * C::NW) * 1024), 16,
-          off_or_oob(kin, voffa[s] + kb), 0, 0, 0);
+          off_or_oob(kin, va + sgpr(s * sa + kb)), 0, 0, 0);
 }
 
 template <class C>
@@ -189,7 +216,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
-    int64_t ldy, int tiles_m, int tiles_n, int y_vec) {
+    int64_t ldy, int tiles_m, int tiles_n, int y_vec, int map_xcd_n) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int BM = C::BM, BN = C::BN, RP = C::RP, RB = C::RB, TM = C::TM, TN = C::TN;
   constexpr int WN = C::WN, NW = C::NW, STAGES = C::STAGES;
@@ -202,16 +229,33 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int lrow = lane & 15;
   const int lk = lane >> 4;
 
-  // ---- tile id: XCD-contiguous, then grouped along M for L2 reuse of W.
-  const int total = tiles_m * tiles_n;
-  const int pid = xcd_contiguous_id(blockIdx.x, total);
-  constexpr int kGroup = 8;
-  const int group = pid / (kGroup * tiles_n);
-  const int first_m = group * kGroup;
-  const int gsize = min(tiles_m - first_m, kGroup);
-  const int local = pid % (kGroup * tiles_n);
-  const int m0 = (first_m + local % gsize) * BM;
-  const int n0 = (local / gsize) * BN;
+  // ---- tile id.  Workgroups reach the 8 XCDs round-robin (id % 8), and each
+  // XCD has its own L2.  When the N tiles split evenly over the XCDs, XCD x
+  // takes N tiles [x * tn/8, (x+1) * tn/8) and all XCDs sweep the same group
+  // of G M tiles at the same time: the X rows of the group are then shared
+  // by all XCDs through the last-level cache, and each L2 serves G M tiles x
+  // its N tiles.  Otherwise tiles are grouped along M (G at a time) within
+  // XCD-contiguous id ranges.
+  int m0, n0;
+  {
+    const int total = tiles_m * tiles_n;
+    if (map_xcd_n) {
+      constexpr int G = C::kGroupShared;
+      const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nper = tiles_n >> 3;
+      const int sg = slot / (G * nper), within = slot % (G * nper);
+      m0 = (sg * G + within % G) * BM;
+      n0 = (xcd * nper + within / G) * BN;
+    } else {
+      constexpr int G = C::kGroup;
+      const int pid = xcd_contiguous_id(blockIdx.x, total);
+      const int group = pid / (G * tiles_n);
+      const int first_m = group * G;
+      const int gsize = min(tiles_m - first_m, G);
+      const int local = pid % (G * tiles_n);
+      m0 = (first_m + local % gsize) * BM;
+      n0 = (local / gsize) * BN;
+    }
+  }
 
   // ---- buffer resources from the tile's first row to its last valid row.
   const int xrows = min(BM, M - m0);
@@ -229,16 +273,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   constexpr int BK = C::BK, kRowB = C::kRowB, kRPL = C::kRowsPerLoad;
   const int lrow_in_load = lane / C::kChunks;
   const int lchunk = (lane % C::kChunks) ^ swz<BK>(lrow_in_load);
-  uint32_t voffx[C::kXL], voffw[C::kWL], voffa[C::kAL];
-#pragma unroll
-  for (int s = 0; s < C::kXL; ++s)
-    voffx[s] = (uint32_t)(((wave + s * NW) * kRPL + lrow_in_load) * ldx * 2 + lchunk * 16);
-#pragma unroll
-  for (int s = 0; s < C::kWL; ++s)
-    voffw[s] = (uint32_t)(((wave + s * NW) * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
-#pragma unroll
-  for (int s = 0; s < C::kAL; ++s)
-    voffa[s] = (uint32_t)(((wave + s * NW) * kRPL + lrow_in_load) * lda * 2 + lchunk * 16);
+  const uint32_t vx = (uint32_t)((wave * kRPL + lrow_in_load) * ldx * 2 + lchunk * 16);
+  const uint32_t vw = (uint32_t)((wave * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
+  const uint32_t va = (uint32_t)((wave * kRPL + lrow_in_load) * lda * 2 + lchunk * 16);
+  const uint32_t sx = (uint32_t)(NW * kRPL * ldx * 2);  // byte stride between a wave's slots
+  const uint32_t sw = (uint32_t)(NW * kRPL * ldw * 2);
+  const uint32_t sa = (uint32_t)(NW * kRPL * lda * 2);
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -249,22 +289,27 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
   for (int s = 0; s < C::kTSlots; ++s) tacc[s] = zero4();
 
-  // K loop, software-pipelined three ways: iteration kt multiplies stage kt
-  // from registers, reads the operand fragments of stage kt+1 from LDS into
-  // a register ring (row i of the next stage lands in a[i] as soon as the
-  // MFMAs of row i have consumed it), and loads stage kt+STAGES-1 from global
-  // memory into the LDS ring.  Loads of stages past K read zeros, so the loop
-  // body has no branches and the scheduler can interleave its three streams.
+  // K loop, software-pipelined three ways.  A stage holds BK = 32 * NSUB
+  // k-values; the MFMAs consume it in NSUB substeps of k32.  Substep u of
+  // stage kt multiplies from registers while the fragments of the next
+  // substep are read from LDS into a register ring (row i lands in a[i] as
+  // soon as the MFMAs of row i have consumed it).  Before the last substep of
+  // stage kt the waves synchronise once: stage kt+1 has landed, and the slot
+  // of stage kt, all of whose fragments have now been read, is refilled with
+  // stage kt+STAGES from global memory.  Loads of stages past K read zeros, so
+  // the substeps have no branches and the scheduler can interleave their
+  // streams.
+  constexpr int NSUB = BK / 32;
   const int nk = (K + BK - 1) / BK;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    issue_stage<C>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, voffx, voffw, voffa);
+  for (int s = 0; s < STAGES; ++s)
+    issue_stage<C>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
 
-  const int xrow0 = wm * TM * 16 + lrow;
+  const int rot = ring_rot<C>(wn);
+  const int xrow0 = wm * TM * 16 + lrow;  // + 16 * ring_row_block(k) for ring slot k
   const int wrow0 = wn * TN * 16 + lrow;
   Frags<C> cur;
-  u32x4 bn[TN], tn[C::kTF];
-  wait_vmcnt<(STAGES - 2) * C::kLoadsMin>();
+  wait_stages<C, STAGES - 1>(wave);
   __builtin_amdgcn_s_barrier();
   {
     const unsigned char* xs = smem;
@@ -272,7 +317,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     const unsigned char* as = ws + BN * kRowB;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      cur.a[i] = *reinterpret_cast<const u32x4*>(xs + stage_off<BK>(xrow0 + i * 16, lk));
+      cur.a[i] = *reinterpret_cast<const u32x4*>(
+          xs + stage_off<BK>(xrow0 + ring_row_block<C>(i, rot) * 16, lk));
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       cur.b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, lk));
@@ -281,58 +327,84 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       cur.t[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk));
   }
 
-  int rbuf = 1 % STAGES;              // ring slot holding stage kt+1
-  int wbuf = (STAGES - 1) % STAGES;   // ring slot to refill with stage kt+STAGES-1
-  for (int kt = 0; kt < nk; ++kt) {
-    // T MFMAs of stage kt first: they keep the MFMA pipe busy across the barrier.
-    t_update<C>(cur, tacc, wn);
-    // Stage kt+1 has landed once at most STAGES-3 later stages are in flight.
-    // The barrier is a bare s_barrier: each wave has waited for its own loads,
-    // and the slot refilled below held stage kt-1, whose fragments were
-    // consumed by MFMAs issued before it; a fence would drain every stage.
-    wait_vmcnt<(STAGES - 3) * C::kLoadsMin>();
-    __builtin_amdgcn_s_barrier();
-    issue_stage<C>(smem, wbuf, (kt + STAGES - 1) * BK, K, wave, lchunk, rx, rw, ra, voffx, voffw,
-                   voffa);
-    const unsigned char* xs = smem + rbuf * C::kStageB;
+  // One substep: MFMAs from (a ring, bc, tc); the next substep's W and A
+  // fragments go to (bx, tx) and its X fragments refill the ring row by row.
+  // The two B/T register sets alternate between substeps, so no copies.
+  auto substep = [&](bool sync, int rslot, int nslot, int kt, int u, u32x4 (&bc)[TN],
+                     u32x4 (&tc)[C::kTF], u32x4 (&bx)[TN], u32x4 (&tx)[C::kTF]) {
+    // T MFMAs first: they keep the MFMA pipe busy across the barrier.
+    t_update_ab<C>(cur.a, tc, tacc);
+    if (sync) {
+      // Stage kt+1 has landed once at most STAGES-2 later stages are in
+      // flight; this wave's reads of stage kt are complete.  After the
+      // barrier every wave is past both.  A bare s_barrier: a fence would
+      // drain every stage in flight.
+      wait_stages<C, STAGES - 2>(wave);
+      __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      issue_stage<C>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx,
+                     sw, sa);
+    }
+    const unsigned char* xs = smem + (sync ? nslot : rslot) * C::kStageB;
     const unsigned char* ws = xs + BM * kRowB;
     const unsigned char* as = ws + BN * kRowB;
-    // Next stage's W and A fragments go to separate registers; X fragments
-    // refill the ring after their row's MFMAs.  On the last iteration the
-    // reads repeat the stage in the slot (harmless, never used).
+    const int cc = (sync ? 0 : (u + 1) * 4) + lk;  // logical 16-B chunk of the next substep
+    // After the final substep the reads fetch a zero stage (never used).
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bn[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, lk));
+      bx[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, cc));
 #pragma unroll
-    for (int u = 0; u < C::kTF; ++u)
-      tn[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk));
+    for (int f = 0; f < C::kTF; ++f)
+      tx[f] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, f) * 16 + lrow, cc));
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(cur.a[i], cur.b[j], acc[i][j]);
-      cur.a[i] = *reinterpret_cast<const u32x4*>(xs + stage_off<BK>(xrow0 + i * 16, lk));
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(cur.a[i], bc[j], acc[i][j]);
+      cur.a[i] = *reinterpret_cast<const u32x4*>(
+          xs + stage_off<BK>(xrow0 + ring_row_block<C>(i, rot) * 16, cc));
     }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) cur.b[j] = bn[j];
-#pragma unroll
-    for (int u = 0; u < C::kTF; ++u) cur.t[u] = tn[u];
-    // Interleave: DMA issues and LDS reads spread between the MFMAs.
+    // Interleave DMA issues and LDS reads between the MFMAs.
     constexpr int kDma = C::kXL + C::kWL;
     constexpr int kReads = TN + C::kTF + TM;
     constexpr int kMfma = TM * TN;
+    if (sync) {
 #pragma unroll
-    for (int d = 0; d < kDma; ++d) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA) issue
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    }
+      for (int d = 0; d < kDma; ++d) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA) issue
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
 #pragma unroll
-    for (int q = 0; q < kReads; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      for (int q = 0; q < kReads; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(
+          0x008, kMfma - kDma - kReads > 0 ? kMfma - kDma - kReads : 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kReads; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads > 0 ? kMfma - kReads : 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kDma - kReads > 0 ? kMfma - kDma - kReads : 0, 0);
-    rbuf = rbuf + 1 == STAGES ? 0 : rbuf + 1;
-    wbuf = wbuf + 1 == STAGES ? 0 : wbuf + 1;
+  };
+
+  u32x4 b2[TN], t2[C::kTF];
+  int rslot = 0;  // ring slot of stage kt
+  for (int kt = 0; kt < nk; ++kt) {
+    const int nslot = rslot + 1 == STAGES ? 0 : rslot + 1;  // slot of stage kt+1
+    if constexpr (NSUB == 2) {
+      substep(false, rslot, nslot, kt, 0, cur.b, cur.t, b2, t2);
+      substep(true, rslot, nslot, kt, 1, b2, t2, cur.b, cur.t);
+    } else {
+      substep(true, rslot, nslot, kt, 0, cur.b, cur.t, b2, t2);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) cur.b[j] = b2[j];
+#pragma unroll
+      for (int f = 0; f < C::kTF; ++f) cur.t[f] = t2[f];
+    }
+    rslot = nslot;
   }
   __syncthreads();
 
@@ -341,8 +413,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   uint16_t* bs = ts + BM * C::kTS;
 #pragma unroll
   for (int sl = 0; sl < C::kTSlots; ++sl) {
-    const int i = t_row_block<C>(wn, sl);
-    const int j = t_block<C>(wn, t_frag_of_slot<C>(sl)) * 16 + lrow;
+    const int i = ring_row_block<C>(t_ring_slot<C>(sl), rot);
+    const int j = t_block<C>(wn, t_frag<C>(sl)) * 16 + lrow;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = wm * TM * 16 + i * 16 + lk * 4 + q;
@@ -364,8 +436,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       u32x4 a[TM], b[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(ts + (wm * TM * 16 + i * 16 + lrow) * C::kTS +
-                                               kk * 32 + lk * 8);
+        a[i] = *reinterpret_cast<const u32x4*>(
+            ts + (wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow) * C::kTS + kk * 32 + lk * 8);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS +
@@ -379,7 +451,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     u32x2 a[TM], b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      a[i] = *reinterpret_cast<const u32x2*>(ts + (wm * TM * 16 + i * 16 + lrow) * C::kTS + lk * 4);
+      a[i] = *reinterpret_cast<const u32x2*>(
+          ts + (wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow) * C::kTS + lk * 4);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       b[j] = *reinterpret_cast<const u32x2*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS + lk * 4);
@@ -398,7 +471,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = wm * TM * 16 + i * 16 + lk * 4 + q;
+        const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lk * 4 + q;
         ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
       }
   __syncthreads();
@@ -422,6 +495,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
   const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
   const int y_vec = ((reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) && (a.ldy % 8 == 0);
+  const int map_xcd_n = (tiles_n % 8 == 0) && (tiles_m % C::kGroupShared == 0);
   auto kern = fwd_tiled_bf16_kernel<C>;
   static bool attr_done = false;
   if (!attr_done) {
@@ -434,14 +508,14 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
                      (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.X), a.ldx,
                      static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
                      a.lda, static_cast<const uint16_t*>(a.B), a.ldb, a.scale,
-                     static_cast<uint16_t*>(a.Y), a.ldy, tiles_m, tiles_n, y_vec);
+                     static_cast<uint16_t*>(a.Y), a.ldy, tiles_m, tiles_n, y_vec, map_xcd_n);
   return hipGetLastError();
 }
 
 // Tile shapes.  Large: 256 x 256, 8 waves (2 x 4), wave tile 128 x 64.
 // Medium: 128 x 128, 4 waves (2 x 2), wave tile 64 x 64.
 template <int RP>
-using Big = Cfg<256, 256, 2, 4, RP, 4, 32>;
+using Big = Cfg<256, 256, 2, 4, RP, 2, 64>;
 template <int RP>
 using Mid = Cfg<128, 128, 2, 2, RP, 4, 32>;
 
