@@ -55,36 +55,52 @@ def _traffic(name, src_files, per_launch_units=1.0):
     return e.get("hbm_bytes_per_launch")
 
 
-class Timer:
-    """Per-launch HIP events on the stream the kernels are launched on."""
-
-    def __init__(self, n):
-        import torch
-        self.s = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        self.e = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-
-    def ms(self):
-        return [a.elapsed_time(b) for a, b in zip(self.s, self.e)]
-
-
-def timed_launches(fn, steps, warmup):
-    """Run fn warmup times, then `steps` times with events around each launch
-    and around the whole region.  Returns (region_ms, per_launch_ms list)."""
+def timed_region(fn, steps, warmup):
+    """fn(i) for i < warmup untimed, then `steps` calls back to back between
+    two events on the launch stream; returns the region time in ms.  For
+    kernels longer than the host's per-call cost the stream stays busy, so
+    region / steps is the average launch duration."""
     import torch
-    for _ in range(warmup):
-        fn(0)
+    for i in range(warmup):
+        fn(i)
     torch.cuda.synchronize()
-    t = Timer(steps)
     r0 = torch.cuda.Event(enable_timing=True)
     r1 = torch.cuda.Event(enable_timing=True)
     r0.record()
     for i in range(steps):
-        t.s[i].record()
         fn(i)
-        t.e[i].record()
     r1.record()
     torch.cuda.synchronize()
-    return r0.elapsed_time(r1), t.ms()
+    return r0.elapsed_time(r1)
+
+
+def graph_region(fn, count, replays, warmup=1):
+    """Capture fn(0) .. fn(count - 1) into one HIP graph and time `replays`
+    replays between two events; returns ms per replay.  Used where one launch
+    is shorter than the host's per-call cost, so the device time is measured
+    rather than the Python dispatch rate."""
+    import torch
+    fn(0)  # first call outside capture (one-time kernel attribute set-up)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(count):
+                fn(i)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(replays):
+        g.replay()
+    r1.record()
+    torch.cuda.synchronize()
+    return r0.elapsed_time(r1) / replays
 
 
 def median(xs):
@@ -95,7 +111,10 @@ def median(xs):
 
 # ------------------------------------------------------------------ workloads
 
-def run_fwd_case(rg, c, steps, warmup, rotate=1, variant="auto"):
+def run_fwd_case(rg, c, steps, warmup, rotate=1, variant="auto", graph=False):
+    """One forward workload.  graph=True times `steps` launches (rotating over
+    `rotate` operand sets) captured in a HIP graph; else back-to-back eager
+    launches between region events."""
     import torch
     import synth
     sets = [synth.fwd_case_on_device(
@@ -107,14 +126,19 @@ def run_fwd_case(rg, c, steps, warmup, rotate=1, variant="auto"):
         s = sets[i % rotate]
         rg.fwd(s["X"], s["W"], s["A"], s["B"], c.scale, out=outs[i % rotate], variant=variant)
 
-    region, per = timed_launches(fn, steps, warmup)
-    k_ms = sum(per) / len(per)
+    if graph:
+        k_ms = graph_region(fn, steps, 3) / steps
+        eager_ms = timed_region(fn, steps, warmup) / steps
+    else:
+        k_ms = timed_region(fn, steps, warmup) / steps
+        eager_ms = k_ms
     return {
         "workload": c.name,
         "variant": variant if variant != "auto" else ("decode" if rg.fwd_pick(
             rg.LORA_BF16, c.M, c.N, c.K, c.r) == 2 else "tiled"),
+        "timing": "hip graph of back-to-back launches" if graph else "back-to-back launches",
         "kernel_us_mean": round(k_ms * 1e3, 3),
-        "kernel_us_median": round(median(per) * 1e3, 3),
+        "eager_us_per_call": round(eager_ms * 1e3, 3),
         "tflops": round(c.flops() / (k_ms * 1e-3) / 1e12, 2),
         "pct_bf16_peak": round(100 * c.flops() / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "gbs": round(c.bytes() / (k_ms * 1e-3) / 1e9, 1),
@@ -124,7 +148,9 @@ def run_fwd_case(rg, c, steps, warmup, rotate=1, variant="auto"):
 
 
 def run_merge_pass(rg, steps, warmup, layers=36):
-    """All 36 x 7 targets, back to back on one stream; one pass = 252 launches."""
+    """All 36 x 7 targets, back to back on one stream; one pass = 252 launches,
+    captured in a HIP graph (a launch of the small targets is shorter than the
+    host's per-call cost); the eager pass time is reported beside it."""
     import torch
     import synth
     tg = synth.merge_targets(layers)
@@ -135,25 +161,25 @@ def run_merge_pass(rg, steps, warmup, layers=36):
         b.append(synth.device_normal(t.cfg, t.case, synth.TB, (t.N, t.r), t.var_b, "bf16"))
         wi.append(torch.empty_like(w0[-1]))
 
-    def one_pass(_):
-        for i, t in enumerate(tg):
-            rg.merge(w0[i], b[i], a[i], t.scale, out=wi[i])
+    def launch(i):
+        t = tg[i]
+        rg.merge(w0[i], b[i], a[i], t.scale, out=wi[i])
 
-    region, per = timed_launches(one_pass, steps, warmup)
-    pass_ms = sum(per) / len(per)
+    pass_ms = graph_region(launch, len(tg), steps, warmup)
+    eager_ms = timed_region(lambda _: [launch(i) for i in range(len(tg))], steps, warmup) / steps
     total_bytes = sum(t.bytes() for t in tg)
-    # per-target-shape kernel times from a separate event-per-launch pass
+    # per-target-shape kernel times: one graph of that target in all layers
     shape_ms = {}
-    torch.cuda.synchronize()
     for i, t in enumerate(tg[:7]):
-        _, ms = timed_launches(lambda _i, i=i, t=t: rg.merge(w0[i], b[i], a[i], t.scale, out=wi[i]),
-                               20, 3)
+        ms = graph_region(lambda j, i=i: launch(i + 7 * j), layers, 5) / layers
         shape_ms[t.name.split(".")[1]] = {
-            "shape": [t.N, t.K], "kernel_us_mean": round(sum(ms) / len(ms) * 1e3, 2),
-            "gbs": round(t.bytes() / (sum(ms) / len(ms) * 1e-3) / 1e9, 1)}
+            "shape": [t.N, t.K], "kernel_us_mean": round(ms * 1e3, 2),
+            "gbs": round(t.bytes() / (ms * 1e-3) / 1e9, 1)}
     return {
         "workload": f"merge_from_pristine_{layers}x7_targets_r32",
+        "timing": "hip graph of the 252 launches",
         "pass_ms_mean": round(pass_ms, 4),
+        "eager_pass_ms": round(eager_ms, 4),
         "gbs": round(total_bytes / (pass_ms * 1e-3) / 1e9, 1),
         "pct_hbm_peak": round(100 * total_bytes / (pass_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "bytes_per_pass": int(total_bytes),
@@ -218,11 +244,12 @@ def main():
     def step(_):
         rg.fwd(X, W, A, B, head.scale, out=Y)
 
-    region_ms, per = timed_launches(step, args.steps, args.warmup)
+    # One step is one launch and the kernel outlasts the host's per-call cost,
+    # so region / steps is the kernel's average launch duration.
+    region_ms = timed_region(step, args.steps, args.warmup)
     ms_per_step = region_ms / args.steps
-    k_ms = sum(per) / len(per)
     value = head.flops() / (ms_per_step * 1e-3) / 1e12
-    achieved = head.flops() / (k_ms * 1e-3) / 1e12
+    achieved = value
     traffic = _traffic("fwd_tiled_cfg2", ["fwd_tiled.hip", "common.h"])
 
     line = {
@@ -242,7 +269,7 @@ def main():
                    "alpha": head.alpha, "accumulate": "fp32", "output": "bf16"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel_us_mean": round(k_ms * 1e3, 3),
+                     "traffic": traffic, "kernel_us_mean": round(ms_per_step * 1e3, 3),
                      "algorithmic_flop_per_launch": head.flops()},
     }
 
@@ -253,7 +280,7 @@ def main():
         for c in synth.CFG3_SQ:
             work.append(run_fwd_case(rg, c, 10, 2))
         for c in synth.CFG4:
-            work.append(run_fwd_case(rg, c, 256, 32, rotate=16))
+            work.append(run_fwd_case(rg, c, 256, 32, rotate=16, graph=True))
         work.append(run_merge_pass(rg, 5, 1))
         line["workloads"] = work
 
@@ -272,8 +299,8 @@ def only(rg, name, steps, warmup):
              "dec64": synth.CFG4[2]}
     if name in table:
         c = table[name]
-        rot = 16 if name.startswith("dec") else 1
-        res = run_fwd_case(rg, c, steps, warmup, rotate=rot)
+        dec = name.startswith("dec")
+        res = run_fwd_case(rg, c, steps, warmup, rotate=16 if dec else 1, graph=dec)
     elif name == "merge":
         res = run_merge_pass(rg, steps, warmup)
     elif name == "copy":
@@ -281,9 +308,9 @@ def only(rg, name, steps, warmup):
         n = 256 << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
-        region, per = timed_launches(lambda _: dst.copy_(src), steps, warmup)
-        res = {"workload": f"copy_{n}_bytes", "kernel_us_mean": sum(per) / len(per) * 1e3,
-               "gbs": 2 * n / (sum(per) / len(per) * 1e-3) / 1e9}
+        ms = timed_region(lambda _: dst.copy_(src), steps, warmup) / steps
+        res = {"workload": f"copy_{n}_bytes", "kernel_us_mean": ms * 1e3,
+               "gbs": 2 * n / (ms * 1e-3) / 1e9}
     else:
         raise SystemExit(f"unknown --only {name}")
     print(json.dumps(res), flush=True)

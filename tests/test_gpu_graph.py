@@ -1,0 +1,60 @@
+"""The C-ABI launches replayed from a HIP graph give the eager results
+bitwise, replay after replay, with eager work and synchronisations between
+the replays (the library records only kernel launches, no memsets)."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays_match_eager(launch, outs, replays=3):
+    import torch
+    launch()
+    torch.cuda.synchronize()
+    eager = [to_host(o).copy() for o in outs]
+    for o in outs:
+        o.fill_(float("nan"))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            launch()
+    torch.cuda.synchronize()
+    for k in range(replays):
+        for o in outs:
+            o.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert to_host(o).tobytes() == e.tobytes(), f"replay {k}"
+
+
+@pytest.mark.parametrize("M", [1, 64, 300])
+def test_fwd_graph_replay(gpu_lib, M):
+    import torch
+    c = synth.FwdCase(f"g{M}", 97, M, M, 1024, 768, 16, 32.0, "bf16")
+    t = c.make()
+    X, W, A, B = (to_dev(t[k]) for k in "XWAB")
+    Y = torch.empty((M, c.N), dtype=torch.bfloat16, device="cuda")
+    _replays_match_eager(lambda: gpu_lib.fwd(X, W, A, B, c.scale, out=Y), [Y])
+
+
+def test_merge_graph_replay(gpu_lib):
+    import torch
+    tg = synth.merge_targets(1)[:3]
+    ins, outs = [], []
+    for t in tg:
+        A, B = t.make_ab(0)
+        ins.append((to_dev(t.make_w0()), to_dev(B), to_dev(A), t.scale))
+        outs.append(torch.empty((t.N, t.K), dtype=torch.bfloat16, device="cuda"))
+
+    def launch():
+        for (w0, b, a, s), o in zip(ins, outs):
+            gpu_lib.merge(w0, b, a, s, out=o)
+
+    _replays_match_eager(launch, outs)
