@@ -216,7 +216,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
-    int64_t ldy, int tiles_m, int tiles_n, int y_vec, int map_xcd_n) {
+    int64_t ldy, int tiles_m, int tiles_n, int y_vec, int map_mode) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int BM = C::BM, BN = C::BN, RP = C::RP, RB = C::RB, TM = C::TM, TN = C::TN;
   constexpr int WN = C::WN, NW = C::NW, STAGES = C::STAGES;
@@ -230,21 +230,27 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int lk = lane >> 4;
 
   // ---- tile id.  Workgroups reach the 8 XCDs round-robin (id % 8), and each
-  // XCD has its own L2.  When the N tiles split evenly over the XCDs, XCD x
-  // takes N tiles [x * tn/8, (x+1) * tn/8) and all XCDs sweep the same group
-  // of G M tiles at the same time: the X rows of the group are then shared
-  // by all XCDs through the last-level cache, and each L2 serves G M tiles x
-  // its N tiles.  Otherwise tiles are grouped along M (G at a time) within
-  // XCD-contiguous id ranges.
+  // XCD has its own L2.  Mode 1: XCD x takes N tiles [x * tn/8, (x+1) * tn/8)
+  // and all XCDs sweep the same group of G M tiles at the same time, so the X
+  // rows of the group are shared by all XCDs through the last-level cache and
+  // each L2 serves G M tiles x its N tiles.  Mode 2, the transpose: XCD x
+  // takes M tiles [x * tm/8, (x+1) * tm/8) and sweeps the N tiles with all of
+  // them at once (W shared through the last-level cache).  The host picks the
+  // mode with fewer L2 fills.  Mode 0: tiles grouped along M (G at a time)
+  // within XCD-contiguous id ranges.
   int m0, n0;
   {
     const int total = tiles_m * tiles_n;
-    if (map_xcd_n) {
+    if (map_mode == 1) {
       constexpr int G = C::kGroupShared;
       const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nper = tiles_n >> 3;
       const int sg = slot / (G * nper), within = slot % (G * nper);
       m0 = (sg * G + within % G) * BM;
       n0 = (xcd * nper + within / G) * BN;
+    } else if (map_mode == 2) {
+      const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, mper = tiles_m >> 3;
+      m0 = (xcd * mper + slot % mper) * BM;
+      n0 = (slot / mper) * BN;
     } else {
       constexpr int G = C::kGroup;
       const int pid = xcd_contiguous_id(blockIdx.x, total);
@@ -495,7 +501,20 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
   const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
   const int y_vec = ((reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) && (a.ldy % 8 == 0);
-  const int map_xcd_n = (tiles_n % 8 == 0) && (tiles_m % C::kGroupShared == 0);
+  // L2 fills (in K-rows of X or W) of the two XCD-split mappings: mode 1
+  // reads all of X on every XCD and W once per group of G M tiles; mode 2
+  // reads all of W on every XCD and X once per N sweep step (32 resident
+  // tiles per XCD).
+  int map_mode = 0;
+  {
+    const bool ok1 = (tiles_n % 8 == 0) && (tiles_m % C::kGroupShared == 0);
+    const bool ok2 = (tiles_m % 8 == 0);
+    const double f1 = 8.0 * a.M + (double)(tiles_m / C::kGroupShared) * a.N;
+    const int per_sweep = 32 / (tiles_m / 8 > 0 ? tiles_m / 8 : 1);
+    const double f2 = 8.0 * a.N + (double)((tiles_n + per_sweep - 1) / (per_sweep > 0 ? per_sweep : 1)) * a.M;
+    if (ok1 && (!ok2 || f1 <= f2)) map_mode = 1;
+    else if (ok2) map_mode = 2;
+  }
   auto kern = fwd_tiled_bf16_kernel<C>;
   static bool attr_done = false;
   if (!attr_done) {
@@ -508,7 +527,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
                      (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.X), a.ldx,
                      static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
                      a.lda, static_cast<const uint16_t*>(a.B), a.ldb, a.scale,
-                     static_cast<uint16_t*>(a.Y), a.ldy, tiles_m, tiles_n, y_vec, map_xcd_n);
+                     static_cast<uint16_t*>(a.Y), a.ldy, tiles_m, tiles_n, y_vec, map_mode);
   return hipGetLastError();
 }
 
