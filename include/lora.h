@@ -30,6 +30,9 @@
  *   - LORA_BF16: pointers 16-byte aligned; K and the ld of X, W, A, W0 and
  *     W_inf multiples of 8.  LORA_F32: pointers 16-byte aligned; K and those
  *     ld multiples of 4.  N, r, ldb and ldy are unrestricted.
+ *   - Limits (LORA_ERR_UNSUPPORTED beyond them): every size <= 2^30 - 1;
+ *     for lora_fwd, ldx, ldw and lda <= LORA_MAX_LD elements (the kernels
+ *     address a 256-row tile of X or W with 32-bit byte offsets).
  *   - Outputs must not overlap any input (LORA_ERR_ALIAS).
  *   - NaN and Inf in the inputs propagate as IEEE arithmetic makes them.
  */
@@ -52,10 +55,13 @@ typedef enum lora_status {
     LORA_ERR_ALIGN = 4,       /* pointer / K / ld alignment rule broken */
     LORA_ERR_DTYPE = 5,       /* unknown lora_dtype */
     LORA_ERR_ALIAS = 6,       /* an output overlaps an input */
-    LORA_ERR_UNSUPPORTED = 7, /* r > LORA_MAX_RANK, or a forced variant that
+    LORA_ERR_UNSUPPORTED = 7, /* r > LORA_MAX_RANK, a size or ld beyond
+                                 the limits below, or a forced variant that
                                  cannot run this shape */
     LORA_ERR_HIP = 8          /* the HIP runtime reported a launch error */
 } lora_status;
+
+#define LORA_MAX_LD (1 << 22)
 
 typedef enum lora_dtype {
     LORA_F32 = 0,

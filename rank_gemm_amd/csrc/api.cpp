@@ -45,6 +45,7 @@ int check_fwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void*
   if (Y == nullptr || B == nullptr) return LORA_ERR_NULL;
   if (K > 0 && (X == nullptr || W == nullptr || A == nullptr)) return LORA_ERR_NULL;
   if (ldx < K || ldw < K || lda < K || ldb < r || ldy < N) return LORA_ERR_STRIDE;
+  if (ldx > LORA_MAX_LD || ldw > LORA_MAX_LD || lda > LORA_MAX_LD) return LORA_ERR_UNSUPPORTED;
   const int64_t e = esize(dtype);
   const int64_t kal = dtype == LORA_BF16 ? 8 : 4;
   if (K > 0) {

@@ -5,59 +5,90 @@
 // decode: the cost is streaming W once from HBM, so the kernel is organised
 // around that stream instead of around output tiles.
 //
-// Per workgroup: 16 output columns (16 rows of W), NW waves.  The K axis is
-// cut into 64-wide blocks dealt round-robin to the waves; each lane streams
-// 32 contiguous bytes of one W row per block, and the matching X and A
-// elements come from L2.  MFMA (16x16x32) accumulates, per wave,
-//   Ybase[m, n] += X W^T   and   T[m, j] += X A^T   (T fully on chip).
+// Per workgroup: 16 output columns (16 rows of W), NW waves.  K is cut into
+// 128-deep blocks dealt round-robin to the waves.  Substep q of a block is
+// one 16-B load per lane: lane l reads row l % 16 at k = 128 b + 32 q +
+// 8 (l / 16), so the four lanes of a row read 64 contiguous bytes and one
+// load instruction touches 16 row segments.  That is the operand layout of
+// v_mfma_f32_16x16x32_bf16 for the k range [128 b + 32 q, +32), the same for
+// the X, W and A operands, so the MFMA accumulates
+//   Ybase[m, n] += X W^T   and   T[m, j] += X A^T   (T stays on chip)
+// straight from the loaded registers.  All loads of a round (U blocks) are
+// issued before its MFMAs, W first: U * 4 KiB of W per wave in flight.  X and
+// A are small and come from L2; rows past M, N or r and k past K read as zero
+// (buffer loads outside the resource's range return 0).
+//
 // The waves' partial sums are added in a fixed order through LDS
 // (deterministic), then the epilogue adds scale * T B^T in fp32 on the VALU
-// and stores bf16.
+// and stores bf16 (one rounding).
 #include "common.h"
 #include "kernels.h"
 
 namespace lora {
 namespace {
 
-template <int MB, int RP, int NW>
+constexpr uint32_t kDecOob = 0x80000000u;  // offset past any resource's range
+
+template <int MB, int RB, int U, int NW>
 struct Dec {
-  static constexpr int RB = RP / 16;
-  static constexpr int kSlots = MB * (1 + RB);           // f32x4 partials per lane
+  static constexpr int RP = RB * 16;
+  static constexpr int kSlots = MB * (1 + RB);            // f32x4 partials per lane
   static constexpr int kRedB = NW * kSlots * kWave * 16;  // LDS for the reduction
-  static constexpr int kTB = MB * 16 * (RP + 1) * 4;      // T rows for the epilogue
+  static constexpr int kTS = RP + 1;                      // T row stride (floats)
+  static constexpr int kTB = MB * 16 * kTS * 4;           // T rows for the epilogue
   static constexpr int kLds = kRedB + kTB;
-  static constexpr int kU = MB >= 4 ? 2 : MB >= 2 ? 4 : 8;  // 64-wide blocks per batch
+  static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
-template <int MB, int RP, int NW>
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int MB, int RB, int U, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
-    int64_t ldy) {
-  using C = Dec<MB, RP, NW>;
-  constexpr int RB = C::RB;
+    int64_t ldy, int b_vec) {
+  using C = Dec<MB, RB, U, NW>;
+  constexpr int RP = C::RP;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane & 15, lq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * 16;
 
-  const uint16_t* wrow = W + (int64_t)min(n0 + lrow, N - 1) * ldw + lq * 16;
-  const uint16_t* xrow[MB];
-  bool xin[MB];
+  // Lanes of rows past N (or M) read row N - 1 (M - 1) again: those MFMA
+  // rows and columns are never stored, and the repeated addresses cost no
+  // extra memory traffic.  Rank rows past r read as zero (the epilogue sums
+  // only j < r, but zero rows keep T finite there).
+  const int wrows = min(16, N - n0);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * ldw), 0, (int)(wrows * ldw * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)(M * ldx * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(r * lda * 2), 0x00020000);
+  const uint32_t lane_k = lg * 16;  // byte offset of the lane's 16-B piece in a substep
+  const uint32_t wbase = min(lrow, wrows - 1) * (uint32_t)ldw * 2 + lane_k;
+  uint32_t xbase[MB], abase[RB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = mb * 16 + lrow;
-    xin[mb] = m < M;
-    xrow[mb] = X + (int64_t)min(m, M - 1) * ldx + lq * 16;
-  }
-  const uint16_t* arow[RB];
-  bool ain[RB];
+  for (int mb = 0; mb < MB; ++mb)
+    xbase[mb] = min(mb * 16 + lrow, M - 1) * (uint32_t)ldx * 2 + lane_k;
 #pragma unroll
-  for (int tj = 0; tj < RB; ++tj) {
-    const int j = tj * 16 + lrow;
-    ain[tj] = j < r;
-    arow[tj] = A + (int64_t)min(j, r - 1) * lda + lq * 16;
+  for (int jb = 0; jb < RB; ++jb) abase[jb] = (jb * 16 + lrow) * (uint32_t)lda * 2 + lane_k;
+
+  // The epilogue's B row (lane: row n0 + l % 16), loaded now by the waves
+  // that run the epilogue, so its latency hides behind the W stream; masking
+  // past r waits for the epilogue, so nothing here waits on these loads.
+  // Positions past r load a valid chunk of the row.  Rows that are not
+  // 16-B aligned (ldb % 8 != 0) are read in the epilogue instead.
+  u32x4 bv[RP / 8];
+  const int64_t brow = min(n0 + lrow, N - 1);
+  if (b_vec && wave < MB) {
+#pragma unroll
+    for (int c = 0; c < RP / 8; ++c)
+      bv[c] = *reinterpret_cast<const u32x4*>(B + brow * ldb + min(c * 8, (r - 1) & ~7));
   }
 
   f32x4 yacc[MB], tacc[MB][RB];
@@ -65,51 +96,58 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
   for (int mb = 0; mb < MB; ++mb) {
     yacc[mb] = zero4();
 #pragma unroll
-    for (int tj = 0; tj < RB; ++tj) tacc[mb][tj] = zero4();
+    for (int jb = 0; jb < RB; ++jb) tacc[mb][jb] = zero4();
   }
 
-  const u32x4 z = {0, 0, 0, 0};
-  const int nblk = (K + 63) / 64;
-  for (int b0 = wave; b0 < nblk; b0 += NW * C::kU) {
-    u32x4 wv[C::kU][2];
-    // Issue the whole batch of W loads first: they are the HBM stream.
+  const int nkb = (K + 127) >> 7;
+  for (int kb0 = wave; kb0 < nkb; kb0 += NW * U) {
+    // Byte offset of each (block, substep) chunk within a row, or past the
+    // range when the block or the 8-element chunk lies beyond K.
+    uint32_t off[U][4];
 #pragma unroll
-    for (int u = 0; u < C::kU; ++u) {
-      const int blk = b0 + u * NW;
-      const int k = blk * 64 + lq * 16;
+    for (int u = 0; u < U; ++u) {
+      const int kb = kb0 + NW * u;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        wv[u][h] = (blk < nblk && k + h * 8 < K)
-                       ? *reinterpret_cast<const u32x4*>(wrow + (int64_t)blk * 64 + h * 8)
-                       : z;
-    }
-#pragma unroll
-    for (int u = 0; u < C::kU; ++u) {
-      const int blk = b0 + u * NW;
-      if (blk >= nblk) break;
-      const int k = blk * 64 + lq * 16;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bool kin = k + h * 8 < K;
-        u32x4 xv[MB], av[RB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          xv[mb] = (kin && xin[mb])
-                       ? *reinterpret_cast<const u32x4*>(xrow[mb] + (int64_t)blk * 64 + h * 8)
-                       : z;
-#pragma unroll
-        for (int tj = 0; tj < RB; ++tj)
-          av[tj] = (kin && ain[tj])
-                       ? *reinterpret_cast<const u32x4*>(arow[tj] + (int64_t)blk * 64 + h * 8)
-                       : z;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          yacc[mb] = mfma16x16x32(xv[mb], wv[u][h], yacc[mb]);
-#pragma unroll
-          for (int tj = 0; tj < RB; ++tj) tacc[mb][tj] = mfma16x16x32(xv[mb], av[tj], tacc[mb][tj]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int k = kb * 128 + q * 32 + lg * 8;
+        off[u][q] = (kb < nkb && k < K) ? (uint32_t)(kb * 256 + q * 64) : kDecOob;
       }
     }
+    // X and A first: they come from L2 and leave the L1's miss queue
+    // quickly, and the T MFMAs run on them while W streams in behind.
+    u32x4 w[U][4], a[U][RB][4], x[U][MB][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) x[u][mb][q] = bload(rx, xbase[mb] + off[u][q]);
+#pragma unroll
+        for (int jb = 0; jb < RB; ++jb) a[u][jb][q] = bload(ra, abase[jb] + off[u][q]);
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[u][q] = bload(rw, wbase + off[u][q]);
+    // Keep the whole round's loads in flight: no MFMA (and no wait) is
+    // scheduled before the last load is issued.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int jb = 0; jb < RB; ++jb)
+            tacc[mb][jb] = mfma16x16x32(x[u][mb][q], a[u][jb][q], tacc[mb][jb]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) yacc[mb] = mfma16x16x32(x[u][mb][q], w[u][q], yacc[mb]);
   }
 
   // Cross-wave reduction in a fixed order (wave 0 + wave 1 + ...).
@@ -118,28 +156,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
   for (int mb = 0; mb < MB; ++mb) {
     red[(wave * C::kSlots + mb * (1 + RB)) * kWave + lane] = yacc[mb];
 #pragma unroll
-    for (int tj = 0; tj < RB; ++tj) red[(wave * C::kSlots + mb * (1 + RB) + 1 + tj) * kWave + lane] = tacc[mb][tj];
+    for (int jb = 0; jb < RB; ++jb)
+      red[(wave * C::kSlots + mb * (1 + RB) + 1 + jb) * kWave + lane] = tacc[mb][jb];
   }
   __syncthreads();
   const bool active = wave < MB;
   const int mb = active ? wave : 0;
   f32x4 y = zero4();
-  float* tl = reinterpret_cast<float*>(smem + C::kRedB) + mb * 16 * (RP + 1);
+  float* tl = reinterpret_cast<float*>(smem + C::kRedB) + mb * 16 * C::kTS;
   if (active) {
     f32x4 t[RB];
 #pragma unroll
-    for (int tj = 0; tj < RB; ++tj) t[tj] = zero4();
+    for (int jb = 0; jb < RB; ++jb) t[jb] = zero4();
     for (int w = 0; w < NW; ++w) {
       y += red[(w * C::kSlots + mb * (1 + RB)) * kWave + lane];
 #pragma unroll
-      for (int tj = 0; tj < RB; ++tj)
-        t[tj] += red[(w * C::kSlots + mb * (1 + RB) + 1 + tj) * kWave + lane];
+      for (int jb = 0; jb < RB; ++jb) t[jb] += red[(w * C::kSlots + mb * (1 + RB) + 1 + jb) * kWave + lane];
     }
-    // T rows of this M block to LDS (fp32) for the up-projection below.
+    // T rows of this M block to LDS (accumulator layout: lane holds column
+    // j = 16 jb + l % 16 of rows 4 (l / 16) + q).
 #pragma unroll
-    for (int tj = 0; tj < RB; ++tj)
+    for (int jb = 0; jb < RB; ++jb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tl[(lq * 4 + q) * (RP + 1) + tj * 16 + lrow] = t[tj][q];
+      for (int q = 0; q < 4; ++q) tl[(lg * 4 + q) * C::kTS + jb * 16 + lrow] = t[jb][q];
   }
   __syncthreads();
   if (!active) return;
@@ -147,24 +186,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
   const int n = n0 + lrow;
   if (n >= N) return;
   float bn[RP];
+  if (b_vec) {
 #pragma unroll
-  for (int j = 0; j < RP; ++j) bn[j] = j < r ? bf2f(B[(int64_t)n * ldb + j]) : 0.f;
+    for (int j = 0; j < RP; ++j) {
+      const uint32_t h = (bv[j >> 3][(j >> 1) & 3] >> ((j & 1) * 16)) & 0xFFFFu;
+      bn[j] = j < r ? bf2f((uint16_t)h) : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < RP; ++j) bn[j] = j < r ? bf2f(B[brow * ldb + j]) : 0.f;
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int m = mb * 16 + lq * 4 + q;
+    const int m = mb * 16 + lg * 4 + q;
     if (m >= M) break;
     float l = 0.f;
 #pragma unroll
-    for (int j = 0; j < RP; ++j) l += tl[(lq * 4 + q) * (RP + 1) + j] * bn[j];
+    for (int j = 0; j < RP; ++j)
+      if (j < r) l += tl[(lg * 4 + q) * C::kTS + j] * bn[j];
     Y[(int64_t)m * ldy + n] = f2bf(y[q] + scale * l);
   }
 }
 
-template <int MB, int RP>
+template <int MB, int RB, int U>
 hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = 8;
-  using C = Dec<MB, RP, NW>;
-  auto kern = fwd_decode_bf16_kernel<MB, RP, NW>;
+  using C = Dec<MB, RB, U, NW>;
+  auto kern = fwd_decode_bf16_kernel<MB, RB, U, NW>;
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -173,28 +221,31 @@ hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
     attr_done = true;
   }
   const int blocks = (int)((a.N + 15) / 16);
+  const int b_vec = ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), C::kLds, s, (int)a.M, (int)a.N, (int)a.K,
                      (int)a.r, static_cast<const uint16_t*>(a.X), a.ldx,
                      static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
                      a.lda, static_cast<const uint16_t*>(a.B), a.ldb, a.scale,
-                     static_cast<uint16_t*>(a.Y), a.ldy);
+                     static_cast<uint16_t*>(a.Y), a.ldy, b_vec);
   return hipGetLastError();
 }
 
-template <int RP>
-hipError_t launch_dec_rp(const FwdArgs& a, hipStream_t s) {
+// Blocks per round: the loads of a round (16 U (1 + RB + MB) VGPRs) stay
+// within about 200 registers.
+template <int RB>
+hipError_t launch_dec_rb(const FwdArgs& a, hipStream_t s) {
   switch ((a.M + 15) / 16) {
-    case 1: return launch_dec<1, RP>(a, s);
-    case 2: return launch_dec<2, RP>(a, s);
-    case 3: return launch_dec<3, RP>(a, s);
-    default: return launch_dec<4, RP>(a, s);
+    case 1: return launch_dec<1, RB, RB == 1 ? 4 : 3>(a, s);
+    case 2: return launch_dec<2, RB, 2>(a, s);
+    case 3: return launch_dec<3, RB, RB == 1 ? 2 : 1>(a, s);
+    default: return launch_dec<4, RB, RB == 1 ? 2 : 1>(a, s);
   }
 }
 
 }  // namespace
 
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s) {
-  return a.r <= 16 ? launch_dec_rp<16>(a, s) : launch_dec_rp<32>(a, s);
+  return a.r <= 16 ? launch_dec_rb<1>(a, s) : launch_dec_rb<2>(a, s);
 }
 
 }  // namespace lora
