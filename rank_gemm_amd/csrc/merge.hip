@@ -10,15 +10,17 @@
 // bf16 kernel.  A workgroup (4 waves) owns a 256-column strip of the output
 // and a range of 16-row blocks; wave w owns columns [64w, 64w + 64) of the
 // strip.  P^T = A^T B^T is computed as 16 x 16 MFMA blocks (rows = k,
-// columns = n, v_mfma_f32_16x16x32_bf16, fp32 accumulate).  The four k-blocks
-// of a wave use a permuted k order, MFMA row i of block kb <-> column
-// 16 (i / 4) + 4 kb + i % 4, so that after the four MFMAs lane l holds, for
-// row n = l % 16, the 16 consecutive columns [16 (l / 16), +16) of the
-// wave's 64: exactly one 32-byte run of W0 and of W_inf.  Each lane then
-// adds its W0 run, rounds once to bf16 and stores the run; no LDS round trip
-// for P.  The A strip is staged in LDS once per workgroup, transposed so that
-// the rank is contiguous, and its fragments stay in registers for every row
-// block.  Several row blocks of W0 loads are kept in flight.
+// columns = n, v_mfma_f32_16x16x32_bf16, fp32 accumulate); with a permuted k
+// order (run_col below) each of the four accumulators of a lane holds four
+// consecutive columns of one row.  The wave writes them to its own fp32 P
+// tile in LDS and reads them back line-wise: lane l takes 8 columns of row
+// l / 8 (and l / 8 + 8), so W0 is loaded and W_inf stored as whole 128-B
+// lines (8 rows x 128 B per instruction), which a half-line layout (16 rows
+// x 64 B) streams measurably slower.  Each lane adds its W0 values in fp32,
+// rounds once to bf16 and stores.  The A strip is staged in LDS once per
+// workgroup, transposed so that the rank is contiguous, and its fragments
+// stay in registers for every row block; the first row blocks' loads are
+// issued before it, and later row blocks are double-buffered.
 //
 // W0 is never written; nothing is accumulated across workgroups, so repeated
 // merges of the same inputs are bitwise identical.
@@ -30,13 +32,15 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 constexpr int kStrip = 256;  // columns per workgroup (64 per wave)
+constexpr int kPS = 64 + 4;  // row stride (floats) of a wave's P tile in LDS
 
 template <int RP>
 struct Mrg {
   static constexpr int RB32 = RP / 32;          // rank chunks of 32
   static constexpr int kAS = RP + 8;            // transposed-A row stride (elements, even)
-  static constexpr int kLds = kStrip * kAS * 2;
-  static constexpr int kU = RP <= 64 ? 4 : 2;   // row blocks in flight per wave
+  static constexpr int kLdsA = kStrip * kAS * 2;  // transposed A strip
+  static constexpr int kLds = kLdsA + 4 * 16 * kPS * 4;  // + one fp32 P tile per wave
+  static constexpr int kU = 2;                  // row blocks per load group (two groups in flight)
 };
 
 // Column (within the wave's 64) of element e (0..15) of lane group lg's run:
@@ -57,7 +61,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
   uint32_t* at32 = reinterpret_cast<uint32_t*>(smem);  // at[k][j] as j-pairs, k < 256
   const uint16_t* at = reinterpret_cast<const uint16_t*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, lg = lane >> 4;
   const int strip = blockIdx.x % strips;
   const int ngrp = blockIdx.x / strips;
@@ -66,6 +71,57 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
   const int nblocks = (N + 15) / 16;
   const int nb_end = min(nblocks, nb_begin + nblk_per_wg);
   const u32x4 z = {0, 0, 0, 0};
+  const int kw = wave * 64;
+  // This wave's P tile in LDS (fp32, 16 rows x 64 columns, padded rows).
+  float* pl = reinterpret_cast<float*>(smem + C::kLdsA) + wave * 16 * kPS;
+
+  // W0 and W_inf move in whole 128-B lines: lane l takes row l / 8 (+ 8 for
+  // the second half) of the row block and columns 8 (l % 8) .. + 7 of the
+  // wave's 64, so one load or store instruction covers 8 rows x 128 B.
+  const int srow = lane >> 3;
+  const int gcol = k0 + kw + 8 * (lane & 7);
+  const bool cin = gcol < K;
+
+  auto load = [&](int nb, u32x4 (&w)[U][2], u32x4 (&bf)[U][RB32]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool bin = (nb + u) < nb_end;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = (nb + u) * 16 + srow + 8 * h;
+        w[u][h] = (bin && n < N && cin) ? *reinterpret_cast<const u32x4*>(W0 + (int64_t)n * ldw0 + gcol) : z;
+      }
+      // B fragment (MFMA operand): row (nb + u) * 16 + l % 16.
+      const int n = (nb + u) * 16 + lrow;
+      const bool nin = bin && n < N;
+      const int64_t row = (int64_t)(nin ? n : 0);
+#pragma unroll
+      for (int kk = 0; kk < RB32; ++kk) {
+        const int j0 = kk * 32 + lg * 8;
+        u32x4 v = z;
+        if (nin) {
+          const uint16_t* src = B + row * ldb + j0;
+          if (b_vec && j0 + 8 <= r) {
+            v = *reinterpret_cast<const u32x4*>(src);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t lo = (j0 + 2 * q < r) ? src[2 * q] : 0u;
+              const uint32_t hi = (j0 + 2 * q + 1 < r) ? src[2 * q + 1] : 0u;
+              v[q] = lo | (hi << 16);
+            }
+          }
+        }
+        bf[u][kk] = v;
+      }
+    }
+  };
+
+  // The first row blocks' loads go out before the A strip is staged, so the
+  // two latencies overlap.
+  u32x4 wa[U][2], ba[U][RB32], wb[U][2], bb[U][RB32];
+  int nb = nb_begin;
+  if (nb < nb_end) load(nb, wa, ba);
 
   // 1. A strip -> LDS transposed to at[k][j]: a thread takes two ranks
   //    (2p, 2p + 1) of one 8-column chunk and writes 32-bit words, so
@@ -88,7 +144,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
 
   // 2. This wave's A^T fragments for its 64 columns: block kb, MFMA row i
   //    holds column run_col(i / 4, 4 kb + i % 4).
-  const int kw = wave * 64;
   u32x4 af[4][RB32];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -98,46 +153,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
       af[kb][kk] = *reinterpret_cast<const u32x4*>(at + kl * C::kAS + kk * 32 + lg * 8);
   }
 
-  // Lane's output: row n, columns g0 .. g0 + 7 and g1 .. g1 + 7.
-  const int g0 = k0 + kw + 8 * lg, g1 = g0 + 32;
-  const bool c0 = g0 < K, c1 = g1 < K;
-
-  auto load = [&](int nb, u32x4 (&w)[U][2], u32x4 (&bf)[U][RB32]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int n = (nb + u) * 16 + lrow;
-      const bool nin = (nb + u) < nb_end && n < N;
-      const int64_t row = (int64_t)(nin ? n : 0);
-      w[u][0] = (nin && c0) ? *reinterpret_cast<const u32x4*>(W0 + row * ldw0 + g0) : z;
-      w[u][1] = (nin && c1) ? *reinterpret_cast<const u32x4*>(W0 + row * ldw0 + g1) : z;
-#pragma unroll
-      for (int kk = 0; kk < RB32; ++kk) {
-        const int j0 = kk * 32 + lg * 8;
-        u32x4 v = z;
-        if (nin) {
-          const uint16_t* src = B + row * ldb + j0;
-          if (b_vec && j0 + 8 <= r) {
-            v = *reinterpret_cast<const u32x4*>(src);
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t lo = (j0 + 2 * q < r) ? src[2 * q] : 0u;
-              const uint32_t hi = (j0 + 2 * q + 1 < r) ? src[2 * q + 1] : 0u;
-              v[q] = lo | (hi << 16);
-            }
-          }
-        }
-        bf[u][kk] = v;
-      }
-    }
-  };
   auto compute_store = [&](int nb, const u32x4 (&w)[U][2], const u32x4 (&bf)[U][RB32]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // The MFMAs read operands from all 64 lanes, so they run wave-uniform;
       // rows past N only skip their stores.
       if ((nb + u) >= nb_end) continue;
-      const int n = (nb + u) * 16 + lrow;
       f32x4 p[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -145,32 +166,33 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
 #pragma unroll
         for (int kk = 0; kk < RB32; ++kk) p[kb] = mfma16x16x32(af[kb][kk], bf[u][kk], p[kb]);
       }
-      // p[kb][q] is element e = 4 kb + q of the lane's run (row n).
-      u32x4 o[2];
+      // p[kb] holds row l % 16, columns run_col(l / 16, 4 kb .. 4 kb + 3):
+      // four consecutive columns.  Through LDS to the line-wise layout.
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int kb = 0; kb < 4; ++kb)
+        *reinterpret_cast<f32x4*>(pl + lrow * kPS + run_col(lg, 4 * kb)) = p[kb];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* src = pl + (srow + 8 * h) * kPS + 8 * (lane & 7);
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(src + 4);
+        const float pv[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        u32x4 o;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
-          const int e = 8 * h + 2 * q2;
           const uint32_t wv = w[u][h][q2];
-          const float lo = __builtin_bit_cast(float, wv << 16) + scale * p[e >> 2][e & 3];
-          const float hi =
-              __builtin_bit_cast(float, wv & 0xFFFF0000u) + scale * p[(e + 1) >> 2][(e + 1) & 3];
-          o[h][q2] = pack_bf2(lo, hi);
+          const float lo = __builtin_bit_cast(float, wv << 16) + scale * pv[2 * q2];
+          const float hi = __builtin_bit_cast(float, wv & 0xFFFF0000u) + scale * pv[2 * q2 + 1];
+          o[q2] = pack_bf2(lo, hi);
         }
-      if (n < N) {
-        uint16_t* dst = Wi + (int64_t)n * ldwi;
-        if (c0) *reinterpret_cast<u32x4*>(dst + g0) = o[0];
-        if (c1) *reinterpret_cast<u32x4*>(dst + g1) = o[1];
+        const int n = (nb + u) * 16 + srow + 8 * h;
+        if (n < N && cin) *reinterpret_cast<u32x4*>(Wi + (int64_t)n * ldwi + gcol) = o;
       }
     }
   };
 
   // 3. Row blocks, U at a time, the loads of the next group in flight while
   //    the current group is combined and stored.
-  u32x4 wa[U][2], ba[U][RB32], wb[U][2], bb[U][RB32];
-  int nb = nb_begin;
-  if (nb < nb_end) load(nb, wa, ba);
   while (nb < nb_end) {
     if (nb + U < nb_end) load(nb + U, wb, bb);
     compute_store(nb, wa, ba);
