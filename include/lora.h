@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -135,6 +135,40 @@ int lora_merge(int dtype, int64_t N, int64_t K, int64_t r,
                const void *W0, int64_t ldw0, const void *B, int64_t ldb,
                const void *A, int64_t lda, float scale,
                void *W_inf, int64_t ldwi, void *stream);
+
+/*
+ * lora_merge_batch -- lora_merge for many targets in few launches
+ *   (the per-layer, per-target refresh loop of [unsloth], all targets of a
+ *   model at once).
+ *
+ * Element t of descs describes one merge exactly as the arguments of
+ * lora_merge do.  The result is bitwise the result of calling lora_merge on
+ * each target in turn.  Targets are merged concurrently, so every W_inf must
+ * also not overlap any other target's W0, B, A or W_inf (LORA_ERR_ALIAS).
+ * bf16 targets of the same padded rank go up to 24 per launch, their
+ * descriptors passed as kernel arguments (nothing is allocated); fp32
+ * targets are launched one by one.
+ *
+ *   dtype         LORA_F32 or LORA_BF16, for every target.
+ *   count         number of descriptors, >= 0 (0: no-op).
+ *   descs         HOST array of count descriptors, read during the call only.
+ *   stream        hipStream_t as void*.
+ * Returns a lora_status; on any invalid descriptor nothing is launched.
+ */
+typedef struct lora_merge_desc {
+    int64_t N, K, r;
+    const void *W0;
+    int64_t ldw0;
+    const void *B;
+    int64_t ldb;
+    const void *A;
+    int64_t lda;
+    float scale;
+    void *W_inf;
+    int64_t ldwi;
+} lora_merge_desc;
+
+int lora_merge_batch(int dtype, int count, const lora_merge_desc *descs, void *stream);
 
 /* Static, NUL-terminated description of a lora_status value. */
 const char *lora_status_str(int status);

@@ -7,6 +7,7 @@ loaded, the first call raises.
 
     Y = fwd(X, W, A, B, scale)          # X W^T + scale * (X A^T) B^T
     merge(W0, B, A, scale, out=W_inf)   # W_inf = W0 + scale * B A, W0 untouched
+    merge_batch([(W0, B, A, scale, W_inf), ...])   # many targets, few launches
 
 Tensors are torch tensors on the current HIP device, all bfloat16 or all
 float32, 2-D with unit inner stride (rows may be padded: the leading
@@ -38,8 +39,18 @@ VARIANTS = {"auto": 0, "tiled": 1, "decode": 2}
 MAX_RANK = 256
 DECODE_MAX_M = 64
 
-EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_status_str",
+EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch", "lora_status_str",
            "lora_abi_version", "lora_fwd_pick")
+
+
+class MergeDesc(ctypes.Structure):
+    """lora_merge_desc of include/lora.h."""
+    _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("r", ctypes.c_int64),
+                ("W0", ctypes.c_void_p), ("ldw0", ctypes.c_int64),
+                ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("lda", ctypes.c_int64),
+                ("scale", ctypes.c_float),
+                ("W_inf", ctypes.c_void_p), ("ldwi", ctypes.c_int64)]
 
 _lib = None
 
@@ -66,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.lora_fwd_variant.restype = i32
     L.lora_merge.argtypes = [i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, vp, i64, vp]
     L.lora_merge.restype = i32
+    L.lora_merge_batch.argtypes = [i32, i32, ctypes.POINTER(MergeDesc), vp]
+    L.lora_merge_batch.restype = i32
     L.lora_status_str.argtypes = [i32]
     L.lora_status_str.restype = ctypes.c_char_p
     L.lora_abi_version.argtypes = []
@@ -108,6 +121,13 @@ def merge_raw(dtype: int, N: int, K: int, r: int, W0: int, ldw0: int, B: int, ld
     """lora_merge with integer addresses; returns the lora_status."""
     return int(lib().lora_merge(dtype, N, K, r, W0, ldw0, B, ldb, A, lda, scale, Wi, ldwi,
                                 stream or None))
+
+
+def merge_batch_raw(dtype: int, descs, stream: int = 0) -> int:
+    """lora_merge_batch over a sequence of MergeDesc (or an array of them)."""
+    if not isinstance(descs, ctypes.Array):
+        descs = (MergeDesc * len(descs))(*descs)
+    return int(lib().lora_merge_batch(dtype, len(descs), descs, stream or None))
 
 
 # ------------------------------------------------------------ torch-facing
@@ -193,3 +213,29 @@ def merge(W0, B, A, scale: float, out=None):
                    _stream(W0.device))
     _check(st, "lora_merge")
     return out
+
+
+def merge_batch(targets):
+    """Merge from pristine for many targets: ``targets`` is a sequence of
+    ``(W0, B, A, scale, W_inf)``; each ``W_inf`` is written as ``merge`` would
+    write it.  All tensors share one dtype and device."""
+    if not targets:
+        return
+    dt = _dtype_code(targets[0][0])
+    dev = targets[0][0].device
+    descs = (MergeDesc * len(targets))()
+    for i, (W0, B, A, scale, out) in enumerate(targets):
+        N, K = W0.shape
+        r = A.shape[0]
+        if A.shape[1] != K or tuple(B.shape) != (N, r) or tuple(out.shape) != (N, K):
+            raise ValueError(f"target {i}: shape mismatch W0{tuple(W0.shape)} B{tuple(B.shape)} "
+                             f"A{tuple(A.shape)} out{tuple(out.shape)}")
+        for t, nm in ((W0, "W0"), (B, "B"), (A, "A"), (out, "out")):
+            if _dtype_code(t) != dt or t.device != dev:
+                raise ValueError(f"target {i}: {nm} must match the first W0 in dtype and device")
+        p0, ld0 = _mat(W0, "W0")
+        pb, ldb = _mat(B, "B")
+        pa, lda = _mat(A, "A")
+        po, ldo = _mat(out, "out")
+        descs[i] = MergeDesc(N, K, r, p0, ld0, pb, ldb, pa, lda, float(scale), po, ldo)
+    _check(merge_batch_raw(dt, descs, _stream(dev)), "lora_merge_batch")

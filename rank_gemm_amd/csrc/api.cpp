@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <vector>
 
 #include "kernels.h"
 
@@ -65,6 +66,29 @@ int pick(int dtype, int64_t M, int64_t r) {
   if (dtype == LORA_BF16 && M <= LORA_DECODE_MAX_M && r <= lora::kDecodeMaxRank)
     return LORA_VARIANT_DECODE;
   return LORA_VARIANT_TILED;
+}
+
+// Host validation shared by lora_merge and lora_merge_batch.
+int check_merge(int dtype, int64_t N, int64_t K, int64_t r, const void* W0, int64_t ldw0,
+                const void* B, int64_t ldb, const void* A, int64_t lda, void* W_inf,
+                int64_t ldwi) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (N < 0 || K < 0 || r < 1) return LORA_ERR_SHAPE;
+  if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
+  if (N > INT32_MAX / 2 || K > INT32_MAX / 2) return LORA_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return LORA_OK;
+  if (W0 == nullptr || B == nullptr || A == nullptr || W_inf == nullptr) return LORA_ERR_NULL;
+  if (ldw0 < K || ldwi < K || lda < K || ldb < r) return LORA_ERR_STRIDE;
+  const int64_t e = esize(dtype);
+  const int64_t kal = dtype == LORA_BF16 ? 8 : 4;
+  if (!aligned16(W0) || !aligned16(A) || !aligned16(W_inf)) return LORA_ERR_ALIGN;
+  if (K % kal || ldw0 % kal || ldwi % kal || lda % kal) return LORA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(B) % e) return LORA_ERR_ALIGN;
+  const Range wi = span(W_inf, N, K, ldwi, e);
+  if (overlap(wi, span(W0, N, K, ldw0, e)) || overlap(wi, span(A, r, K, lda, e)) ||
+      overlap(wi, span(B, N, r, ldb, e)))
+    return LORA_ERR_ALIAS;
+  return LORA_OK;
 }
 
 }  // namespace
@@ -130,22 +154,8 @@ int lora_fwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void* 
 int lora_merge(int dtype, int64_t N, int64_t K, int64_t r, const void* W0, int64_t ldw0,
                const void* B, int64_t ldb, const void* A, int64_t lda, float scale, void* W_inf,
                int64_t ldwi, void* stream) {
-  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
-  if (N < 0 || K < 0 || r < 1) return LORA_ERR_SHAPE;
-  if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
-  if (N > INT32_MAX / 2 || K > INT32_MAX / 2) return LORA_ERR_UNSUPPORTED;
-  if (N == 0 || K == 0) return LORA_OK;
-  if (W0 == nullptr || B == nullptr || A == nullptr || W_inf == nullptr) return LORA_ERR_NULL;
-  if (ldw0 < K || ldwi < K || lda < K || ldb < r) return LORA_ERR_STRIDE;
-  const int64_t e = esize(dtype);
-  const int64_t kal = dtype == LORA_BF16 ? 8 : 4;
-  if (!aligned16(W0) || !aligned16(A) || !aligned16(W_inf)) return LORA_ERR_ALIGN;
-  if (K % kal || ldw0 % kal || ldwi % kal || lda % kal) return LORA_ERR_ALIGN;
-  if (reinterpret_cast<uintptr_t>(B) % e) return LORA_ERR_ALIGN;
-  const Range wi = span(W_inf, N, K, ldwi, e);
-  if (overlap(wi, span(W0, N, K, ldw0, e)) || overlap(wi, span(A, r, K, lda, e)) ||
-      overlap(wi, span(B, N, r, ldb, e)))
-    return LORA_ERR_ALIAS;
+  const int st = check_merge(dtype, N, K, r, W0, ldw0, B, ldb, A, lda, W_inf, ldwi);
+  if (st != LORA_OK || N == 0 || K == 0) return st;
   const lora::MergeArgs a{N, K, r, W0, ldw0, B, ldb, A, lda, scale, W_inf, ldwi};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t err =
@@ -153,4 +163,47 @@ int lora_merge(int dtype, int64_t N, int64_t K, int64_t r, const void* W0, int64
   return err == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+int lora_merge_batch(int dtype, int count, const lora_merge_desc* descs, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (count < 0) return LORA_ERR_SHAPE;
+  if (count == 0) return LORA_OK;
+  if (descs == nullptr) return LORA_ERR_NULL;
+  const int64_t e = esize(dtype);
+  std::vector<lora::MergeArgs> work;
+  work.reserve(count);
+  for (int i = 0; i < count; ++i) {
+    const lora_merge_desc& d = descs[i];
+    const int st = check_merge(dtype, d.N, d.K, d.r, d.W0, d.ldw0, d.B, d.ldb, d.A, d.lda,
+                               d.W_inf, d.ldwi);
+    if (st != LORA_OK) return st;
+    if (d.N == 0 || d.K == 0) continue;
+    work.push_back({d.N, d.K, d.r, d.W0, d.ldw0, d.B, d.ldb, d.A, d.lda, d.scale, d.W_inf,
+                    d.ldwi});
+  }
+  // Every output against every other target's inputs and output.
+  for (size_t i = 0; i < work.size(); ++i) {
+    const lora::MergeArgs& a = work[i];
+    const Range wi = span(a.Wi, a.N, a.K, a.ldwi, e);
+    for (size_t j = 0; j < work.size(); ++j) {
+      if (j == i) continue;
+      const lora::MergeArgs& b = work[j];
+      if (overlap(wi, span(b.W0, b.N, b.K, b.ldw0, e)) ||
+          overlap(wi, span(b.A, b.r, b.K, b.lda, e)) ||
+          overlap(wi, span(b.B, b.N, b.r, b.ldb, e)) ||
+          overlap(wi, span(b.Wi, b.N, b.K, b.ldwi, e)))
+        return LORA_ERR_ALIAS;
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (dtype == LORA_BF16) {
+    err = lora::launch_merge_bf16_batch(work.data(), (int)work.size(), s);
+  } else {
+    for (const lora::MergeArgs& a : work)
+      if ((err = lora::launch_merge_f32(a, s)) != hipSuccess) break;
+  }
+  return err == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 }  // extern "C"
+

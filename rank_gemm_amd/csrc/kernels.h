@@ -37,6 +37,7 @@ hipError_t launch_fwd_tiled_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge_bf16(const MergeArgs& a, hipStream_t s);
 hipError_t launch_merge_f32(const MergeArgs& a, hipStream_t s);
+hipError_t launch_merge_bf16_batch(const MergeArgs* a, int count, hipStream_t s);
 
 // Largest rank the decode kernel is instantiated for.
 constexpr int kDecodeMaxRank = 32;

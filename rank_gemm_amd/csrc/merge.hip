@@ -33,6 +33,7 @@ namespace {
 constexpr int kMergeThreads = 256;
 constexpr int kStrip = 256;  // columns per workgroup (64 per wave)
 constexpr int kPS = 64 + 4;  // row stride (floats) of a wave's P tile in LDS
+constexpr int kMergeBatch = 24;  // targets per batched launch (kernel-argument space)
 
 template <int RP>
 struct Mrg {
@@ -49,23 +50,25 @@ struct Mrg {
 // row covers 64 contiguous bytes.
 __device__ __forceinline__ int run_col(int lg, int e) { return (e >> 3) * 32 + 8 * lg + (e & 7); }
 
+// One workgroup's work: strip (wg % strips) of the output, row blocks
+// [(wg / strips) * nblk_per_wg, +nblk_per_wg).  Shared by the one-target and
+// the batched kernels.
 template <int RP>
-__global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
-    int N, int K, int r, const uint16_t* __restrict__ W0, int64_t ldw0,
-    const uint16_t* __restrict__ B, int64_t ldb, const uint16_t* __restrict__ A, int64_t lda,
-    float scale, uint16_t* __restrict__ Wi, int64_t ldwi, int strips, int nblk_per_wg,
-    int b_vec) {
+__device__ __forceinline__ void merge_bf16_tile(
+    unsigned char* smem, int wg, int N, int K, int r, const uint16_t* __restrict__ W0,
+    int64_t ldw0, const uint16_t* __restrict__ B, int64_t ldb, const uint16_t* __restrict__ A,
+    int64_t lda, float scale, uint16_t* __restrict__ Wi, int64_t ldwi, int strips,
+    int nblk_per_wg, int b_vec) {
   using C = Mrg<RP>;
   constexpr int RB32 = C::RB32, U = C::kU;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint32_t* at32 = reinterpret_cast<uint32_t*>(smem);  // at[k][j] as j-pairs, k < 256
   const uint16_t* at = reinterpret_cast<const uint16_t*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, lg = lane >> 4;
-  const int strip = blockIdx.x % strips;
-  const int ngrp = blockIdx.x / strips;
+  const int strip = wg % strips;
+  const int ngrp = wg / strips;
   const int k0 = strip * kStrip;
   const int nb_begin = ngrp * nblk_per_wg;
   const int nblocks = (N + 15) / 16;
@@ -205,31 +208,133 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
 }
 
 template <int RP>
-hipError_t launch_m(const MergeArgs& a, hipStream_t s) {
-  using C = Mrg<RP>;
-  auto kern = merge_bf16_kernel<RP>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
+__global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
+    int N, int K, int r, const uint16_t* __restrict__ W0, int64_t ldw0,
+    const uint16_t* __restrict__ B, int64_t ldb, const uint16_t* __restrict__ A, int64_t lda,
+    float scale, uint16_t* __restrict__ Wi, int64_t ldwi, int strips, int nblk_per_wg,
+    int b_vec) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  merge_bf16_tile<RP>(smem, blockIdx.x, N, K, r, W0, ldw0, B, ldb, A, lda, scale, Wi, ldwi,
+                      strips, nblk_per_wg, b_vec);
+}
+
+// Batched merge: up to kMergeBatch targets per launch, their descriptors in
+// the kernel arguments (no device memory).  Workgroups [first[t], first[t+1])
+// belong to target t; a workgroup finds its target by a uniform binary search.
+struct MergeDesc {
+  const uint16_t* W0;
+  const uint16_t* B;
+  const uint16_t* A;
+  uint16_t* Wi;
+  int64_t ldw0, ldb, lda, ldwi;
+  int N, K, r, strips, per, b_vec;
+  float scale;
+};
+
+struct MergeBatch {
+  int count;
+  int first[kMergeBatch + 1];
+  MergeDesc d[kMergeBatch];
+};
+
+template <int RP>
+__global__ __launch_bounds__(kMergeThreads) void merge_bf16_batch_kernel(const MergeBatch args) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int b = blockIdx.x;
+  int lo = 0, hi = args.count - 1;  // last t with first[t] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (args.first[mid] <= b) lo = mid; else hi = mid - 1;
   }
-  const int strips = (int)((a.K + kStrip - 1) / kStrip);
-  const int nblocks = (int)((a.N + 15) / 16);
-  // About 512 workgroups (2 per CU), each streaming at least 2 U-groups of
-  // row blocks so the A-strip staging is amortised.
-  int groups = (512 + strips - 1) / strips;
+  const MergeDesc& d = args.d[lo];
+  merge_bf16_tile<RP>(smem, b - args.first[lo], d.N, d.K, d.r, d.W0, d.ldw0, d.B, d.ldb, d.A,
+                      d.lda, d.scale, d.Wi, d.ldwi, d.strips, d.per, d.b_vec);
+}
+
+// Grid of one target: 256-column strips x groups of row blocks.  About 512
+// workgroups (2 per CU) for a lone target, each streaming at least two load
+// groups of row blocks so the A-strip staging is amortised.
+struct MergeGrid {
+  int strips, per, groups;
+};
+
+template <int RP>
+MergeGrid merge_grid(int64_t N, int64_t K, int target_wgs) {
+  using C = Mrg<RP>;
+  MergeGrid g;
+  g.strips = (int)((K + kStrip - 1) / kStrip);
+  const int nblocks = (int)((N + 15) / 16);
+  int groups = (target_wgs + g.strips - 1) / g.strips;
   if (groups > nblocks) groups = nblocks;
   if (groups < 1) groups = 1;
   int per = (nblocks + groups - 1) / groups;
   if (per < 2 * C::kU) per = nblocks < 2 * C::kU ? nblocks : 2 * C::kU;
-  groups = (nblocks + per - 1) / per;
-  const int b_vec = ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0);
-  hipLaunchKernelGGL(kern, dim3(strips * groups), dim3(kMergeThreads), C::kLds, s, (int)a.N,
+  g.per = per;
+  g.groups = (nblocks + per - 1) / per;
+  return g;
+}
+
+template <class K>
+hipError_t set_lds(K kern, int bytes, bool& done) {
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+int b_vec_of(const void* B, int64_t ldb) {
+  return ((reinterpret_cast<uintptr_t>(B) & 15) == 0) && (ldb % 8 == 0);
+}
+
+template <int RP>
+hipError_t launch_m(const MergeArgs& a, hipStream_t s) {
+  using C = Mrg<RP>;
+  auto kern = merge_bf16_kernel<RP>;
+  static bool attr_done = false;
+  if (hipError_t e = set_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
+  const MergeGrid g = merge_grid<RP>(a.N, a.K, 512);
+  hipLaunchKernelGGL(kern, dim3(g.strips * g.groups), dim3(kMergeThreads), C::kLds, s, (int)a.N,
                      (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.W0), a.ldw0,
                      static_cast<const uint16_t*>(a.B), a.ldb, static_cast<const uint16_t*>(a.A),
-                     a.lda, a.scale, static_cast<uint16_t*>(a.Wi), a.ldwi, strips, per, b_vec);
+                     a.lda, a.scale, static_cast<uint16_t*>(a.Wi), a.ldwi, g.strips, g.per,
+                     b_vec_of(a.B, a.ldb));
+  return hipGetLastError();
+}
+
+// Targets [i0, i1) of a batch, all padded to rank RP, in one launch.  Each
+// target gets row-block groups of 4 load groups (128 rows), so small and
+// large targets share the launch in proportion to their size.
+template <int RP>
+hipError_t launch_mb(const MergeArgs* a, int i0, int i1, hipStream_t s) {
+  using C = Mrg<RP>;
+  auto kern = merge_bf16_batch_kernel<RP>;
+  static bool attr_done = false;
+  if (hipError_t e = set_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
+  MergeBatch mb{};
+  mb.count = i1 - i0;
+  int wgs = 0;
+  for (int i = i0; i < i1; ++i) {
+    const MergeArgs& t = a[i];
+    const int strips = (int)((t.K + kStrip - 1) / kStrip);
+    const int nblocks = (int)((t.N + 15) / 16);
+    const int per = 8 * C::kU;
+    const int groups = (nblocks + per - 1) / per;
+    MergeDesc& d = mb.d[i - i0];
+    d.W0 = static_cast<const uint16_t*>(t.W0);
+    d.B = static_cast<const uint16_t*>(t.B);
+    d.A = static_cast<const uint16_t*>(t.A);
+    d.Wi = static_cast<uint16_t*>(t.Wi);
+    d.ldw0 = t.ldw0; d.ldb = t.ldb; d.lda = t.lda; d.ldwi = t.ldwi;
+    d.N = (int)t.N; d.K = (int)t.K; d.r = (int)t.r;
+    d.strips = strips; d.per = per; d.b_vec = b_vec_of(t.B, t.ldb);
+    d.scale = t.scale;
+    mb.first[i - i0] = wgs;
+    wgs += strips * groups;
+  }
+  mb.first[i1 - i0] = wgs;
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kMergeThreads), C::kLds, s, mb);
   return hipGetLastError();
 }
 
@@ -262,6 +367,29 @@ hipError_t launch_merge_bf16(const MergeArgs& a, hipStream_t s) {
     case 128: return launch_m<128>(a, s);
     default: return launch_m<256>(a, s);
   }
+}
+
+// Batch: runs of consecutive targets with the same padded rank, at most
+// kMergeBatch per launch.
+hipError_t launch_merge_bf16_batch(const MergeArgs* a, int count, hipStream_t s) {
+  int i = 0;
+  while (i < count) {
+    const int rp = pad_rank(a[i].r) < 32 ? 32 : pad_rank(a[i].r);
+    int j = i + 1;
+    while (j < count && j - i < kMergeBatch &&
+           (pad_rank(a[j].r) < 32 ? 32 : pad_rank(a[j].r)) == rp)
+      ++j;
+    hipError_t e;
+    switch (rp) {
+      case 32: e = launch_mb<32>(a, i, j, s); break;
+      case 64: e = launch_mb<64>(a, i, j, s); break;
+      case 128: e = launch_mb<128>(a, i, j, s); break;
+      default: e = launch_mb<256>(a, i, j, s); break;
+    }
+    if (e != hipSuccess) return e;
+    i = j;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_merge_f32(const MergeArgs& a, hipStream_t s) {

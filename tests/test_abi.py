@@ -33,7 +33,7 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 1
+    assert rg.abi_version() == 2
     for s in range(9):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
@@ -131,6 +131,41 @@ def test_merge_rejects_before_any_hip_call(kw, want):
 @pytest.mark.parametrize("kw", [dict(N=0), dict(K=0)])
 def test_merge_empty_is_noop(kw):
     assert _merge(**kw) == rg.LORA_OK
+
+
+def _desc(**kw):
+    a = dict(N=64, K=64, r=16, W0=PW, ldw0=64, B=PB, ldb=16, A=PA, lda=64, scale=2.0, W_inf=PY,
+             ldwi=64)
+    a.update(kw)
+    return rg.MergeDesc(a["N"], a["K"], a["r"], a["W0"], a["ldw0"], a["B"], a["ldb"], a["A"],
+                        a["lda"], a["scale"], a["W_inf"], a["ldwi"])
+
+
+# A second target, far from the first one's buffers.
+SECOND = dict(W0=PX, B=PX + 0x100000, A=PX + 0x200000, W_inf=PX + 0x300000)
+
+
+@pytest.mark.parametrize("descs,want", [
+    ([_desc(r=0)], rg.LORA_ERR_SHAPE),
+    ([_desc(), _desc(**SECOND, ldwi=8)], rg.LORA_ERR_STRIDE),        # second one invalid
+    ([_desc(), _desc(**{**SECOND, "W0": PX + 2})], rg.LORA_ERR_ALIGN),
+    ([_desc(W_inf=PW)], rg.LORA_ERR_ALIAS),                         # own input
+    ([_desc(), _desc(**{**SECOND, "W0": PY})], rg.LORA_ERR_ALIAS),   # W_inf of 0 is W0 of 1
+    ([_desc(), _desc(**{**SECOND, "W_inf": PY + 128})], rg.LORA_ERR_ALIAS),  # outputs overlap
+    ([_desc(), _desc(**{**SECOND, "A": PY + 64})], rg.LORA_ERR_ALIAS),
+])
+def test_merge_batch_rejects_before_any_hip_call(descs, want):
+    assert rg.merge_batch_raw(rg.LORA_BF16, descs) == want
+
+
+def test_merge_batch_argument_checks():
+    assert rg.merge_batch_raw(rg.LORA_BF16, []) == rg.LORA_OK
+    assert rg.merge_batch_raw(5, [_desc()]) == rg.LORA_ERR_DTYPE
+    L = rg.lib()
+    assert L.lora_merge_batch(rg.LORA_BF16, -1, None, None) == rg.LORA_ERR_SHAPE
+    assert L.lora_merge_batch(rg.LORA_BF16, 2, None, None) == rg.LORA_ERR_NULL
+    # empty targets are skipped (no launch), whatever their pointers
+    assert rg.merge_batch_raw(rg.LORA_BF16, [_desc(N=0, W0=0), _desc(K=0, W_inf=0)]) == rg.LORA_OK
 
 
 def test_torch_wrapper_rejects_cpu_tensors():

@@ -167,3 +167,63 @@ def test_rslora_scale_passed_through(gpu_lib):
     got = to_host(_merge(gpu_lib, to_dev(W0), to_dev(A), to_dev(B), s))
     Wd, Wb = oracle.merge(W0, B, A, s)
     _check_bf16_merge(got, Wd, Wb, W0, B, A, s, t.r, "rslora")
+
+
+def _batch_targets(dtype):
+    """Layer-0 targets plus ragged ones with mixed ranks, 31 in all (more
+    than one launch's worth, rank changes forcing separate launches)."""
+    tg = list(LAYER0) if dtype == "bf16" else []
+    shapes = [(37, 264, 7), (100, 520, 32), (33, 1000, 33), (300, 256, 64), (17, 272, 128),
+              (70, 520, 200), (1, 8, 1), (64, 776, 100)]
+    i = 0
+    while len(tg) < 31:
+        N, K, r = shapes[i % len(shapes)]
+        tg.append(synth.MergeTarget(f"b{i}", 93, i, N + i, K, r, 2.0 * r, dtype))
+        i += 1
+    return tg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_batch_equals_per_target_merges(gpu_lib, dtype):
+    import torch
+    tg = _batch_targets(dtype)
+    ins, w0_host = [], []
+    for t in tg:
+        W0 = t.make_w0()
+        A, B = t.make_ab(0)
+        w0_host.append(W0)
+        ins.append((to_dev(W0), to_dev(B), to_dev(A), t.scale))
+    one = [_merge(gpu_lib, w0, a, b, s) for (w0, b, a, s) in ins]
+    outs = [torch.full_like(o, float("nan")) for o in one]
+    gpu_lib.merge_batch([(w0, b, a, s, o) for (w0, b, a, s), o in zip(ins, outs)])
+    torch.cuda.synchronize()
+    for t, o, ref, (w0, _, _, _), h in zip(tg, outs, one, ins, w0_host):
+        assert to_host(o).tobytes() == to_host(ref).tobytes(), t.name
+        assert to_host(w0).tobytes() == h.tobytes(), t.name  # pristine untouched
+    # one ragged target against the oracle directly
+    t = tg[-1]
+    A, B = t.make_ab(0)
+    Wd, Wb = oracle.merge(w0_host[-1], B, A, t.scale, want_bf16=(dtype == "bf16"))
+    got = to_host(outs[-1])
+    if dtype == "bf16":
+        _check_bf16_merge(got, Wd, Wb, w0_host[-1], B, A, t.scale, t.r, "batch " + t.name)
+    else:
+        assert rel_fro(as_f64(got), Wd) <= TOL[dtype]
+
+
+def test_batch_full_model_pass_matches_per_target(gpu_lib):
+    """All 36 x 7 targets in one call, bitwise equal to one call per target."""
+    import torch
+    tg = synth.merge_targets(36)
+    w0, a, b, one, outs = [], [], [], [], []
+    for t in tg:
+        w0.append(synth.device_normal(t.cfg, t.case, synth.TW, (t.N, t.K), t.var_w0, "bf16"))
+        a.append(synth.device_normal(t.cfg, t.case, synth.TA, (t.r, t.K), 1.0 / t.K, "bf16"))
+        b.append(synth.device_normal(t.cfg, t.case, synth.TB, (t.N, t.r), t.var_b, "bf16"))
+    for i, t in enumerate(tg):
+        one.append(gpu_lib.merge(w0[i], b[i], a[i], t.scale))
+        outs.append(torch.empty_like(w0[i]))
+    gpu_lib.merge_batch([(w0[i], b[i], a[i], t.scale, outs[i]) for i, t in enumerate(tg)])
+    torch.cuda.synchronize()
+    for i in range(len(tg)):
+        assert torch.equal(outs[i].view(torch.int16), one[i].view(torch.int16)), tg[i].name
