@@ -68,8 +68,10 @@ typedef enum lora_dtype {
     LORA_BF16 = 1
 } lora_dtype;
 
-/* Forward variants.  AUTO picks DECODE for bf16 with M <= LORA_DECODE_MAX_M,
- * TILED otherwise.  Forcing one is for tests and measurement. */
+/* Forward variants.  AUTO picks DECODE for bf16 with M <= LORA_DECODE_AUTO_M
+ * and r <= 32, TILED otherwise (for 16 < M <= 64 the tiled kernel runs a
+ * 64 x 32 tile streaming W with a deep stage ring, faster there than the
+ * decode kernel).  Forcing one is for tests and measurement. */
 typedef enum lora_variant {
     LORA_VARIANT_AUTO = 0,
     LORA_VARIANT_TILED = 1,   /* MFMA-tiled fused forward, any M */
@@ -78,6 +80,7 @@ typedef enum lora_variant {
 
 #define LORA_MAX_RANK 256
 #define LORA_DECODE_MAX_M 64
+#define LORA_DECODE_AUTO_M 16
 
 /*
  * lora_fwd -- fused LoRA linear forward   [fastaf], "FWD kernel speedup".

@@ -63,7 +63,7 @@ int check_fwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void*
 }
 
 int pick(int dtype, int64_t M, int64_t r) {
-  if (dtype == LORA_BF16 && M <= LORA_DECODE_MAX_M && r <= lora::kDecodeMaxRank)
+  if (dtype == LORA_BF16 && M <= LORA_DECODE_AUTO_M && r <= lora::kDecodeMaxRank)
     return LORA_VARIANT_DECODE;
   return LORA_VARIANT_TILED;
 }

@@ -538,11 +538,19 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 // whole 128-B lines per row.
 template <int RP>
 using Big = Cfg<256, 256, 2, 4, RP, 2, 64>;
+// Tall: 64 x 32, 4 waves (4 x 1), eight 64-deep stages in flight, for few
+// tokens (M <= 64): the cost is streaming W and re-reading X from L2, so the
+// tile is narrow and the ring deep.
+template <int RP>
+using Tall = Cfg<64, 32, 4, 1, RP, 8, 64>;
 template <int RP>
 using Mid = Cfg<128, 128, 4, 2, RP, 2, 64>;
 
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
+  if constexpr (RP <= 32) {
+    if (a.M <= 64) return launch<Tall<RP>>(a, s);
+  }
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   if constexpr (RP <= 64) {
     if (big_tiles >= 256) return launch<Big<RP>>(a, s);

@@ -41,7 +41,9 @@ def test_version_and_status_strings():
 
 def test_variant_pick():
     assert rg.fwd_pick(rg.LORA_BF16, 1, 4096, 4096, 16) == 2
-    assert rg.fwd_pick(rg.LORA_BF16, 64, 4096, 4096, 16) == 2
+    assert rg.fwd_pick(rg.LORA_BF16, 16, 4096, 4096, 16) == 2
+    assert rg.fwd_pick(rg.LORA_BF16, 17, 4096, 4096, 16) == 1      # tall tiles beyond 16 tokens
+    assert rg.fwd_pick(rg.LORA_BF16, 64, 4096, 4096, 16) == 1
     assert rg.fwd_pick(rg.LORA_BF16, 65, 4096, 4096, 16) == 1
     assert rg.fwd_pick(rg.LORA_BF16, 8, 4096, 4096, 64) == 1      # rank above the decode kernel's
     assert rg.fwd_pick(rg.LORA_F32, 8, 512, 512, 16) == 1

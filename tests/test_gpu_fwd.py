@@ -110,6 +110,8 @@ EDGE = [
     (77, 64, 64, 100, "bf16", "tiled"),
     (130, 260, 72, 256, "bf16", "tiled"),
     (257, 129, 200, 128, "bf16", "tiled"),
+    (40, 97, 264, 20, "bf16", "tiled"),         # tall tiles: ragged N, rank 20
+    (64, 4100, 2056, 32, "bf16", "tiled"),
     (33, 4100, 2056, 16, "bf16", "decode"),
     (64, 513, 4104, 32, "bf16", "decode"),
     (17, 513, 4104, 20, "bf16", "decode"),
@@ -200,6 +202,7 @@ INT_CASES = [
     (67, 130, 200, 2, 2.0, "bf16", "tiled"),
     (130, 67, 256, 5, 0.5, "bf16", "tiled"),
     (64, 70, 136, 1, 1.0, "bf16", "decode"),
+    (61, 70, 136, 2, 2.0, "bf16", "tiled"),
     (9, 33, 256, 3, 2.0, "bf16", "decode"),
     (67, 130, 200, 2, 2.0, "f32", "tiled"),
 ]
