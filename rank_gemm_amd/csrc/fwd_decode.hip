@@ -29,28 +29,47 @@ namespace {
 
 constexpr uint32_t kDecOob = 0x80000000u;  // offset past any resource's range
 
-template <int MB, int RB, int U, int NW>
+typedef __attribute__((address_space(3))) void lds_void;
+
+// AL: A (and, with XL, the single X row) reach the waves through LDS: each
+// wave stages the rows of its own K range with 16-B-per-lane DMA loads
+// (buffer_load ... lds), whole 128-B lines per instruction, instead of
+// 16-row x 64-B register loads; the MFMA fragments are then read from LDS.
+template <int MB, int RB, int U, int NW, bool AL, bool XL>
 struct Dec {
   static constexpr int RP = RB * 16;
+  static constexpr int kRowB = U * 256;                   // bytes of a staged row per round
+  static constexpr int kChunks = U * 16;                  // 16-B chunks per staged row
+  static constexpr int kAB = AL ? NW * RP * kRowB : 0;    // per-wave A regions
+  static constexpr int kXB = XL ? NW * kRowB : 0;         // per-wave X row
   static constexpr int kSlots = MB * (1 + RB);            // f32x4 partials per lane
   static constexpr int kRedB = NW * kSlots * kWave * 16;  // LDS for the reduction
   static constexpr int kTS = RP + 1;                      // T row stride (floats)
   static constexpr int kTB = MB * 16 * kTS * 4;           // T rows for the epilogue
-  static constexpr int kLds = kRedB + kTB;
+  static constexpr int kRedOff = kAB + kXB;
+  static constexpr int kLds = kRedOff + kRedB + kTB;
   static_assert(kLds <= 160 * 1024, "LDS budget");
+  static_assert(!AL || (MB == 1 && (kRowB == 512 || kRowB == 1024)), "LDS staging shape");
+  static_assert(!XL || (AL && kRowB == 1024), "X staging: one full 1-KiB DMA per round");
 };
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-template <int MB, int RB, int U, int NW>
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MB, int RB, int U, int NW, bool AL, bool XL>
 __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
     int64_t ldy, int b_vec) {
-  using C = Dec<MB, RB, U, NW>;
+  using C = Dec<MB, RB, U, NW, AL, XL>;
   constexpr int RP = C::RP;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -99,32 +118,67 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
     for (int jb = 0; jb < RB; ++jb) tacc[mb][jb] = zero4();
   }
 
+  // Wave w takes U consecutive 128-deep blocks per round: K range
+  // [128 kbw, 128 (kbw + U)) with kbw = (round NW + w) U.
   const int nkb = (K + 127) >> 7;
-  for (int kb0 = wave; kb0 < nkb; kb0 += NW * U) {
+  unsigned char* as = smem + wave * (RP * C::kRowB);            // AL: this wave's A rows
+  unsigned char* xs = smem + C::kAB + wave * C::kRowB;          // XL: this wave's X row
+  for (int kbw = wave * U; kbw < nkb; kbw += NW * U) {
     // Byte offset of each (block, substep) chunk within a row, or past the
-    // range when the block or the 8-element chunk lies beyond K.
+    // range when the 8-element chunk lies beyond K.
     uint32_t off[U][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kb = kb0 + NW * u;
+      const int kb = kbw + u;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int k = kb * 128 + q * 32 + lg * 8;
-        off[u][q] = (kb < nkb && k < K) ? (uint32_t)(kb * 256 + q * 64) : kDecOob;
+        off[u][q] = k < K ? (uint32_t)(kb * 256 + q * 64) : kDecOob;
       }
     }
     // X and A first: they come from L2 and leave the L1's miss queue
     // quickly, and the T MFMAs run on them while W streams in behind.
     u32x4 w[U][4], a[U][RB][4], x[U][MB][4];
+    if constexpr (AL) {
+      // Staged row j holds chunk c of the round's K range in slot c ^ (j % 16)
+      // (conflict-free 16-row fragment reads); a 1-KiB DMA covers
+      // 1024 / kRowB rows, lane i writing slot i % kChunks.
+      constexpr int kRowsPerDma = 1024 / C::kRowB;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) x[u][mb][q] = bload(rx, xbase[mb] + off[u][q]);
-#pragma unroll
-        for (int jb = 0; jb < RB; ++jb) a[u][jb][q] = bload(ra, abase[jb] + off[u][q]);
+      for (int d = 0; d < RP / kRowsPerDma; ++d) {
+        const int j = d * kRowsPerDma + lane / C::kChunks;
+        const int c = (lane % C::kChunks) ^ (j & 15);
+        const int k = kbw * 128 + c * 8;
+        const uint32_t vo = k < K ? (uint32_t)j * (uint32_t)lda * 2 + (uint32_t)k * 2 : kDecOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(as + d * 1024), 16, vo, 0, 0, 0);
       }
+      if constexpr (XL) {
+        // The X row (M == 1): one 1-KiB DMA, lane i chunk i, unswizzled (all
+        // sixteen row lanes read the same chunk: a broadcast).
+        const int k = kbw * 128 + lane * 8;
+        const uint32_t vo = k < K ? (uint32_t)k * 2 : kDecOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)xs, 16, vo, 0, 0, 0);
+      }
+      // Nothing below may be scheduled before the DMAs: the wait further
+      // down counts on them being the oldest loads of the round.
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!XL) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[u][0][q] = bload(rx, xbase[0] + off[u][q]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) x[u][mb][q] = bload(rx, xbase[mb] + off[u][q]);
+#pragma unroll
+          for (int jb = 0; jb < RB; ++jb) a[u][jb][q] = bload(ra, abase[jb] + off[u][q]);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -132,6 +186,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
     // Keep the whole round's loads in flight: no MFMA (and no wait) is
     // scheduled before the last load is issued.
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (AL) {
+      // The DMAs were issued first: waiting until only the later register
+      // loads (W, and X unless staged) are outstanding completes them.
+      wait_vmcnt<U * 4 * (XL ? 1 : 2)>();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = u * 16 + q * 4 + lg;
+#pragma unroll
+          for (int jb = 0; jb < RB; ++jb) {
+            const int j = jb * 16 + lrow;
+            a[u][jb][q] = *reinterpret_cast<const u32x4*>(as + j * C::kRowB + ((c ^ lrow) << 4));
+          }
+          if constexpr (XL) x[u][0][q] = *reinterpret_cast<const u32x4*>(xs + (c << 4));
+        }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -151,7 +223,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
   }
 
   // Cross-wave reduction in a fixed order (wave 0 + wave 1 + ...).
-  f32x4* red = reinterpret_cast<f32x4*>(smem);
+  f32x4* red = reinterpret_cast<f32x4*>(smem + C::kRedOff);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     red[(wave * C::kSlots + mb * (1 + RB)) * kWave + lane] = yacc[mb];
@@ -163,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
   const bool active = wave < MB;
   const int mb = active ? wave : 0;
   f32x4 y = zero4();
-  float* tl = reinterpret_cast<float*>(smem + C::kRedB) + mb * 16 * C::kTS;
+  float* tl = reinterpret_cast<float*>(smem + C::kRedOff + C::kRedB) + mb * 16 * C::kTS;
   if (active) {
     f32x4 t[RB];
 #pragma unroll
@@ -208,11 +280,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
   }
 }
 
-template <int MB, int RB, int U>
+template <int MB, int RB, int U, bool AL = false, bool XL = false>
 hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = 8;
-  using C = Dec<MB, RB, U, NW>;
-  auto kern = fwd_decode_bf16_kernel<MB, RB, U, NW>;
+  using C = Dec<MB, RB, U, NW, AL, XL>;
+  auto kern = fwd_decode_bf16_kernel<MB, RB, U, NW, AL, XL>;
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -235,7 +307,11 @@ hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
 template <int RB>
 hipError_t launch_dec_rb(const FwdArgs& a, hipStream_t s) {
   switch ((a.M + 15) / 16) {
-    case 1: return launch_dec<1, RB, RB == 1 ? 4 : 3>(a, s);
+    case 1:
+      if constexpr (RB == 1) {
+        if (a.M == 1) return launch_dec<1, 1, 4, true, true>(a, s);
+      }
+      return launch_dec<1, RB, RB == 1 ? 4 : 2, true, false>(a, s);
     case 2: return launch_dec<2, RB, 2>(a, s);
     case 3: return launch_dec<3, RB, RB == 1 ? 2 : 1>(a, s);
     default: return launch_dec<4, RB, RB == 1 ? 2 : 1>(a, s);
