@@ -23,6 +23,8 @@
 //     T -> scale * T -> bf16 -> LDS; B[BN x RP] -> LDS (zero padded)
 //     acc += (s T) B^T               (MFMA over the rank)
 //     acc -> bf16 -> LDS -> coalesced 16-B stores of Y.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -86,6 +88,11 @@ struct Cfg {
   static constexpr int kYS = BN + 8;                // output staging row stride (elements)
   static constexpr int kYB = BM * kYS * 2;
   static constexpr int kLds = cmax(STAGES * kStageB, cmax(kEpiB, kYB));
+  // With T kept across the N tiles of a group: T after the ring, the B tile
+  // and the output staging inside it.
+  static constexpr int kTOffG = STAGES * kStageB;
+  static constexpr int kLdsG = kTOffG + BM * kTS * 2;
+  static_assert(BN * kTS * 2 <= kTOffG && kYB <= kTOffG, "group epilogue fits in the ring");
   static constexpr int kTSlots = (TM * RB + WN - 1) / WN;  // T accumulators per wave
   static constexpr int kGroup = 4;         // M tiles per group (XCD-contiguous ids)
   static constexpr int kGroupShared = 16;  // M tiles swept together by all XCDs
@@ -165,8 +172,12 @@ __device__ __forceinline__ void t_update_ab(const u32x4 (&a)[C::TM], const u32x4
 // Wait until this wave's loads of all but its `Newer` most recent stages have
 // landed.  Loads complete in issue order, so the count must be this wave's
 // own per-stage load count: waves that also load an A row issue one more.
-template <class C, int Newer>
+template <class C, int Newer, bool WT = true>
 __device__ __forceinline__ void wait_stages(int wave) {
+  if constexpr (!WT) {
+    wait_vmcnt<Newer * (C::kXL + C::kWL)>();  // stages without A loads
+    return;
+  }
   if constexpr (C::kLoadsHi != C::kLoadsLo) {
     if (wave < C::kAN % C::NW) {
       wait_vmcnt<Newer * C::kLoadsHi>();
@@ -184,7 +195,7 @@ __device__ __forceinline__ uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_r
 // slots and (waves below kAN) its A slot.  Slot s of a matrix is the wave's
 // slot 0 plus s * NW 1-KiB loads, i.e. a wave-uniform byte stride.  Lanes
 // whose 16-B chunk lies past K read zeros.
-template <class C>
+template <class C, bool WT = true>
 __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0, int K, int wave,
                                             int lchunk, __amdgpu_buffer_rsrc_t rx,
                                             __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
@@ -203,6 +214,7 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rw, (lds_void*)(base + C::BM * kRowB + (wave + s * C::NW) * 1024), 16,
         off_or_oob(kin, vw + sgpr(s * sw + kb)), 0, 0, 0);
+  if constexpr (!WT) return;  // T already known: no A rows
 #pragma unroll
   for (int s = 0; s < C::kAL; ++s)
     if (wave + s * C::NW < C::kAN)
@@ -211,7 +223,13 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
           off_or_oob(kin, va + sgpr(s * sa + kb)), 0, 0, 0);
 }
 
-template <class C>
+// G > 1: a workgroup computes G consecutive N tiles of one M tile.  The first
+// tile runs the fused K loop (base and T = X A^T); its epilogue keeps s T
+// (bf16) in an LDS region outside the stage ring, and the later tiles run
+// the K loop without A loads or T MFMAs and reuse it.  For large ranks this
+// removes the per-tile recomputation of T (2 M K r flop per N tile, as much
+// as the base contraction when r = BN).  tiles_n then counts groups of G.
+template <class C, int G>
 __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
@@ -238,38 +256,35 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // them at once (W shared through the last-level cache).  The host picks the
   // mode with fewer L2 fills.  Mode 0: tiles grouped along M (G at a time)
   // within XCD-contiguous id ranges.
-  int m0, n0;
+  int m0, ng0;  // ng0: first N column of the group, in units of BN
   {
     const int total = tiles_m * tiles_n;
     if (map_mode == 1) {
-      constexpr int G = C::kGroupShared;
+      constexpr int GS = C::kGroupShared;
       const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nper = tiles_n >> 3;
-      const int sg = slot / (G * nper), within = slot % (G * nper);
-      m0 = (sg * G + within % G) * BM;
-      n0 = (xcd * nper + within / G) * BN;
+      const int sg = slot / (GS * nper), within = slot % (GS * nper);
+      m0 = (sg * GS + within % GS) * BM;
+      ng0 = (xcd * nper + within / GS) * G;
     } else if (map_mode == 2) {
       const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, mper = tiles_m >> 3;
       m0 = (xcd * mper + slot % mper) * BM;
-      n0 = (slot / mper) * BN;
+      ng0 = (slot / mper) * G;
     } else {
-      constexpr int G = C::kGroup;
+      constexpr int GS = C::kGroup;
       const int pid = xcd_contiguous_id(blockIdx.x, total);
-      const int group = pid / (G * tiles_n);
-      const int first_m = group * G;
-      const int gsize = min(tiles_m - first_m, G);
-      const int local = pid % (G * tiles_n);
+      const int group = pid / (GS * tiles_n);
+      const int first_m = group * GS;
+      const int gsize = min(tiles_m - first_m, GS);
+      const int local = pid % (GS * tiles_n);
       m0 = (first_m + local % gsize) * BM;
-      n0 = (local / gsize) * BN;
+      ng0 = (local / gsize) * G;
     }
   }
 
   // ---- buffer resources from the tile's first row to its last valid row.
   const int xrows = min(BM, M - m0);
-  const int wrows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(X + (int64_t)m0 * ldx), 0, (int)(xrows * ldx * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (int64_t)n0 * ldw), 0, (int)(wrows * ldw * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       (void*)A, 0, (int)(r * lda * 2), 0x00020000);
 
@@ -286,14 +301,26 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const uint32_t sw = (uint32_t)(NW * kRPL * ldw * 2);
   const uint32_t sa = (uint32_t)(NW * kRPL * lda * 2);
 
+  const int rot = ring_rot<C>(wn);
   f32x4 acc[TM][TN];
+  f32x4 tacc[C::kTSlots];
+#pragma unroll
+  for (int s = 0; s < C::kTSlots; ++s) tacc[s] = zero4();
+
+  for (int g = 0; g < G; ++g) {
+  const int n0 = (ng0 + g) * BN;
+  if (n0 >= N) break;  // uniform: the group's last tiles may lie past N
+  const int wrows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * ldw), 0, (int)(wrows * ldw * 2), 0x00020000);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
-  f32x4 tacc[C::kTSlots];
-#pragma unroll
-  for (int s = 0; s < C::kTSlots; ++s) tacc[s] = zero4();
+
+  // The K loop, with (WT) or without the down-projection.
+  auto kloop = [&](auto wt) {
+  constexpr bool WT = decltype(wt)::value;
 
   // K loop, software-pipelined three ways.  A stage holds BK = 32 * NSUB
   // k-values; the MFMAs consume it in NSUB substeps of k32.  Substep u of
@@ -309,13 +336,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int nk = (K + BK - 1) / BK;
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
-    issue_stage<C>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+    issue_stage<C, WT>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
 
-  const int rot = ring_rot<C>(wn);
   const int xrow0 = wm * TM * 16 + lrow;  // + 16 * ring_row_block(k) for ring slot k
   const int wrow0 = wn * TN * 16 + lrow;
   Frags<C> cur;
-  wait_stages<C, STAGES - 1>(wave);
+  wait_stages<C, STAGES - 1, WT>(wave);
   __builtin_amdgcn_s_barrier();
   {
     const unsigned char* xs = smem;
@@ -328,9 +354,11 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       cur.b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, lk));
+    if constexpr (WT) {
 #pragma unroll
-    for (int u = 0; u < C::kTF; ++u)
-      cur.t[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk));
+      for (int u = 0; u < C::kTF; ++u)
+        cur.t[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk));
+    }
   }
 
   // One substep: MFMAs from (a ring, bc, tc); the next substep's W and A
@@ -339,16 +367,16 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   auto substep = [&](bool sync, int rslot, int nslot, int kt, int u, u32x4 (&bc)[TN],
                      u32x4 (&tc)[C::kTF], u32x4 (&bx)[TN], u32x4 (&tx)[C::kTF]) {
     // T MFMAs first: they keep the MFMA pipe busy across the barrier.
-    t_update_ab<C>(cur.a, tc, tacc);
+    if constexpr (WT) t_update_ab<C>(cur.a, tc, tacc);
     if (sync) {
       // Stage kt+1 has landed once at most STAGES-2 later stages are in
       // flight; this wave's reads of stage kt are complete.  After the
       // barrier every wave is past both.  A bare s_barrier: a fence would
       // drain every stage in flight.
-      wait_stages<C, STAGES - 2>(wave);
+      wait_stages<C, STAGES - 2, WT>(wave);
       __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
-      issue_stage<C>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx,
+      issue_stage<C, WT>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx,
                      sw, sa);
     }
     const unsigned char* xs = smem + (sync ? nslot : rslot) * C::kStageB;
@@ -359,9 +387,11 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       bx[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, cc));
+    if constexpr (WT) {
 #pragma unroll
-    for (int f = 0; f < C::kTF; ++f)
-      tx[f] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, f) * 16 + lrow, cc));
+      for (int f = 0; f < C::kTF; ++f)
+        tx[f] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, f) * 16 + lrow, cc));
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -371,7 +401,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     }
     // Interleave DMA issues and LDS reads between the MFMAs.
     constexpr int kDma = C::kXL + C::kWL;
-    constexpr int kReads = TN + C::kTF + TM;
+    constexpr int kReads = TN + (WT ? C::kTF : 0) + TM;
     constexpr int kMfma = TM * TN;
     if (sync) {
 #pragma unroll
@@ -412,11 +442,16 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     }
     rslot = nslot;
   }
+  };  // kloop
+  if (g == 0) kloop(std::true_type{});
+  else kloop(std::false_type{});
   __syncthreads();
 
-  // ---- epilogue 1: scaled T (bf16) and the B tile into LDS.
-  uint16_t* ts = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* bs = ts + BM * C::kTS;
+  // ---- epilogue 1: scaled T (bf16) and the B tile into LDS.  With G > 1,
+  // T lives past the stage ring and is written by the first tile only.
+  uint16_t* ts = reinterpret_cast<uint16_t*>(smem + (G > 1 ? C::kTOffG : 0));
+  uint16_t* bs = G > 1 ? reinterpret_cast<uint16_t*>(smem) : ts + BM * C::kTS;
+  if (g == 0) {
 #pragma unroll
   for (int sl = 0; sl < C::kTSlots; ++sl) {
     const int i = ring_row_block<C>(t_ring_slot<C>(sl), rot);
@@ -426,6 +461,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       const int row = wm * TM * 16 + i * 16 + lk * 4 + q;
       ts[row * C::kTS + j] = j < r ? f2bf(scale * tacc[sl][q]) : uint16_t(0);
     }
+  }
   }
   for (int e = tid; e < BN * RP; e += C::NT) {
     const int n = e / RP, j = e % RP;
@@ -494,12 +530,14 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       for (int q = 0; q < 8 && gn + q < N; ++q) dst[q] = src[q];
     }
   }
+  if (G > 1) __syncthreads();  // the next tile's loads reuse the staging area
+  }  // tiles of the group
 }
 
-template <class C>
+template <class C, int G = 1>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
-  const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
+  const int tiles_n = (int)((a.N + C::BN * G - 1) / (C::BN * G));  // groups of G N tiles
   const int y_vec = ((reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) && (a.ldy % 8 == 0);
   // L2 fills (in K-rows of X or W) of the two XCD-split mappings: mode 1
   // reads all of X on every XCD and W once per group of G M tiles; mode 2
@@ -515,15 +553,17 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
     if (ok1 && (!ok2 || f1 <= f2)) map_mode = 1;
     else if (ok2) map_mode = 2;
   }
-  auto kern = fwd_tiled_bf16_kernel<C>;
+  auto kern = fwd_tiled_bf16_kernel<C, G>;
+  constexpr int lds = G > 1 ? C::kLdsG : C::kLds;
+  static_assert(lds <= 160 * 1024, "LDS budget");
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(C::NT), C::kLds, s, (int)a.M, (int)a.N,
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(C::NT), lds, s, (int)a.M, (int)a.N,
                      (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.X), a.ldx,
                      static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
                      a.lda, static_cast<const uint16_t*>(a.B), a.ldb, a.scale,
@@ -554,6 +594,13 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   if constexpr (RP <= 64) {
     if (big_tiles >= 256) return launch<Big<RP>>(a, s);
+  }
+  if constexpr (RP == 128) {
+    // Rank 128 on 128 x 128 tiles: compute T once per 4 N tiles, when that
+    // still leaves a few workgroups per CU.  (Rank 256 does not fit the LDS
+    // budget with T kept; rank <= 64 takes 256 x 256 tiles at this size.)
+    const int64_t mid_tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+    if (a.N > 3 * 128 && mid_tiles >= 4 * 256) return launch<Mid<RP>, 4>(a, s);
   }
   return launch<Mid<RP>>(a, s);
 }

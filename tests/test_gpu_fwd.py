@@ -92,6 +92,22 @@ def test_cfg3_square_rank_sweep_sampled_rows(gpu_lib, c):
     assert np.isfinite(as_f64(got)).all()
 
 
+@pytest.mark.parametrize("M,N,K,r", [(4097, 4100, 264, 100), (4096, 4096, 136, 128)])
+def test_large_rank_groups_sampled_rows(gpu_lib, M, N, K, r):
+    """Large ranks on 128 x 128 tiles where a workgroup computes T once for a
+    group of N tiles: ragged M and N (the last group runs past N), ranks below
+    the padded rank, checked on sampled rows against the oracle."""
+    c = synth.FwdCase(f"grp{M}x{N}r{r}", 94, r, M, N, K, r, 2.0 * r, "bf16")
+    t = c.make()
+    got = _run(gpu_lib, t, c.scale)
+    rows = sample_rows(M, 32, seed=r)
+    ref = _oracle_rows(t, c.scale, rows)
+    err = rel_fro(as_f64(got[rows]), ref)
+    print(f"{c.name}: rows={len(rows)} rel_fro={err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.isfinite(as_f64(got)).all()
+
+
 # ------------------------------------------------------ shapes and edges
 
 def _rand_case(seed, M, N, K, r, dtype, var_b=0.02):
