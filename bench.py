@@ -14,7 +14,7 @@ W[4096,4096], rotated over 16 operand sets so the 256 MB last-level cache
 cannot hold them) and the merge of 36 layers x 7 targets at r = 32.
 
 --only NAME runs just one kernel a few times (for rocprofv3); NAME is one of
-cfg1, cfg2, q, v, sq8, sq16, sq64, sq128, dec1, dec8, dec64, merge, copy.
+tiny, mid, q, v, sq8, sq16, sq64, sq128, dec1, dec8, dec64, merge, copy.
 """
 from __future__ import annotations
 
@@ -118,7 +118,7 @@ def run_fwd_case(rg, c, steps, warmup, rotate=1, variant="auto", graph=False):
     import torch
     import synth
     sets = [synth.fwd_case_on_device(
-        synth.FwdCase(c.name, c.cfg, c.case + 100 * i, c.M, c.N, c.K, c.r, c.alpha, c.dtype,
+        synth.FwdCase(c.name, c.group, c.case + 100 * i, c.M, c.N, c.K, c.r, c.alpha, c.dtype,
                       var_b=c.var_b) if i else c) for i in range(rotate)]
     outs = [torch.empty((c.M, c.N), dtype=sets[0]["X"].dtype, device="cuda") for _ in sets]
 
@@ -157,9 +157,9 @@ def run_merge_pass(rg, steps, warmup, layers=36):
     tg = synth.merge_targets(layers)
     w0, a, b, wi = [], [], [], []
     for t in tg:
-        w0.append(synth.device_normal(t.cfg, t.case, synth.TW, (t.N, t.K), t.var_w0, "bf16"))
-        a.append(synth.device_normal(t.cfg, t.case, synth.TA, (t.r, t.K), 1.0 / t.K, "bf16"))
-        b.append(synth.device_normal(t.cfg, t.case, synth.TB, (t.N, t.r), t.var_b, "bf16"))
+        w0.append(synth.device_normal(t.group, t.case, synth.TW, (t.N, t.K), t.var_w0, "bf16"))
+        a.append(synth.device_normal(t.group, t.case, synth.TA, (t.r, t.K), 1.0 / t.K, "bf16"))
+        b.append(synth.device_normal(t.group, t.case, synth.TB, (t.N, t.r), t.var_b, "bf16"))
         wi.append(torch.empty_like(w0[-1]))
 
     def launch(i):
@@ -245,7 +245,7 @@ def main():
     if args.only:
         return only(rg, args.only, args.steps, args.warmup)
 
-    head = synth.CFG2
+    head = synth.MID
     t = head.make()
 
     def dev(a):
@@ -264,7 +264,7 @@ def main():
     ms_per_step = region_ms / args.steps
     value = head.flops() / (ms_per_step * 1e-3) / 1e12
     achieved = value
-    traffic = _traffic("fwd_tiled_cfg2", ["fwd_tiled.hip", "common.h"])
+    traffic = _traffic("fwd_tiled_mid_x4096x1024_w1024_r16", ["fwd_tiled.hip", "common.h"])
 
     line = {
         "metric": "fused LoRA fwd TFLOP/s (% bf16 MFMA peak); merge/decode GB/s (% HBM peak)",
@@ -289,11 +289,11 @@ def main():
 
     if not args.quick:
         work = []
-        for c in (synth.CFG3_Q, synth.CFG3_V):
+        for c in (synth.QPROJ, synth.VPROJ):
             work.append(run_fwd_case(rg, c, 30, 5))
-        for c in synth.CFG3_SQ:
+        for c in synth.SQUARE:
             work.append(run_fwd_case(rg, c, 10, 2))
-        for c in synth.CFG4:
+        for c in synth.DECODE:
             work.append(run_fwd_case(rg, c, 256, 32, rotate=16, graph=True))
         work.append(run_merge_pass(rg, 5, 1))
         line["workloads"] = work
@@ -307,10 +307,10 @@ def only(rg, name, steps, warmup):
     """One kernel, a few launches, for profiler runs."""
     import torch
     import synth
-    table = {"cfg1": synth.CFG1, "cfg2": synth.CFG2, "q": synth.CFG3_Q, "v": synth.CFG3_V,
-             "sq8": synth.CFG3_SQ[0], "sq16": synth.CFG3_SQ[1], "sq64": synth.CFG3_SQ[2],
-             "sq128": synth.CFG3_SQ[3], "dec1": synth.CFG4[0], "dec8": synth.CFG4[1],
-             "dec64": synth.CFG4[2]}
+    table = {"tiny": synth.TINY, "mid": synth.MID, "q": synth.QPROJ, "v": synth.VPROJ,
+             "sq8": synth.SQUARE[0], "sq16": synth.SQUARE[1], "sq64": synth.SQUARE[2],
+             "sq128": synth.SQUARE[3], "dec1": synth.DECODE[0], "dec8": synth.DECODE[1],
+             "dec64": synth.DECODE[2]}
     if name in table:
         c = table[name]
         dec = name.startswith("dec")

@@ -5,7 +5,7 @@ the benchmark.  It holds no step of the method's arithmetic: it only draws
 normal samples, narrows them to the storage precision and names the workloads.
 
 Recipe (stated once, used everywhere):
-  * ``rng = numpy.random.Generator(PCG64(SeedSequence([cfg, case, tensor])))``
+  * ``rng = numpy.random.Generator(PCG64(SeedSequence([group, case, tensor])))``
   * ``rng.standard_normal(shape, float64) * std`` where ``std = sqrt(var)``:
     the pages' ``N(0, v)`` is read as mean 0, *variance* v.
   * narrowed to float32 with round-to-nearest-even (numpy ``astype``), then,
@@ -27,8 +27,8 @@ import numpy as np
 TX, TW, TA, TB = 0, 1, 2, 3
 
 
-def _rng(cfg: int, case: int, tensor: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg, case, tensor])))
+def _rng(group: int, case: int, tensor: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([group, case, tensor])))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -52,10 +52,10 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def normal(cfg: int, case: int, tensor: int, shape: Tuple[int, ...], var: float,
+def normal(group: int, case: int, tensor: int, shape: Tuple[int, ...], var: float,
            dtype: str) -> np.ndarray:
     """One seeded tensor: N(0, var) in fp64 -> fp32 (RNE) -> bf16 (RNE) if asked."""
-    g = _rng(cfg, case, tensor)
+    g = _rng(group, case, tensor)
     x = (g.standard_normal(shape, dtype=np.float64) * math.sqrt(var)).astype(np.float32)
     if dtype == "f32":
         return x
@@ -78,7 +78,7 @@ def to_f64(x: np.ndarray) -> np.ndarray:
 @dataclass(frozen=True)
 class FwdCase:
     name: str
-    cfg: int
+    group: int      # seed group (first SeedSequence word)
     case: int
     M: int
     N: int
@@ -90,7 +90,7 @@ class FwdCase:
     var_w: Optional[float] = None      # default 1/K
     var_a: Optional[float] = None      # default 1/K
     var_b: float = 0.02
-    x_from: Optional[Tuple[int, int]] = None   # (cfg, case) whose X this case shares
+    x_from: Optional[Tuple[int, int]] = None   # (group, case) whose X this case shares
 
     @property
     def scale(self) -> float:
@@ -109,22 +109,22 @@ class FwdCase:
         vw = self.var_w if self.var_w is not None else 1.0 / self.K
         va = self.var_a if self.var_a is not None else 1.0 / self.K
         out: Dict[str, np.ndarray] = {}
-        xc = self.x_from if self.x_from is not None else (self.cfg, self.case)
+        xc = self.x_from if self.x_from is not None else (self.group, self.case)
         if "X" in parts:
             out["X"] = normal(xc[0], xc[1], TX, (self.M, self.K), self.var_x, self.dtype)
         if "W" in parts:
-            out["W"] = normal(self.cfg, self.case, TW, (self.N, self.K), vw, self.dtype)
+            out["W"] = normal(self.group, self.case, TW, (self.N, self.K), vw, self.dtype)
         if "A" in parts:
-            out["A"] = normal(self.cfg, self.case, TA, (self.r, self.K), va, self.dtype)
+            out["A"] = normal(self.group, self.case, TA, (self.r, self.K), va, self.dtype)
         if "B" in parts:
-            out["B"] = normal(self.cfg, self.case, TB, (self.N, self.r), self.var_b, self.dtype)
+            out["B"] = normal(self.group, self.case, TB, (self.N, self.r), self.var_b, self.dtype)
         return out
 
 
 @dataclass(frozen=True)
 class MergeTarget:
     name: str
-    cfg: int
+    group: int      # seed group (first SeedSequence word)
     case: int
     N: int        # out features
     K: int        # in features
@@ -146,31 +146,33 @@ class MergeTarget:
         return 2.0 * self.r * self.N * self.K
 
     def make_w0(self) -> np.ndarray:
-        return normal(self.cfg, self.case, TW, (self.N, self.K), self.var_w0, self.dtype)
+        return normal(self.group, self.case, TW, (self.N, self.K), self.var_w0, self.dtype)
 
     def make_ab(self, cycle: int = 0) -> Tuple[np.ndarray, np.ndarray]:
-        A = normal(self.cfg, self.case, 10 * cycle + TA, (self.r, self.K), 1.0 / self.K, self.dtype)
-        B = normal(self.cfg, self.case, 10 * cycle + TB, (self.N, self.r), self.var_b, self.dtype)
+        A = normal(self.group, self.case, 10 * cycle + TA, (self.r, self.K), 1.0 / self.K, self.dtype)
+        B = normal(self.group, self.case, 10 * cycle + TB, (self.N, self.r), self.var_b, self.dtype)
         return A, B
 
 
-# cfg 1: tiny fp32 LoRA linear.
-CFG1 = FwdCase("tiny_f32_x128x512_w512x512_r16", 1, 0, 128, 512, 512, 16, 32.0, "f32")
-# cfg 2: bf16 mid-size, 4 x 1024 tokens.
-CFG2 = FwdCase("bf16_mid_x4096x1024_w1024x1024_r16", 2, 0, 4096, 1024, 1024, 16, 32.0, "bf16")
-# cfg 3: transformer projection shapes (hidden 2560, 8192 tokens) and a large square sweep.
-CFG3_Q = FwdCase("bf16_qproj_x8192x2560_w4096x2560_r32", 3, 0, 8192, 4096, 2560, 32, 64.0, "bf16")
-CFG3_V = FwdCase("bf16_vproj_x8192x2560_w1024x2560_r32", 3, 1, 8192, 1024, 2560, 32, 64.0, "bf16",
+# Tiny fp32 LoRA linear (seed group 1).
+TINY = FwdCase("tiny_f32_x128x512_w512x512_r16", 1, 0, 128, 512, 512, 16, 32.0, "f32")
+# bf16 mid-size, 4 x 1024 tokens (seed group 2).
+MID = FwdCase("bf16_mid_x4096x1024_w1024x1024_r16", 2, 0, 4096, 1024, 1024, 16, 32.0, "bf16")
+# Transformer projection shapes (hidden 2560, 8192 tokens) and a large square
+# sweep (seed group 3).
+QPROJ = FwdCase("bf16_qproj_x8192x2560_w4096x2560_r32", 3, 0, 8192, 4096, 2560, 32, 64.0, "bf16")
+VPROJ = FwdCase("bf16_vproj_x8192x2560_w1024x2560_r32", 3, 1, 8192, 1024, 2560, 32, 64.0, "bf16",
                  x_from=(3, 0))
-CFG3_SQ = tuple(
+SQUARE = tuple(
     FwdCase(f"bf16_square_x16384x8192_w8192x8192_r{r}", 3, 2 + i, 16384, 8192, 8192, r, 2.0 * r, "bf16")
     for i, r in enumerate((8, 16, 64, 128)))
-# cfg 4: decode-shaped, bandwidth-bound.
-CFG4 = tuple(
+# Decode-shaped, bandwidth-bound (seed group 4).
+DECODE = tuple(
     FwdCase(f"bf16_decode_m{m}_w4096x4096_r16", 4, i, m, 4096, 4096, 16, 32.0, "bf16")
     for i, m in enumerate((1, 8, 64)))
 
-# cfg 5: merge from pristine over 36 layers x 7 targets of a hidden-2560 model, rank 32.
+# Merge from pristine over 36 layers x 7 targets of a hidden-2560 model, rank 32
+# (seed group 5).
 MERGE_LAYERS = 36
 MERGE_TARGET_SHAPES: List[Tuple[str, int, int]] = [
     ("q", 4096, 2560), ("k", 1024, 2560), ("v", 1024, 2560), ("o", 2560, 4096),
@@ -186,27 +188,27 @@ def merge_targets(layers: int = MERGE_LAYERS) -> List[MergeTarget]:
     return out
 
 
-FWD_CASES: List[FwdCase] = [CFG1, CFG2, CFG3_Q, CFG3_V, *CFG3_SQ, *CFG4]
+FWD_CASES: List[FwdCase] = [TINY, MID, QPROJ, VPROJ, *SQUARE, *DECODE]
 
 
 # ---------------------------------------------------------------------------
 # Device-side generation for throughput runs whose inputs are too large to
 # draw on the host in reasonable time (the 7.3 GB merge set, the square sweep).
 # Same distributions, a different generator: torch's Philox stream on the
-# device, seeded from (cfg, case, tensor).  Parity tests use the numpy recipe.
+# device, seeded from (group, case, tensor).  Parity tests use the numpy recipe.
 # ---------------------------------------------------------------------------
 
-def device_seed(cfg: int, case: int, tensor: int) -> int:
-    return int(np.random.SeedSequence([cfg, case, tensor]).generate_state(1, np.uint64)[0]
+def device_seed(group: int, case: int, tensor: int) -> int:
+    return int(np.random.SeedSequence([group, case, tensor]).generate_state(1, np.uint64)[0]
                & 0x7FFFFFFFFFFFFFFF)
 
 
-def device_normal(cfg: int, case: int, tensor: int, shape, var: float, dtype: str,
+def device_normal(group: int, case: int, tensor: int, shape, var: float, dtype: str,
                   device="cuda"):
     """N(0, var) drawn on the device, fp32 then narrowed (bf16: nearest-even)."""
     import torch
     g = torch.Generator(device=device)
-    g.manual_seed(device_seed(cfg, case, tensor))
+    g.manual_seed(device_seed(group, case, tensor))
     x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
     x.mul_(math.sqrt(var))
     return x.to(torch.bfloat16) if dtype == "bf16" else x
@@ -215,10 +217,10 @@ def device_normal(cfg: int, case: int, tensor: int, shape, var: float, dtype: st
 def fwd_case_on_device(c: FwdCase, device="cuda"):
     vw = c.var_w if c.var_w is not None else 1.0 / c.K
     va = c.var_a if c.var_a is not None else 1.0 / c.K
-    xc = c.x_from if c.x_from is not None else (c.cfg, c.case)
+    xc = c.x_from if c.x_from is not None else (c.group, c.case)
     return {
         "X": device_normal(xc[0], xc[1], TX, (c.M, c.K), c.var_x, c.dtype, device),
-        "W": device_normal(c.cfg, c.case, TW, (c.N, c.K), vw, c.dtype, device),
-        "A": device_normal(c.cfg, c.case, TA, (c.r, c.K), va, c.dtype, device),
-        "B": device_normal(c.cfg, c.case, TB, (c.N, c.r), c.var_b, c.dtype, device),
+        "W": device_normal(c.group, c.case, TW, (c.N, c.K), vw, c.dtype, device),
+        "A": device_normal(c.group, c.case, TA, (c.r, c.K), va, c.dtype, device),
+        "B": device_normal(c.group, c.case, TB, (c.N, c.r), c.var_b, c.dtype, device),
     }

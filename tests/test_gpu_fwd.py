@@ -36,8 +36,8 @@ def _case_name(c):
 
 # ------------------------------------------------------------ the workloads
 
-def test_cfg1_tiny_fp32_full(gpu_lib):
-    c = synth.CFG1
+def test_tiny_fp32_full(gpu_lib):
+    c = synth.TINY
     t = c.make()
     got = _run(gpu_lib, t, c.scale)
     ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)
@@ -46,8 +46,8 @@ def test_cfg1_tiny_fp32_full(gpu_lib):
     assert err <= TOL["f32"]
 
 
-def test_cfg2_bf16_mid_full(gpu_lib):
-    c = synth.CFG2
+def test_mid_bf16_full(gpu_lib):
+    c = synth.MID
     t = c.make()
     got = _run(gpu_lib, t, c.scale)
     ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)
@@ -56,9 +56,9 @@ def test_cfg2_bf16_mid_full(gpu_lib):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("c", synth.CFG4, ids=_case_name)
+@pytest.mark.parametrize("c", synth.DECODE, ids=_case_name)
 @pytest.mark.parametrize("variant", ["decode", "tiled"])
-def test_cfg4_decode_shapes_full(gpu_lib, c, variant):
+def test_decode_shapes_full(gpu_lib, c, variant):
     t = c.make()
     got = _run(gpu_lib, t, c.scale, variant)
     ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)
@@ -67,8 +67,8 @@ def test_cfg4_decode_shapes_full(gpu_lib, c, variant):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("c", [synth.CFG3_Q, synth.CFG3_V], ids=_case_name)
-def test_cfg3_projection_sampled_rows(gpu_lib, c):
+@pytest.mark.parametrize("c", [synth.QPROJ, synth.VPROJ], ids=_case_name)
+def test_projection_sampled_rows(gpu_lib, c):
     t = c.make()
     got = _run(gpu_lib, t, c.scale)
     rows = sample_rows(c.M, 64, seed=c.case)
@@ -80,8 +80,8 @@ def test_cfg3_projection_sampled_rows(gpu_lib, c):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("c", synth.CFG3_SQ, ids=_case_name)
-def test_cfg3_square_rank_sweep_sampled_rows(gpu_lib, c):
+@pytest.mark.parametrize("c", synth.SQUARE, ids=_case_name)
+def test_square_rank_sweep_sampled_rows(gpu_lib, c):
     t = c.make()
     got = _run(gpu_lib, t, c.scale)
     rows = sample_rows(c.M, 24, seed=c.case)
@@ -243,7 +243,7 @@ def test_integer_inputs_bitwise(gpu_lib, M, N, K, r, s, dtype, variant):
         np.testing.assert_array_equal(got.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("c", [synth.CFG2, synth.CFG4[2], synth.CFG1], ids=_case_name)
+@pytest.mark.parametrize("c", [synth.MID, synth.DECODE[2], synth.TINY], ids=_case_name)
 def test_deterministic(gpu_lib, c):
     t = c.make()
     a = _run(gpu_lib, t, c.scale)

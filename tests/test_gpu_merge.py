@@ -217,9 +217,9 @@ def test_batch_full_model_pass_matches_per_target(gpu_lib):
     tg = synth.merge_targets(36)
     w0, a, b, one, outs = [], [], [], [], []
     for t in tg:
-        w0.append(synth.device_normal(t.cfg, t.case, synth.TW, (t.N, t.K), t.var_w0, "bf16"))
-        a.append(synth.device_normal(t.cfg, t.case, synth.TA, (t.r, t.K), 1.0 / t.K, "bf16"))
-        b.append(synth.device_normal(t.cfg, t.case, synth.TB, (t.N, t.r), t.var_b, "bf16"))
+        w0.append(synth.device_normal(t.group, t.case, synth.TW, (t.N, t.K), t.var_w0, "bf16"))
+        a.append(synth.device_normal(t.group, t.case, synth.TA, (t.r, t.K), 1.0 / t.K, "bf16"))
+        b.append(synth.device_normal(t.group, t.case, synth.TB, (t.N, t.r), t.var_b, "bf16"))
     for i, t in enumerate(tg):
         one.append(gpu_lib.merge(w0[i], b[i], a[i], t.scale))
         outs.append(torch.empty_like(w0[i]))

@@ -6,24 +6,24 @@ import synth
 
 
 def test_same_seed_same_bytes():
-    a = synth.CFG2.make()
-    b = synth.CFG2.make()
+    a = synth.MID.make()
+    b = synth.MID.make()
     for k in "XWAB":
         assert a[k].tobytes() == b[k].tobytes()
-    c = synth.CFG1.make()
+    c = synth.TINY.make()
     assert c["X"].dtype == np.float32 and a["X"].dtype == np.uint16
 
 
 def test_distinct_tensors_and_shared_hidden_states():
-    q = synth.CFG3_Q.make("XA")
-    v = synth.CFG3_V.make("XA")
+    q = synth.QPROJ.make("XA")
+    v = synth.VPROJ.make("XA")
     assert q["X"].tobytes() == v["X"].tobytes()          # q and v read the same X
     assert q["A"].tobytes() != v["A"].tobytes()
 
 
 def test_variance_reading():
     # N(0, v) is read as variance v: std of B ~ sqrt(0.02), of W ~ sqrt(1/K)
-    t = synth.CFG2.make()
+    t = synth.MID.make()
     w = synth.to_f64(t["W"])
     b = synth.to_f64(t["B"])
     assert abs(w.std() - (1 / 1024) ** 0.5) / (1 / 1024) ** 0.5 < 0.01
@@ -42,9 +42,9 @@ def test_bf16_narrowing_matches_torch():
 
 
 def test_workload_sizes():
-    assert round(synth.CFG2.flops() / 1e9, 3) == 8.858
-    assert round(synth.CFG3_Q.flops() / 1e9, 2) == 175.29
-    assert round(synth.CFG4[0].bytes() / 1e6, 3) == 33.833
+    assert round(synth.MID.flops() / 1e9, 3) == 8.858
+    assert round(synth.QPROJ.flops() / 1e9, 2) == 175.29
+    assert round(synth.DECODE[0].bytes() / 1e6, 3) == 33.833
     tg = synth.merge_targets()
     assert len(tg) == 252
     assert round(sum(t.bytes() for t in tg) / 1e9, 3) == 14.665
