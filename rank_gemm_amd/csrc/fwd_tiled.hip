@@ -95,7 +95,7 @@ struct Cfg {
   static_assert(BN * kTS * 2 <= kTOffG && kYB <= kTOffG, "group epilogue fits in the ring");
   static constexpr int kTSlots = (TM * RB + WN - 1) / WN;  // T accumulators per wave
   static constexpr int kGroup = 4;         // M tiles per group (XCD-contiguous ids)
-  static constexpr int kGroupShared = 16;  // M tiles swept together by all XCDs
+  static constexpr int kGroupShared = 8;   // M tiles swept together by all XCDs (measured best)
   // T tile (i, tj) of a wave row belongs to wave (i * RB + tj) % WN.  With RB a
   // multiple of WN a wave owns rank blocks tj = wn + u * WN for every i and keeps
   // RB / WN A fragments; with WN a multiple of RB it owns rows
