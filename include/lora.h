@@ -32,7 +32,7 @@
  *     ld multiples of 4.  N, r, ldb and ldy are unrestricted.
  *   - Limits (LORA_ERR_UNSUPPORTED beyond them): every size <= 2^30 - 1;
  *     for lora_fwd, ldx, ldw and lda <= LORA_MAX_LD elements (the kernels
- *     address a 256-row tile of X or W with 32-bit byte offsets).
+ *     address a 256-row tile of X or W with signed 32-bit byte ranges).
  *   - Outputs must not overlap any input (LORA_ERR_ALIAS).
  *   - NaN and Inf in the inputs propagate as IEEE arithmetic makes them.
  */
@@ -61,7 +61,7 @@ typedef enum lora_status {
     LORA_ERR_HIP = 8          /* the HIP runtime reported a launch error */
 } lora_status;
 
-#define LORA_MAX_LD (1 << 22)
+#define LORA_MAX_LD ((1 << 22) - 8)
 
 typedef enum lora_dtype {
     LORA_F32 = 0,

@@ -285,13 +285,8 @@ hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = 8;
   using C = Dec<MB, RB, U, NW, AL, XL>;
   auto kern = fwd_decode_bf16_kernel<MB, RB, U, NW, AL, XL>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   const int blocks = (int)((a.N + 15) / 16);
   const int b_vec = ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), C::kLds, s, (int)a.M, (int)a.N, (int)a.K,

@@ -148,13 +148,8 @@ hipError_t launch_f32(const FwdArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + kF32BM - 1) / kF32BM);
   const int tiles_n = (int)((a.N + kF32BN - 1) / kF32BN);
   auto kern = fwd_tiled_f32_kernel<RP>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kF32Threads), C::kLds, s, (int)a.M,
                      (int)a.N, (int)a.K, (int)a.r, static_cast<const float*>(a.X), a.ldx,
                      static_cast<const float*>(a.W), a.ldw, static_cast<const float*>(a.A), a.lda,

@@ -274,15 +274,6 @@ MergeGrid merge_grid(int64_t N, int64_t K, int target_wgs) {
   return g;
 }
 
-template <class K>
-hipError_t set_lds(K kern, int bytes, bool& done) {
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) done = true;
-  return e;
-}
-
 int b_vec_of(const void* B, int64_t ldb) {
   return ((reinterpret_cast<uintptr_t>(B) & 15) == 0) && (ldb % 8 == 0);
 }
@@ -291,8 +282,8 @@ template <int RP>
 hipError_t launch_m(const MergeArgs& a, hipStream_t s) {
   using C = Mrg<RP>;
   auto kern = merge_bf16_kernel<RP>;
-  static bool attr_done = false;
-  if (hipError_t e = set_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
+  static std::atomic<uint64_t> attr_done{0};
+  if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   const MergeGrid g = merge_grid<RP>(a.N, a.K, 512);
   hipLaunchKernelGGL(kern, dim3(g.strips * g.groups), dim3(kMergeThreads), C::kLds, s, (int)a.N,
                      (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.W0), a.ldw0,
@@ -309,8 +300,8 @@ template <int RP>
 hipError_t launch_mb(const MergeArgs* a, int i0, int i1, hipStream_t s) {
   using C = Mrg<RP>;
   auto kern = merge_bf16_batch_kernel<RP>;
-  static bool attr_done = false;
-  if (hipError_t e = set_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
+  static std::atomic<uint64_t> attr_done{0};
+  if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   MergeBatch mb{};
   mb.count = i1 - i0;
   int wgs = 0;

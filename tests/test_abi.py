@@ -76,9 +76,9 @@ def _merge(**kw):
     (dict(variant=2, M=65), rg.LORA_ERR_UNSUPPORTED),
     (dict(variant=2, dtype=rg.LORA_F32), rg.LORA_ERR_UNSUPPORTED),
     (dict(variant=2, r=33, ldb=33), rg.LORA_ERR_UNSUPPORTED),
-    (dict(ldx=(1 << 22) + 8), rg.LORA_ERR_UNSUPPORTED),
-    (dict(ldw=(1 << 22) + 8), rg.LORA_ERR_UNSUPPORTED),
-    (dict(lda=(1 << 22) + 8), rg.LORA_ERR_UNSUPPORTED),
+    (dict(ldx=1 << 22), rg.LORA_ERR_UNSUPPORTED),
+    (dict(ldw=1 << 22), rg.LORA_ERR_UNSUPPORTED),
+    (dict(lda=1 << 22), rg.LORA_ERR_UNSUPPORTED),
     (dict(M=1 << 30), rg.LORA_ERR_UNSUPPORTED),
     (dict(X=0), rg.LORA_ERR_NULL),
     (dict(W=0), rg.LORA_ERR_NULL),
