@@ -62,17 +62,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1>
+template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_, BK = BK_;
-  // KS groups of WM x WN waves split the K range of the tile; each group has
-  // its own stage ring, and the groups' partial sums meet in LDS.
-  static constexpr int KS = KS_;
   static constexpr int kRowB = BK * 2;                // bytes per staged row
   static constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one 1-KiB wave load covers
   static constexpr int kChunks = BK / 8;              // 16-B chunks per row
   static constexpr int NW = WM * WN;
-  static constexpr int NT = KS * NW * kWave;
+  static constexpr int NT = NW * kWave;
   static constexpr int TM = BM / WM / 16;
   static constexpr int TN = BN / WN / 16;
   static constexpr int RB = RP / 16;
@@ -90,15 +87,12 @@ struct Cfg {
   static constexpr int kEpiB = (BM + BN) * kTS * 2;
   static constexpr int kYS = BN + 8;                // output staging row stride (elements)
   static constexpr int kYB = BM * kYS * 2;
-  static constexpr int kRing = STAGES * kStageB;
-  static constexpr int kRedB = KS > 1 ? NW * kWave * (TM * TN + (TM * RB + WN - 1) / WN) * 16 : 0;
-  static constexpr int kLds = cmax(KS * kRing, cmax(cmax(kEpiB, kYB), kRedB));
+  static constexpr int kLds = cmax(STAGES * kStageB, cmax(kEpiB, kYB));
   // With T kept across the N tiles of a group: T after the ring, the B tile
   // and the output staging inside it.
   static constexpr int kTOffG = STAGES * kStageB;
   static constexpr int kLdsG = kTOffG + BM * kTS * 2;
   static_assert(BN * kTS * 2 <= kTOffG && kYB <= kTOffG, "group epilogue fits in the ring");
-  static_assert(KS == 1 || KS == 2, "K split in one or two wave groups");
   static constexpr int kTSlots = (TM * RB + WN - 1) / WN;  // T accumulators per wave
   static constexpr int kGroup = 4;         // M tiles per group (XCD-contiguous ids)
   static constexpr int kGroupShared = 8;   // M tiles swept together by all XCDs (measured best)
@@ -248,10 +242,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int grp = wave / NW;       // K-split group (0 with KS == 1)
-  const int gw = wave - grp * NW;  // wave within its group
-  const int wm = gw / WN;
-  const int wn = gw % WN;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
   const int lrow = lane & 15;
   const int lk = lane >> 4;
 
@@ -302,15 +294,9 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   constexpr int BK = C::BK, kRowB = C::kRowB, kRPL = C::kRowsPerLoad;
   const int lrow_in_load = lane / C::kChunks;
   const int lchunk = (lane % C::kChunks) ^ swz<BK>(lrow_in_load);
-  const uint32_t vx = (uint32_t)((gw * kRPL + lrow_in_load) * ldx * 2 + lchunk * 16);
-  const uint32_t vw = (uint32_t)((gw * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
-  const uint32_t va = (uint32_t)((gw * kRPL + lrow_in_load) * lda * 2 + lchunk * 16);
-  // This group's K range and stage ring.  Every group runs the same number of
-  // stages (workgroup barriers must match); stages past kend read zeros.
-  const int nkg = ((K + BK - 1) / BK + C::KS - 1) / C::KS;
-  const int kbeg = grp * nkg * BK;
-  const int kend = min(K, kbeg + nkg * BK);
-  unsigned char* gsm = smem + grp * C::kRing;
+  const uint32_t vx = (uint32_t)((wave * kRPL + lrow_in_load) * ldx * 2 + lchunk * 16);
+  const uint32_t vw = (uint32_t)((wave * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
+  const uint32_t va = (uint32_t)((wave * kRPL + lrow_in_load) * lda * 2 + lchunk * 16);
   const uint32_t sx = (uint32_t)(NW * kRPL * ldx * 2);  // byte stride between a wave's slots
   const uint32_t sw = (uint32_t)(NW * kRPL * ldw * 2);
   const uint32_t sa = (uint32_t)(NW * kRPL * lda * 2);
@@ -347,18 +333,18 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // the substeps have no branches and the scheduler can interleave their
   // streams.
   constexpr int NSUB = BK / 32;
-  const int nk = nkg;
+  const int nk = (K + BK - 1) / BK;
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
-    issue_stage<C, WT>(gsm, s, kbeg + s * BK, kend, gw, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+    issue_stage<C, WT>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
 
   const int xrow0 = wm * TM * 16 + lrow;  // + 16 * ring_row_block(k) for ring slot k
   const int wrow0 = wn * TN * 16 + lrow;
   Frags<C> cur;
-  wait_stages<C, STAGES - 1, WT>(gw);
+  wait_stages<C, STAGES - 1, WT>(wave);
   __builtin_amdgcn_s_barrier();
   {
-    const unsigned char* xs = gsm;
+    const unsigned char* xs = smem;
     const unsigned char* ws = xs + BM * kRowB;
     const unsigned char* as = ws + BN * kRowB;
 #pragma unroll
@@ -387,13 +373,13 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       // flight; this wave's reads of stage kt are complete.  After the
       // barrier every wave is past both.  A bare s_barrier: a fence would
       // drain every stage in flight.
-      wait_stages<C, STAGES - 2, WT>(gw);
+      wait_stages<C, STAGES - 2, WT>(wave);
       __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
-      issue_stage<C, WT>(gsm, rslot, kbeg + (kt + STAGES) * BK, kend, gw, lchunk, rx, rw, ra, vx, vw, va, sx,
+      issue_stage<C, WT>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx,
                      sw, sa);
     }
-    const unsigned char* xs = gsm + (sync ? nslot : rslot) * C::kStageB;
+    const unsigned char* xs = smem + (sync ? nslot : rslot) * C::kStageB;
     const unsigned char* ws = xs + BM * kRowB;
     const unsigned char* as = ws + BN * kRowB;
     const int cc = (sync ? 0 : (u + 1) * 4) + lk;  // logical 16-B chunk of the next substep
@@ -461,38 +447,11 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   else kloop(std::false_type{});
   __syncthreads();
 
-  // ---- K-split groups: group 1 parks its partial sums (base and T) in LDS,
-  // group 0 adds them in a fixed order; group 0 alone runs the epilogue's
-  // per-wave parts.
-  const bool epi = grp == 0;
-  if constexpr (C::KS > 1) {
-    constexpr int kPer = TM * TN + C::kTSlots;  // f32x4 per lane
-    f32x4* red = reinterpret_cast<f32x4*>(smem);
-    if (grp == 1) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) red[(gw * kPer + i * TN + j) * kWave + lane] = acc[i][j];
-#pragma unroll
-      for (int sl = 0; sl < C::kTSlots; ++sl) red[(gw * kPer + TM * TN + sl) * kWave + lane] = tacc[sl];
-    }
-    __syncthreads();
-    if (grp == 0) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] += red[(gw * kPer + i * TN + j) * kWave + lane];
-#pragma unroll
-      for (int sl = 0; sl < C::kTSlots; ++sl) tacc[sl] += red[(gw * kPer + TM * TN + sl) * kWave + lane];
-    }
-    __syncthreads();
-  }
-
   // ---- epilogue 1: scaled T (bf16) and the B tile into LDS.  With G > 1,
   // T lives past the stage ring and is written by the first tile only.
   uint16_t* ts = reinterpret_cast<uint16_t*>(smem + (G > 1 ? C::kTOffG : 0));
   uint16_t* bs = G > 1 ? reinterpret_cast<uint16_t*>(smem) : ts + BM * C::kTS;
-  if (g == 0 && epi) {
+  if (g == 0) {
 #pragma unroll
   for (int sl = 0; sl < C::kTSlots; ++sl) {
     const int i = ring_row_block<C>(t_ring_slot<C>(sl), rot);
@@ -513,8 +472,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   __syncthreads();
 
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank.
-  if (!epi) {
-  } else if constexpr (RP >= 32) {
+  if constexpr (RP >= 32) {
 #pragma unroll
     for (int kk = 0; kk < RP / 32; ++kk) {
       u32x4 a[TM], b[TN];
@@ -549,17 +507,15 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 
   // ---- epilogue 3: round once to bf16, stage, store coalesced.
   uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
-  if (epi) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lk * 4 + q;
-          ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
-        }
-  }
+      for (int q = 0; q < 4; ++q) {
+        const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lk * 4 + q;
+        ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
+      }
   __syncthreads();
   constexpr int kCPR = BN / 8;  // 16-B chunks per output row
   for (int e = tid; e < BM * kCPR; e += C::NT) {
@@ -624,11 +580,6 @@ template <int RP>
 using Tall = Cfg<64, 32, 4, 1, RP, 8, 64>;
 template <int RP>
 using Mid = Cfg<128, 128, 4, 2, RP, 2, 64>;
-// MidK: the 128 x 128 tile with K split over two groups of 8 waves (16 waves,
-// four per SIMD): twice the loads in flight per CU for shapes with about one
-// tile per CU.
-template <int RP>
-using MidK = Cfg<128, 128, 4, 2, RP, 2, 64, 2>;
 
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
