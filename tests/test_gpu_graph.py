@@ -58,3 +58,18 @@ def test_merge_graph_replay(gpu_lib):
             gpu_lib.merge(w0, b, a, s, out=o)
 
     _replays_match_eager(launch, outs)
+
+
+def test_merge_batch_graph_replay(gpu_lib):
+    import torch
+    tg = synth.merge_targets(2)
+    ins, outs = [], []
+    for t in tg:
+        A, B = t.make_ab(1)
+        ins.append((to_dev(t.make_w0()), to_dev(B), to_dev(A), t.scale))
+        outs.append(torch.empty((t.N, t.K), dtype=torch.bfloat16, device="cuda"))
+
+    def launch():
+        gpu_lib.merge_batch([(w0, b, a, s, o) for (w0, b, a, s), o in zip(ins, outs)])
+
+    _replays_match_eager(launch, outs)
