@@ -20,6 +20,15 @@
  * Element types: ORC_F32 (float) or ORC_BF16 (uint16 bit patterns of bf16).
  * Every input value is widened exactly to double; every sum runs in ascending
  * index order in double; the forward result is not rounded.
+ *
+ * Pins (tests/test_oracle_pins.py; no function here is left unpinned):
+ * oracle_fwd_rows against hand-worked values, a literal quadruple loop on
+ * tiny shapes (bitwise), B = 0 / scale = 0 / W = 0 reductions, linearity in
+ * the scale, the merged-weight form, exact integer cases and numpy float64;
+ * oracle_fwd_entries bitwise against oracle_fwd_rows; oracle_merge_rows
+ * against hand-worked values, its special cases and numpy float64;
+ * oracle_round_bf16 against torch's float32 -> bf16 conversion and against
+ * ties and double-rounding cases.
  */
 #include <math.h>
 #include <stdint.h>
