@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 2
+#define LORA_ABI_VERSION 3
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -172,6 +172,22 @@ typedef struct lora_merge_desc {
 } lora_merge_desc;
 
 int lora_merge_batch(int dtype, int count, const lora_merge_desc *descs, void *stream);
+
+/*
+ * lora_merge_inplace -- W = round( W + scale * B A ), in place.
+ *   [unsloth], the merge_adapter / unmerge_adapter path that the pristine
+ *   refresh replaces: merging into the base weight and subtracting again
+ *   (scale -> -scale) does not return the base bit for bit in bf16 (about
+ *   one ULP of drift per cycle).  Offered as that negative control and for
+ *   callers that merge once and never restore.
+ *
+ *   dtype, N, K, r, B, ldb, A, lda, scale, stream as for lora_merge.
+ *   W, ldw        [N,K] weight, read and overwritten; must not overlap B or A.
+ * Returns a lora_status.
+ */
+int lora_merge_inplace(int dtype, int64_t N, int64_t K, int64_t r,
+                       void *W, int64_t ldw, const void *B, int64_t ldb,
+                       const void *A, int64_t lda, float scale, void *stream);
 
 /* Static, NUL-terminated description of a lora_status value. */
 const char *lora_status_str(int status);

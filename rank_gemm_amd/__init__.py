@@ -8,6 +8,7 @@ loaded, the first call raises.
     Y = fwd(X, W, A, B, scale)          # X W^T + scale * (X A^T) B^T
     merge(W0, B, A, scale, out=W_inf)   # W_inf = W0 + scale * B A, W0 untouched
     merge_batch([(W0, B, A, scale, W_inf), ...])   # many targets, few launches
+    merge_inplace(W, B, A, scale)       # W += scale * B A in place (not bit-reversible)
 
 Tensors are torch tensors on the current HIP device, all bfloat16 or all
 float32, 2-D with unit inner stride (rows may be padded: the leading
@@ -39,8 +40,8 @@ VARIANTS = {"auto": 0, "tiled": 1, "decode": 2}
 MAX_RANK = 256
 DECODE_MAX_M = 64
 
-EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch", "lora_status_str",
-           "lora_abi_version", "lora_fwd_pick")
+EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch",
+           "lora_merge_inplace", "lora_status_str", "lora_abi_version", "lora_fwd_pick")
 
 
 class MergeDesc(ctypes.Structure):
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.lora_fwd_variant.restype = i32
     L.lora_merge.argtypes = [i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, vp, i64, vp]
     L.lora_merge.restype = i32
+    L.lora_merge_inplace.argtypes = [i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, vp]
+    L.lora_merge_inplace.restype = i32
     L.lora_merge_batch.argtypes = [i32, i32, ctypes.POINTER(MergeDesc), vp]
     L.lora_merge_batch.restype = i32
     L.lora_status_str.argtypes = [i32]
@@ -121,6 +124,13 @@ def merge_raw(dtype: int, N: int, K: int, r: int, W0: int, ldw0: int, B: int, ld
     """lora_merge with integer addresses; returns the lora_status."""
     return int(lib().lora_merge(dtype, N, K, r, W0, ldw0, B, ldb, A, lda, scale, Wi, ldwi,
                                 stream or None))
+
+
+def merge_inplace_raw(dtype: int, N: int, K: int, r: int, W: int, ldw: int, B: int, ldb: int,
+                      A: int, lda: int, scale: float, stream: int = 0) -> int:
+    """lora_merge_inplace with integer addresses; returns the lora_status."""
+    return int(lib().lora_merge_inplace(dtype, N, K, r, W, ldw, B, ldb, A, lda, scale,
+                                        stream or None))
 
 
 def merge_batch_raw(dtype: int, descs, stream: int = 0) -> int:
@@ -239,3 +249,22 @@ def merge_batch(targets):
         po, ldo = _mat(out, "out")
         descs[i] = MergeDesc(N, K, r, p0, ld0, pb, ldb, pa, lda, float(scale), po, ldo)
     _check(merge_batch_raw(dt, descs, _stream(dev)), "lora_merge_batch")
+
+
+def merge_inplace(W, B, A, scale: float):
+    """In-place merge ``W = W + scale * B A`` (a negative scale unmerges).
+    Not bit-reversible in bf16; ``merge`` from a pristine copy is."""
+    N, K = W.shape
+    r = A.shape[0]
+    if A.shape[1] != K or tuple(B.shape) != (N, r):
+        raise ValueError(f"shape mismatch W{tuple(W.shape)} B{tuple(B.shape)} A{tuple(A.shape)}")
+    dt = _dtype_code(W)
+    for t, nm in ((B, "B"), (A, "A")):
+        if t.dtype != W.dtype or t.device != W.device:
+            raise ValueError(f"{nm} must match W in dtype and device")
+    pw, ldw = _mat(W, "W")
+    pb, ldb = _mat(B, "B")
+    pa, lda = _mat(A, "A")
+    _check(merge_inplace_raw(dt, N, K, r, pw, ldw, pb, ldb, pa, lda, float(scale), _stream(W.device)),
+           "lora_merge_inplace")
+    return W

@@ -163,6 +163,32 @@ int lora_merge(int dtype, int64_t N, int64_t K, int64_t r, const void* W0, int64
   return err == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+int lora_merge_inplace(int dtype, int64_t N, int64_t K, int64_t r, void* W, int64_t ldw,
+                       const void* B, int64_t ldb, const void* A, int64_t lda, float scale,
+                       void* stream) {
+  // lora_merge's checks with W as both the input and the output.
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (N < 0 || K < 0 || r < 1) return LORA_ERR_SHAPE;
+  if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
+  if (N > INT32_MAX / 2 || K > INT32_MAX / 2) return LORA_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return LORA_OK;
+  if (W == nullptr || B == nullptr || A == nullptr) return LORA_ERR_NULL;
+  if (ldw < K || lda < K || ldb < r) return LORA_ERR_STRIDE;
+  const int64_t e = esize(dtype);
+  const int64_t kal = dtype == LORA_BF16 ? 8 : 4;
+  if (!aligned16(W) || !aligned16(A)) return LORA_ERR_ALIGN;
+  if (K % kal || ldw % kal || lda % kal) return LORA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(B) % e) return LORA_ERR_ALIGN;
+  const Range w = span(W, N, K, ldw, e);
+  if (overlap(w, span(A, r, K, lda, e)) || overlap(w, span(B, N, r, ldb, e)))
+    return LORA_ERR_ALIAS;
+  const lora::MergeArgs a{N, K, r, W, ldw, B, ldb, A, lda, scale, W, ldw};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err =
+      dtype == LORA_BF16 ? lora::launch_merge_bf16(a, s) : lora::launch_merge_f32(a, s);
+  return err == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 int lora_merge_batch(int dtype, int count, const lora_merge_desc* descs, void* stream) {
   if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
   if (count < 0) return LORA_ERR_SHAPE;

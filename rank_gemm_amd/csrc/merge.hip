@@ -23,7 +23,10 @@
 // issued before it, and later row blocks are double-buffered.
 //
 // W0 is never written; nothing is accumulated across workgroups, so repeated
-// merges of the same inputs are bitwise identical.
+// merges of the same inputs are bitwise identical.  Every element of W0 is
+// read once and its W_inf element written afterwards by the same lane, so
+// the same code also merges in place (W_inf == W0), which lora_merge_inplace
+// offers as the merge/unmerge path that the pristine merge replaces.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,9 +58,9 @@ __device__ __forceinline__ int run_col(int lg, int e) { return (e >> 3) * 32 + 8
 // the batched kernels.
 template <int RP>
 __device__ __forceinline__ void merge_bf16_tile(
-    unsigned char* smem, int wg, int N, int K, int r, const uint16_t* __restrict__ W0,
+    unsigned char* smem, int wg, int N, int K, int r, const uint16_t* W0,
     int64_t ldw0, const uint16_t* __restrict__ B, int64_t ldb, const uint16_t* __restrict__ A,
-    int64_t lda, float scale, uint16_t* __restrict__ Wi, int64_t ldwi, int strips,
+    int64_t lda, float scale, uint16_t* Wi, int64_t ldwi, int strips,
     int nblk_per_wg, int b_vec) {
   using C = Mrg<RP>;
   constexpr int RB32 = C::RB32, U = C::kU;
@@ -209,9 +212,9 @@ __device__ __forceinline__ void merge_bf16_tile(
 
 template <int RP>
 __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(
-    int N, int K, int r, const uint16_t* __restrict__ W0, int64_t ldw0,
+    int N, int K, int r, const uint16_t* W0, int64_t ldw0,
     const uint16_t* __restrict__ B, int64_t ldb, const uint16_t* __restrict__ A, int64_t lda,
-    float scale, uint16_t* __restrict__ Wi, int64_t ldwi, int strips, int nblk_per_wg,
+    float scale, uint16_t* Wi, int64_t ldwi, int strips, int nblk_per_wg,
     int b_vec) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   merge_bf16_tile<RP>(smem, blockIdx.x, N, K, r, W0, ldw0, B, ldb, A, lda, scale, Wi, ldwi,
@@ -332,8 +335,8 @@ hipError_t launch_mb(const MergeArgs* a, int i0, int i1, hipStream_t s) {
 // fp32 merge: plain VALU, 4 consecutive columns per thread, fp32 FMA chain
 // over the rank.
 __global__ __launch_bounds__(256) void merge_f32_kernel(
-    int N, int K, int r, const float* __restrict__ W0, int64_t ldw0, const float* __restrict__ B,
-    int64_t ldb, const float* __restrict__ A, int64_t lda, float scale, float* __restrict__ Wi,
+    int N, int K, int r, const float* W0, int64_t ldw0, const float* __restrict__ B,
+    int64_t ldb, const float* __restrict__ A, int64_t lda, float scale, float* Wi,
     int64_t ldwi, int kblocks) {
   const int n = blockIdx.x / kblocks;
   const int k = ((blockIdx.x % kblocks) * 256 + threadIdx.x) * 4;

@@ -33,7 +33,7 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 2
+    assert rg.abi_version() == 3
     for s in range(9):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
@@ -168,6 +168,25 @@ def test_merge_batch_argument_checks():
     assert L.lora_merge_batch(rg.LORA_BF16, 2, None, None) == rg.LORA_ERR_NULL
     # empty targets are skipped (no launch), whatever their pointers
     assert rg.merge_batch_raw(rg.LORA_BF16, [_desc(N=0, W0=0), _desc(K=0, W_inf=0)]) == rg.LORA_OK
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=3), rg.LORA_ERR_DTYPE),
+    (dict(N=-1), rg.LORA_ERR_SHAPE),
+    (dict(r=0), rg.LORA_ERR_SHAPE),
+    (dict(W=0), rg.LORA_ERR_NULL),
+    (dict(ldw=32), rg.LORA_ERR_STRIDE),
+    (dict(W=PW + 2), rg.LORA_ERR_ALIGN),
+    (dict(W=PA), rg.LORA_ERR_ALIAS),
+    (dict(W=PB - 96), rg.LORA_ERR_ALIAS),
+    (dict(N=0, W=0), rg.LORA_OK),
+])
+def test_merge_inplace_rejects_before_any_hip_call(kw, want):
+    a = dict(dtype=rg.LORA_BF16, N=64, K=64, r=16, W=PW, ldw=64, B=PB, ldb=16, A=PA, lda=64,
+             scale=2.0)
+    a.update(kw)
+    assert rg.merge_inplace_raw(a["dtype"], a["N"], a["K"], a["r"], a["W"], a["ldw"], a["B"],
+                                a["ldb"], a["A"], a["lda"], a["scale"]) == want
 
 
 def test_torch_wrapper_rejects_cpu_tensors():

@@ -227,3 +227,44 @@ def test_batch_full_model_pass_matches_per_target(gpu_lib):
     torch.cuda.synchronize()
     for i in range(len(tg)):
         assert torch.equal(outs[i].view(torch.int16), one[i].view(torch.int16)), tg[i].name
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_inplace_merge_equals_pristine_merge(gpu_lib, dtype):
+    """One in-place merge writes exactly what the merge from pristine writes."""
+    t = synth.MergeTarget("inplace", 95, 0, 300, 520, 32, 64.0, dtype)
+    W0 = t.make_w0()
+    A, B = t.make_ab(0)
+    a, b = to_dev(A), to_dev(B)
+    ref = to_host(_merge(gpu_lib, to_dev(W0), a, b, t.scale))
+    w = to_dev(W0)
+    gpu_lib.merge_inplace(w, b, a, t.scale)
+    import torch
+    torch.cuda.synchronize()
+    assert to_host(w).tobytes() == ref.tobytes()
+
+
+def test_merge_unmerge_cycles_drift_but_pristine_does_not(gpu_lib):
+    """Negative control for the pristine invariant: ten in-place merge +
+    unmerge cycles (scale, then -scale) leave the bf16 base changed, while ten
+    merges from pristine leave W0 bit-identical.  Reports the drift."""
+    import torch
+    t = LAYER0[0]
+    W0 = t.make_w0()
+    w = to_dev(W0)
+    w0 = to_dev(W0)
+    wi = torch.empty_like(w0)
+    for cycle in range(10):
+        A, B = t.make_ab(cycle)
+        a, b = to_dev(A), to_dev(B)
+        gpu_lib.merge_inplace(w, b, a, t.scale)
+        gpu_lib.merge_inplace(w, b, a, -t.scale)
+        gpu_lib.merge(w0, b, a, t.scale, out=wi)
+    torch.cuda.synchronize()
+    drifted = to_host(w)
+    ulp = ulp_distance_bf16(drifted, W0)
+    diff = np.abs(as_f64(drifted) - as_f64(W0))
+    print(f"after 10 merge/unmerge cycles: {float((ulp > 0).mean()):.4f} of elements moved, "
+          f"max {int(ulp.max())} ulp, max abs {diff.max():.3e}")
+    assert (ulp > 0).any()                                  # the in-place path drifts
+    assert to_host(w0).tobytes() == W0.tobytes()            # the pristine path does not
