@@ -14,6 +14,9 @@ What it computes (page titles as published):
   replacing the copy+merge_adapter pair: ``W_inf = pristine + scaling * (B A)``
   with fp32 accumulation, the pristine copy left untouched.  The oracle gives
   the exact value in fp64 and its bf16 rounding (nearest, ties to even).
+* the same fastaf page, section "BWD kernel speedup": the backward of the
+  layer with W frozen, ``dX = dY W + scale (dY B) A``,
+  ``dA = scale (dY B)^T X``, ``dB = scale dY^T (X A^T)``, in fp64.
 
 Arrays: fp32 data as ``numpy.float32``; bf16 data as ``numpy.uint16`` bit
 patterns.  All pins live in ``tests/test_oracle_pins.py``.
@@ -47,6 +50,9 @@ def _load():
     lib.oracle_fwd_entries.restype = ctypes.c_int
     lib.oracle_merge_rows.argtypes = [ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, f, vp, vp]
     lib.oracle_merge_rows.restype = ctypes.c_int
+    lib.oracle_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp, f, i64, i64,
+                               dp, dp, dp]
+    lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -152,6 +158,37 @@ def merge(W0: np.ndarray, B: np.ndarray, A: np.ndarray, scale: float,
     if rc != 0:
         raise MemoryError("oracle_merge_rows could not allocate its work buffer")
     return Wd, Wb
+
+
+def bwd(X: np.ndarray, W: np.ndarray, A: np.ndarray, B: np.ndarray, dY: np.ndarray,
+        scale: float, dx_rows: Optional[Sequence[int]] = None):
+    """Backward of the layer with W frozen, in fp64:
+    ``dX = dY W + scale (dY B) A``, ``dA = scale (dY B)^T X``,
+    ``dB = scale dY^T (X A^T)``.
+
+    Returns ``(dX, dA, dB)``; dX holds rows ``dx_rows = (m0, m1)`` only (all
+    rows when None; ``(0, 0)`` skips it).
+    """
+    lib = _load()
+    X, W, A, B, dY = _c(X), _c(W), _c(A), _c(B), _c(dY)
+    dt = _dt(X, W, A, B, dY)
+    M, K = X.shape
+    N = W.shape[0]
+    r = A.shape[0]
+    if W.shape != (N, K) or A.shape != (r, K) or B.shape != (N, r) or dY.shape != (M, N):
+        raise ValueError(f"shape mismatch X{X.shape} W{W.shape} A{A.shape} B{B.shape} dY{dY.shape}")
+    m0, m1 = (0, M) if dx_rows is None else (int(dx_rows[0]), int(dx_rows[1]))
+    if not (0 <= m0 <= m1 <= M):
+        raise ValueError("row range out of bounds")
+    dX = np.zeros((m1 - m0, K), dtype=np.float64)
+    dA = np.zeros((r, K), dtype=np.float64)
+    dB = np.zeros((N, r), dtype=np.float64)
+    rc = lib.oracle_bwd(dt, M, N, K, r, X.ctypes.data, W.ctypes.data, A.ctypes.data,
+                        B.ctypes.data, dY.ctypes.data, float(np.float32(scale)), m0, m1,
+                        dX.ctypes.data if m1 > m0 else None, dA.ctypes.data, dB.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle_bwd could not allocate its work buffers")
+    return dX, dA, dB
 
 
 def round_bf16(x) -> np.ndarray:

@@ -9,7 +9,8 @@
  * Sources (page titles as published):
  *   "fastaf: Minimal LoRA fine-tuning with hand-written Triton kernels",
  *     section "FWD kernel speedup": the forward of one LoRA layer is
- *     out = X W^T + ((X A^T) B^T) * scale, with scale = alpha / r.
+ *     out = X W^T + ((X A^T) B^T) * scale, with scale = alpha / r;
+ *     section "BWD kernel speedup": its backward yields dA, dB and dX.
  *   unsloth commit log for scripts/benchmarks/qwen3_flex_inference.py, entry
  *     "Replace the copy+merge_adapter pair ...": the refresh writes
  *     W_inf = pristine + scaling * (B A) in one addmm, accumulated in fp32,
@@ -28,7 +29,10 @@
  * oracle_fwd_entries bitwise against oracle_fwd_rows; oracle_merge_rows
  * against hand-worked values, its special cases and numpy float64;
  * oracle_round_bf16 against torch's float32 -> bf16 conversion and against
- * ties and double-rounding cases.
+ * ties and double-rounding cases; oracle_bwd against the forward through the
+ * adjoint identities <dY, Y(X)> = <dX, X> and their A and B counterparts,
+ * a literal loop on tiny shapes (bitwise), B = 0 / A = 0 / scale = 0
+ * reductions and numpy float64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -227,5 +231,79 @@ int oracle_merge_rows(int dt, int64_t n0, int64_t n1, int64_t K, int64_t r,
         }
     }
     free(Ad);
+    return 0;
+}
+
+/*
+ * Backward of the layer with the base weight frozen, "fastaf: Minimal LoRA
+ * fine-tuning with hand-written Triton kernels", section "BWD kernel speedup"
+ * (the three gradients dA, dB, dX of out = X W^T + ((X A^T) B^T) * scale):
+ *   T[m,j]  = sum_k X[m,k] A[j,k]             (the forward's intermediate)
+ *   G[m,j]  = sum_n dY[m,n] B[n,j]            (the output gradient in rank space)
+ *   dX[m,k] = sum_n dY[m,n] W[n,k] + scale * sum_j G[m,j] A[j,k]
+ *   dA[j,k] = scale * sum_m G[m,j] X[m,k]
+ *   dB[n,j] = scale * sum_m dY[m,n] T[m,j]
+ * All in double, ascending sums.  dX is written for rows [dx0, dx1) only
+ * (into dX[(m - dx0) * K + k]; dX may be NULL), so that large shapes can be
+ * checked on sampled rows; dA ([r, K]) and dB ([N, r]) are always complete.
+ * Returns 0, or -1 when a work buffer cannot be allocated.
+ */
+int oracle_bwd(int dt, int64_t M, int64_t N, int64_t K, int64_t r,
+               const void *X, const void *W, const void *A, const void *B, const void *dY,
+               float scale, int64_t dx0, int64_t dx1, double *dX, double *dA, double *dB)
+{
+    const double s = (double)scale;
+    double *T = (double *)malloc(sizeof(double) * (size_t)(M * r > 0 ? M * r : 1));
+    double *G = (double *)malloc(sizeof(double) * (size_t)(M * r > 0 ? M * r : 1));
+    if (T == NULL || G == NULL) {
+        free(T);
+        free(G);
+        return -1;
+    }
+#pragma omp parallel for num_threads(oracle_get_threads()) schedule(dynamic, 4)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < r; ++j) {
+            double t = 0.0, g = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                t += widen(dt, X, m * K + k) * widen(dt, A, j * K + k);
+            for (int64_t n = 0; n < N; ++n)
+                g += widen(dt, dY, m * N + n) * widen(dt, B, n * r + j);
+            T[m * r + j] = t;
+            G[m * r + j] = g;
+        }
+    }
+    if (dX != NULL) {
+#pragma omp parallel for num_threads(oracle_get_threads()) schedule(dynamic, 1)
+        for (int64_t m = dx0; m < dx1; ++m) {
+            for (int64_t k = 0; k < K; ++k) {
+                double base = 0.0, lora = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    base += widen(dt, dY, m * N + n) * widen(dt, W, n * K + k);
+                for (int64_t j = 0; j < r; ++j)
+                    lora += G[m * r + j] * widen(dt, A, j * K + k);
+                dX[(m - dx0) * K + k] = base + s * lora;
+            }
+        }
+    }
+#pragma omp parallel for num_threads(oracle_get_threads()) schedule(dynamic, 4)
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t j = 0; j < r; ++j) {
+            double a = 0.0;
+            for (int64_t m = 0; m < M; ++m)
+                a += G[m * r + j] * widen(dt, X, m * K + k);
+            dA[j * K + k] = s * a;
+        }
+    }
+#pragma omp parallel for num_threads(oracle_get_threads()) schedule(dynamic, 4)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < r; ++j) {
+            double b = 0.0;
+            for (int64_t m = 0; m < M; ++m)
+                b += widen(dt, dY, m * N + n) * T[m * r + j];
+            dB[n * r + j] = s * b;
+        }
+    }
+    free(T);
+    free(G);
     return 0;
 }

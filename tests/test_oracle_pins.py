@@ -259,3 +259,76 @@ def test_round_bf16_single_rounding_from_double():
     assert oracle.round_bf16(2.0 ** -134) == 0x0000                   # tie -> even (0)
     assert oracle.round_bf16(1.5 * 2.0 ** -134) == 0x0001
     assert oracle.round_bf16(float("nan")) == 0x7FC0
+
+
+# ---------------------------------------------------------------- backward
+
+def _bwd_inputs(seed, M, N, K, r, dtype="f32"):
+    c = synth.FwdCase(f"bwd{seed}", 96, seed, M, N, K, r, 2.0 * r, dtype)
+    t = c.make()
+    dY = synth.normal(96, seed, 4, (M, N), 1.0, dtype)
+    return t["X"], t["W"], t["A"], t["B"], dY, c.scale
+
+
+@pytest.mark.parametrize("shape", [(7, 9, 12, 3), (33, 40, 24, 16), (64, 17, 80, 5)])
+def test_bwd_adjoint_identities_against_forward(shape):
+    """The layer is linear in X, in A and in B separately, so its gradients
+    are pinned by <dY, Y(X)> = <dX, X>, <dY, Y(A) - Y(0)> = <dA, A> and
+    <dY, Y(B) - Y(0)> = <dB, B>, with Y from the forward oracle."""
+    M, N, K, r = shape
+    X, W, A, B, dY, s = _bwd_inputs(1, M, N, K, r)
+    dX, dA, dB = oracle.bwd(X, W, A, B, dY, s)
+    f64 = synth.to_f64
+    Y = oracle.fwd(X, W, A, B, s)
+    Y0A = oracle.fwd(X, W, np.zeros_like(A), B, s)
+    Y0B = oracle.fwd(X, W, A, np.zeros_like(B), s)
+    dy = f64(dY)
+
+    def close(a, b):
+        assert abs(a - b) <= 1e-11 * max(1.0, abs(a), abs(b)), (a, b)
+
+    close(float((dy * Y).sum()), float((dX * f64(X)).sum()))
+    close(float((dy * (Y - Y0A)).sum()), float((dA * f64(A)).sum()))
+    close(float((dy * (Y - Y0B)).sum()), float((dB * f64(B)).sum()))
+
+
+def test_bwd_brute_force_tiny_bitwise():
+    """A literal loop transcription (same summation order) on tiny shapes."""
+    for (M, N, K, r) in [(1, 1, 1, 1), (2, 3, 5, 2), (5, 3, 2, 3)]:
+        X, W, A, B, dY, s = _bwd_inputs(2, M, N, K, r)
+        x, w, a, b, dy = (synth.to_f64(v).tolist() for v in (X, W, A, B, dY))
+        sd = float(np.float32(s))
+        T = [[sum(x[m][k] * a[j][k] for k in range(K)) for j in range(r)] for m in range(M)]
+        G = [[sum(dy[m][n] * b[n][j] for n in range(N)) for j in range(r)] for m in range(M)]
+        dX = [[sum(dy[m][n] * w[n][k] for n in range(N)) + sd * sum(G[m][j] * a[j][k] for j in range(r))
+               for k in range(K)] for m in range(M)]
+        dA = [[sd * sum(G[m][j] * x[m][k] for m in range(M)) for k in range(K)] for j in range(r)]
+        dB = [[sd * sum(dy[m][n] * T[m][j] for m in range(M)) for j in range(r)] for n in range(N)]
+        gX, gA, gB = oracle.bwd(X, W, A, B, dY, s)
+        assert gX.tolist() == dX and gA.tolist() == dA and gB.tolist() == dB
+
+
+def test_bwd_zero_adapter_cases():
+    M, N, K, r = 20, 24, 32, 4
+    X, W, A, B, dY, s = _bwd_inputs(3, M, N, K, r)
+    base = synth.to_f64(dY) @ synth.to_f64(W)
+    dX, dA, dB = oracle.bwd(X, W, A, np.zeros_like(B), dY, s)   # B = 0: G = 0
+    assert (dA == 0).all() and np.array_equal(dX, oracle.bwd(X, W, A, B, dY, 0.0)[0])
+    assert np.abs(dX - base).max() < 1e-12
+    dX, dA, dB = oracle.bwd(X, W, np.zeros_like(A), B, dY, s)   # A = 0: T = 0
+    assert (dB == 0).all()
+    dX, dA, dB = oracle.bwd(X, W, A, B, dY, 0.0)                # scale = 0
+    assert (dA == 0).all() and (dB == 0).all()
+
+
+def test_bwd_numpy_cross_check_bf16():
+    M, N, K, r = 96, 80, 136, 16
+    X, W, A, B, dY, s = _bwd_inputs(4, M, N, K, r, "bf16")
+    dX, dA, dB = oracle.bwd(X, W, A, B, dY, s)
+    x, w, a, b, dy = (synth.to_f64(v) for v in (X, W, A, B, dY))
+    G, T = dy @ b, x @ a.T
+    assert _rel_fro(dX, dy @ w + s * G @ a) < 1e-12
+    assert _rel_fro(dA, s * G.T @ x) < 1e-12
+    assert _rel_fro(dB, s * dy.T @ T) < 1e-12
+    dXr, _, _ = oracle.bwd(X, W, A, B, dY, s, dx_rows=(10, 30))
+    assert np.array_equal(dXr, dX[10:30])
