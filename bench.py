@@ -11,10 +11,12 @@ the other shapes of the same path measured in the same run: transformer
 projections (8192 tokens, hidden 2560, r = 32), the 16384 x 8192 x 8192
 square at r in {8, 16, 64, 128}, decode-shaped forwards (M in {1, 8, 64},
 W[4096,4096], rotated over 16 operand sets so the 256 MB last-level cache
-cannot hold them) and the merge of 36 layers x 7 targets at r = 32.
+cannot hold them), the merge of 36 layers x 7 targets at r = 32, and the
+backward (dX, dA, dB with W frozen) on the mid-size and q_proj shapes.
 
 --only NAME runs just one kernel a few times (for rocprofv3); NAME is one of
-tiny, mid, q, v, sq8, sq16, sq64, sq128, dec1, dec8, dec64, merge, copy.
+tiny, mid, q, v, sq8, sq16, sq64, sq128, dec1, dec8, dec64, merge, copy,
+bwd_mid, bwd_q.
 """
 from __future__ import annotations
 
@@ -201,6 +203,50 @@ def run_merge_pass(rg, steps, warmup, layers=36):
     }
 
 
+def bwd_flops(c):
+    """Algorithmic flops of one backward: dY W (2 M N K), G = dY B and
+    dB = s dY^T T (2 M N r each), T = X A^T, s G A and dA = s G^T X
+    (2 M K r each)."""
+    M, N, K, r = c.M, c.N, c.K, c.r
+    return 2.0 * M * N * K + 4.0 * M * N * r + 6.0 * M * K * r
+
+
+def run_bwd_case(rg, c, steps, warmup):
+    """One backward workload (lora_bwd: five launches), timed as a HIP graph
+    of `steps` back-to-back backward passes and eagerly."""
+    import torch
+    import synth
+    t = synth.fwd_case_on_device(c)
+    dY = synth.dy_on_device(c)
+    M, N, K, r = c.M, c.N, c.K, c.r
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((r, K), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((N, r), dtype=torch.bfloat16, device="cuda")
+    need = rg.bwd_workspace_size(rg.LORA_BF16, M, N, K, r)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    args = (rg.LORA_BF16, M, N, K, r, t["X"].data_ptr(), K, t["W"].data_ptr(), K,
+            t["A"].data_ptr(), K, t["B"].data_ptr(), r, dY.data_ptr(), N, c.scale,
+            dX.data_ptr(), K, dA.data_ptr(), K, dB.data_ptr(), r, ws.data_ptr(), need)
+
+    def fn(_):
+        st = rg.bwd_raw(*args, torch.cuda.current_stream().cuda_stream)
+        assert st == rg.LORA_OK, rg.status_str(st)
+
+    ms = graph_region(fn, steps, 3) / steps
+    eager_ms = timed_region(fn, steps, warmup) / steps
+    f = bwd_flops(c)
+    return {
+        "workload": "bwd_" + c.name,
+        "timing": "hip graph of back-to-back backward passes (5 launches each)",
+        "pass_us_mean": round(ms * 1e3, 3),
+        "eager_us_per_call": round(eager_ms * 1e3, 3),
+        "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "algorithmic_flop_per_pass": f,
+        "workspace_bytes": need,
+    }
+
+
 def cpu_baseline(c, budget_s=10.0):
     """The fp64 oracle, as it is, on the host cores: full passes of the
     headline workload until the budget is spent."""
@@ -296,6 +342,8 @@ def main():
         for c in synth.DECODE:
             work.append(run_fwd_case(rg, c, 256, 32, rotate=16, graph=True))
         work.append(run_merge_pass(rg, 5, 1))
+        for c in (synth.MID, synth.QPROJ):
+            work.append(run_bwd_case(rg, c, 20, 3))
         line["workloads"] = work
 
     if not args.no_cpu:
@@ -317,6 +365,8 @@ def only(rg, name, steps, warmup):
         res = run_fwd_case(rg, c, steps, warmup, rotate=16 if dec else 1, graph=dec)
     elif name == "merge":
         res = run_merge_pass(rg, steps, warmup)
+    elif name in ("bwd_mid", "bwd_q"):
+        res = run_bwd_case(rg, synth.MID if name == "bwd_mid" else synth.QPROJ, steps, warmup)
     elif name == "copy":
         # Plain device copy of a known size: the reference for counter scaling.
         n = 256 << 20

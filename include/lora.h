@@ -7,7 +7,9 @@
  *   [fastaf]  "fastaf: Minimal LoRA fine-tuning with hand-written Triton
  *             kernels", section "FWD kernel speedup": one LoRA layer computes
  *             out = X W^T + ((X A^T) B^T) * scale, scale = alpha / r, and the
- *             fused kernel keeps the [tokens, r] intermediate X A^T on chip.
+ *             fused kernel keeps the [tokens, r] intermediate X A^T on chip;
+ *             section "BWD kernel speedup": its backward produces dA, dB and
+ *             dX, and dA is parallelised over the sequence.
  *   [unsloth] unsloth commit log for scripts/benchmarks/qwen3_flex_inference.py,
  *             the entry that replaces copy+merge_adapter by one
  *             addmm(pristine, B, A, alpha=scaling, out=W_inf) per layer: the
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 3
+#define LORA_ABI_VERSION 4
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -58,7 +60,9 @@ typedef enum lora_status {
     LORA_ERR_UNSUPPORTED = 7, /* r > LORA_MAX_RANK, a size or ld beyond
                                  the limits below, or a forced variant that
                                  cannot run this shape */
-    LORA_ERR_HIP = 8          /* the HIP runtime reported a launch error */
+    LORA_ERR_HIP = 8,         /* the HIP runtime reported a launch error */
+    LORA_ERR_WORKSPACE = 9    /* lora_bwd workspace NULL, smaller than
+                                 lora_bwd_workspace_size or not 256-B aligned */
 } lora_status;
 
 #define LORA_MAX_LD ((1 << 22) - 8)
@@ -188,6 +192,53 @@ int lora_merge_batch(int dtype, int count, const lora_merge_desc *descs, void *s
 int lora_merge_inplace(int dtype, int64_t N, int64_t K, int64_t r,
                        void *W, int64_t ldw, const void *B, int64_t ldb,
                        const void *A, int64_t lda, float scale, void *stream);
+
+/*
+ * lora_bwd -- backward of the layer with W frozen   [fastaf], "BWD kernel
+ * speedup".
+ *
+ *   T[m,j]  = sum_k X[m,k] A[j,k]          G[m,j] = sum_n dY[m,n] B[n,j]
+ *   dX[m,k] = round( sum_n dY[m,n] W[n,k] + scale * sum_j G[m,j] A[j,k] )
+ *   dA[j,k] = round( scale * sum_m G[m,j] X[m,k] )
+ *   dB[n,j] = round( scale * sum_m dY[m,n] T[m,j] )
+ *
+ * T and G are rounded to bf16 once before the token contractions (they are
+ * MFMA operands there); everything else accumulates in fp32.  dA and dB are
+ * contracted over token ranges whose fp32 partial sums are then added in a
+ * fixed order: repeated calls give bitwise-identical results (no atomics).
+ *
+ *   dtype         LORA_BF16 only (LORA_F32: LORA_ERR_UNSUPPORTED).
+ *   M, N, K, r    tokens, d_out, d_in, rank; N and K multiples of 8.
+ *                 M == 0: dA = 0 and dB = 0 are written.  1 <= r <= 256, and
+ *                 (r padded to 16/32/64/128/256) * (M rounded up to 64)
+ *                 <= 2^30.
+ *   X, ldx        [M,K] layer input (the forward's X).
+ *   W, ldw        [N,K] base weight; only read for dX (may be NULL when dX is).
+ *   A, lda        [r,K] lora_A.       B, ldb   [N,r] lora_B.
+ *   dY, lddy      [M,N] gradient of the layer output.
+ *   scale         the adapter's scaling, as in the forward.
+ *   dX, lddx      [M,K] input gradient, or NULL to skip it (frozen input).
+ *   dA, ldda      [r,K] gradient of lora_A.
+ *   dB, lddb      [N,r] gradient of lora_B.
+ *   workspace     device scratch of workspace_bytes >= lora_bwd_workspace_size,
+ *                 256-byte aligned, owned by the caller; its content on entry
+ *                 is ignored and on return is unspecified.  Calls in flight at
+ *                 the same time need separate workspaces.
+ *   stream        hipStream_t as void*.
+ * ldx, lda, ldda, lddy and ldw multiples of 8; X, W, A, dY, dA 16-byte
+ * aligned.  Outputs and the workspace must not overlap any input or each
+ * other (LORA_ERR_ALIAS).  Returns a lora_status.
+ */
+int lora_bwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r,
+             const void *X, int64_t ldx, const void *W, int64_t ldw,
+             const void *A, int64_t lda, const void *B, int64_t ldb,
+             const void *dY, int64_t lddy, float scale,
+             void *dX, int64_t lddx, void *dA, int64_t ldda, void *dB, int64_t lddb,
+             void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes lora_bwd needs for these sizes (0 is possible), or -1 when
+ * dtype or the sizes are not supported.  Depends on the sizes only. */
+int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int64_t r);
 
 /* Static, NUL-terminated description of a lora_status value. */
 const char *lora_status_str(int status);

@@ -1,5 +1,5 @@
 """rank_gemm_amd -- Python binding of liblora.so, the MI355X (gfx950) fused
-LoRA linear forward and pristine merge.
+LoRA linear forward and backward and the pristine merge.
 
 The binding only marshals arguments: every step of the computation runs in
 the library's HIP kernels.  There is no CPU fallback; if the library cannot be
@@ -9,6 +9,7 @@ loaded, the first call raises.
     merge(W0, B, A, scale, out=W_inf)   # W_inf = W0 + scale * B A, W0 untouched
     merge_batch([(W0, B, A, scale, W_inf), ...])   # many targets, few launches
     merge_inplace(W, B, A, scale)       # W += scale * B A in place (not bit-reversible)
+    dX, dA, dB = bwd(X, W, A, B, dY, scale)   # gradients with W frozen (bf16)
 
 Tensors are torch tensors on the current HIP device, all bfloat16 or all
 float32, 2-D with unit inner stride (rows may be padded: the leading
@@ -34,6 +35,7 @@ LORA_ERR_DTYPE = 5
 LORA_ERR_ALIAS = 6
 LORA_ERR_UNSUPPORTED = 7
 LORA_ERR_HIP = 8
+LORA_ERR_WORKSPACE = 9
 LORA_F32 = 0
 LORA_BF16 = 1
 VARIANTS = {"auto": 0, "tiled": 1, "decode": 2}
@@ -41,7 +43,8 @@ MAX_RANK = 256
 DECODE_MAX_M = 64
 
 EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch",
-           "lora_merge_inplace", "lora_status_str", "lora_abi_version", "lora_fwd_pick")
+           "lora_merge_inplace", "lora_status_str", "lora_abi_version", "lora_fwd_pick",
+           "lora_bwd", "lora_bwd_workspace_size")
 
 
 class MergeDesc(ctypes.Structure):
@@ -88,6 +91,11 @@ def lib() -> ctypes.CDLL:
     L.lora_abi_version.restype = i32
     L.lora_fwd_pick.argtypes = [i32, i64, i64, i64, i64]
     L.lora_fwd_pick.restype = i32
+    L.lora_bwd.argtypes = [i32, i64, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64,
+                           f32, vp, i64, vp, i64, vp, i64, vp, i64, vp]
+    L.lora_bwd.restype = i32
+    L.lora_bwd_workspace_size.argtypes = [i32, i64, i64, i64, i64]
+    L.lora_bwd_workspace_size.restype = i64
     _lib = L
     return L
 
@@ -138,6 +146,22 @@ def merge_batch_raw(dtype: int, descs, stream: int = 0) -> int:
     if not isinstance(descs, ctypes.Array):
         descs = (MergeDesc * len(descs))(*descs)
     return int(lib().lora_merge_batch(dtype, len(descs), descs, stream or None))
+
+
+def bwd_workspace_size(dtype: int, M: int, N: int, K: int, r: int) -> int:
+    """lora_bwd_workspace_size: bytes, or -1 when not supported."""
+    return int(lib().lora_bwd_workspace_size(dtype, M, N, K, r))
+
+
+def bwd_raw(dtype: int, M: int, N: int, K: int, r: int, X: int, ldx: int, W: int, ldw: int,
+            A: int, lda: int, B: int, ldb: int, dY: int, lddy: int, scale: float, dX: int,
+            lddx: int, dA: int, ldda: int, dB: int, lddb: int, ws: int, ws_bytes: int,
+            stream: int = 0) -> int:
+    """lora_bwd with integer addresses (0 for NULL); returns the lora_status."""
+    return int(lib().lora_bwd(dtype, M, N, K, r, X or None, ldx, W or None, ldw, A or None, lda,
+                              B or None, ldb, dY or None, lddy, scale, dX or None, lddx,
+                              dA or None, ldda, dB or None, lddb, ws or None, ws_bytes,
+                              stream or None))
 
 
 # ------------------------------------------------------------ torch-facing
@@ -268,3 +292,47 @@ def merge_inplace(W, B, A, scale: float):
     _check(merge_inplace_raw(dt, N, K, r, pw, ldw, pb, ldb, pa, lda, float(scale), _stream(W.device)),
            "lora_merge_inplace")
     return W
+
+
+def bwd(X, W, A, B, dY, scale: float, want_dx: bool = True, workspace=None):
+    """Backward of the layer with W frozen (bf16 only): returns ``(dX, dA, dB)``
+
+    ``dX = dY W + scale (dY B) A``, ``dA = scale (dY B)^T X``,
+    ``dB = scale dY^T (X A^T)``; ``dX`` is None when ``want_dx`` is false (W may
+    then be None).  ``workspace``: a uint8 device tensor of at least
+    ``bwd_workspace_size`` bytes, allocated here when not given.
+    """
+    import torch
+    M, K = X.shape
+    N = dY.shape[1]
+    r = A.shape[0]
+    if (dY.shape[0] != M or A.shape[1] != K or tuple(B.shape) != (N, r)
+            or (want_dx and tuple(W.shape) != (N, K))):
+        raise ValueError(f"shape mismatch X{tuple(X.shape)} A{tuple(A.shape)} B{tuple(B.shape)} "
+                         f"dY{tuple(dY.shape)}" + (f" W{tuple(W.shape)}" if want_dx else ""))
+    dt = _dtype_code(X)
+    for t, nm in ((A, "A"), (B, "B"), (dY, "dY")) + (((W, "W"),) if want_dx else ()):
+        if t.dtype != X.dtype or t.device != X.device:
+            raise ValueError(f"{nm} must match X in dtype and device")
+    dev = X.device
+    need = bwd_workspace_size(dt, M, N, K, r)
+    if need < 0:
+        _check(LORA_ERR_UNSUPPORTED if dt == LORA_F32 else LORA_ERR_SHAPE, "lora_bwd")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    dA = torch.empty((r, K), dtype=X.dtype, device=dev)
+    dB = torch.empty((N, r), dtype=X.dtype, device=dev)
+    dX = torch.empty((M, K), dtype=X.dtype, device=dev) if want_dx else None
+    px, ldx = _mat(X, "X")
+    pa, lda = _mat(A, "A")
+    pb, ldb = _mat(B, "B")
+    pdy, lddy = _mat(dY, "dY")
+    pw, ldw = _mat(W, "W") if want_dx else (0, K)
+    pdx, lddx = _mat(dX, "dX") if want_dx else (0, K)
+    pda, ldda = _mat(dA, "dA")
+    pdb, lddb = _mat(dB, "dB")
+    st = bwd_raw(dt, M, N, K, r, px, ldx, pw, ldw, pa, lda, pb, ldb, pdy, lddy, float(scale),
+                 pdx, lddx, pda, ldda, pdb, lddb, workspace.data_ptr(), workspace.numel(),
+                 _stream(dev))
+    _check(st, "lora_bwd")
+    return dX, dA, dB

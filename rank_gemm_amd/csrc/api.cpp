@@ -91,6 +91,63 @@ int check_merge(int dtype, int64_t N, int64_t K, int64_t r, const void* W0, int6
   return LORA_OK;
 }
 
+// Workspace bytes of the backward, or -1 when the sizes are out of range.
+int64_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M < 0 || N < 0 || K < 0 || r < 1 || r > LORA_MAX_RANK) return -1;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return -1;
+  // T^T and G^T rows ([rank padded, M rounded to 64] bf16) are addressed with
+  // 32-bit byte offsets.
+  if ((int64_t)lora::pad_rank(r) * ((M + 63) / 64 * 64) > (int64_t(1) << 30)) return -1;
+  return lora::bwd_plan(M, N, K, r).bytes;
+}
+
+int check_bwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void* X, int64_t ldx,
+              const void* W, int64_t ldw, const void* A, int64_t lda, const void* B, int64_t ldb,
+              const void* dY, int64_t lddy, void* dX, int64_t lddx, void* dA, int64_t ldda,
+              void* dB, int64_t lddb, void* ws, int64_t ws_bytes) {
+  if (dtype == LORA_F32) return LORA_ERR_UNSUPPORTED;
+  if (dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || r < 1) return LORA_ERR_SHAPE;
+  const int64_t need = bwd_ws_bytes(M, N, K, r);
+  if (need < 0) return LORA_ERR_UNSUPPORTED;
+  const bool tok = M > 0, wantx = dX != nullptr && M > 0 && K > 0;
+  if ((K > 0 && (dA == nullptr || A == nullptr)) || (N > 0 && (dB == nullptr || B == nullptr)) ||
+      (tok && K > 0 && X == nullptr) || (tok && N > 0 && dY == nullptr) ||
+      (wantx && N > 0 && W == nullptr))
+    return LORA_ERR_NULL;
+  // X and dY are only read when there are tokens.
+  if ((tok && (ldx < K || lddy < N)) || lda < K || ldda < K || ldb < r || lddb < r ||
+      (wantx && (ldw < K || lddx < K)))
+    return LORA_ERR_STRIDE;
+  if ((tok && (ldx > LORA_MAX_LD || lddy > LORA_MAX_LD)) || lda > LORA_MAX_LD ||
+      N > LORA_MAX_LD || (wantx && ldw > LORA_MAX_LD))
+    return LORA_ERR_UNSUPPORTED;
+  if (K % 8 || N % 8 || (tok && (ldx % 8 || lddy % 8)) || lda % 8 || ldda % 8 ||
+      (wantx && ldw % 8))
+    return LORA_ERR_ALIGN;
+  if ((K > 0 && (!aligned16(A) || !aligned16(dA) || (tok && !aligned16(X)))) ||
+      (tok && N > 0 && !aligned16(dY)) || (wantx && N > 0 && !aligned16(W)) ||
+      (N > 0 && ((reinterpret_cast<uintptr_t>(B) & 1) || (reinterpret_cast<uintptr_t>(dB) & 1))) ||
+      (wantx && (reinterpret_cast<uintptr_t>(dX) & 1)))
+    return LORA_ERR_ALIGN;
+  if (need > 0 && (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255)))
+    return LORA_ERR_WORKSPACE;
+  // Outputs and workspace against every input and against each other.
+  const Range in[5] = {span(X, M, K, ldx, 2), span(W, wantx ? N : 0, K, ldw, 2),
+                       span(A, r, K, lda, 2), span(B, N, r, ldb, 2), span(dY, M, N, lddy, 2)};
+  const Range out[4] = {span(dX, wantx ? M : 0, K, lddx, 2), span(dA, r, K, ldda, 2),
+                        span(dB, N, r, lddb, 2),
+                        {reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) +
+                                                              static_cast<uintptr_t>(need)}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& x : in)
+      if (overlap(out[i], x)) return LORA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j])) return LORA_ERR_ALIAS;
+  }
+  return LORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +165,7 @@ const char* lora_status_str(int s) {
     case LORA_ERR_ALIAS: return "LORA_ERR_ALIAS: output overlaps an input";
     case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED: rank or variant not supported";
     case LORA_ERR_HIP: return "LORA_ERR_HIP: HIP launch error";
+    case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace missing, too small or misaligned";
     default: return "unknown lora_status";
   }
 }
@@ -231,5 +289,23 @@ int lora_merge_batch(int dtype, int count, const lora_merge_desc* descs, void* s
   return err == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
-}  // extern "C"
+int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (dtype != LORA_BF16) return -1;
+  return bwd_ws_bytes(M, N, K, r);
+}
 
+int lora_bwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void* X, int64_t ldx,
+             const void* W, int64_t ldw, const void* A, int64_t lda, const void* B, int64_t ldb,
+             const void* dY, int64_t lddy, float scale, void* dX, int64_t lddx, void* dA,
+             int64_t ldda, void* dB, int64_t lddb, void* workspace, int64_t workspace_bytes,
+             void* stream) {
+  const int st = check_bwd(dtype, M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, dY, lddy, dX, lddx,
+                           dA, ldda, dB, lddb, workspace, workspace_bytes);
+  if (st != LORA_OK) return st;
+  const lora::BwdArgs a{M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, dY, lddy, scale,
+                        (M > 0 && K > 0) ? dX : nullptr, lddx, dA, ldda, dB, lddb};
+  const hipError_t e = lora::launch_bwd_bf16(a, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,459 @@
+// bwd.hip -- backward of the fused LoRA linear layer, bf16 operands, fp32
+// accumulation, on gfx950 MFMA.
+//
+// With the base weight frozen, the backward of Y = X W^T + s (X A^T) B^T (the
+// gradients dA, dB and dX of "fastaf: Minimal LoRA fine-tuning with
+// hand-written Triton kernels", section "BWD kernel speedup") is
+//   T  = X A^T   [M, r]           G  = dY B    [M, r]
+//   dX = dY W + s G A             the forward of dY with W' = W^T, A' = B^T,
+//                                 B' = A^T: the tiled kernel's NN form
+//   dA = s G^T X  [r, K]          dB = s dY^T T  [N, r]
+// dA and dB contract over the tokens.  That page found a loop over the whole
+// sequence inside one program per output block starves the GPU, and moved dA
+// to a token-parallel split with atomic adds.  Here both are split over S
+// token ranges, each range writing fp32 partial sums that a second kernel
+// adds in a fixed order: every CU has work and the result is deterministic.
+//
+// Launches, in stream order, all through the caller's workspace:
+//   1. bt_kernel     B^T [r, N] bf16 (small)
+//   2. proj_kernel   T^T = A X^T and G^T = B^T dY^T, [r, Mp] bf16 each
+//   3. tc_kernel     dA and dB partial sums per token range, fp32
+//   4. red_kernel    dA, dB = round(s * ordered sum of the partials)
+//   5. dX: the tiled forward kernel in NN form on (dY, W, B^T, A)
+#include "common.h"
+#include "kernels.h"
+
+namespace lora {
+namespace {
+
+constexpr int cmaxi(int a, int b) { return a > b ? a : b; }
+constexpr int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
+
+// 128-B staged rows of 64 bf16 with 16-B chunks swizzled by row & 7: the MFMA
+// operand read pattern (16 rows at one chunk) is free of bank conflicts.
+__device__ __forceinline__ int row_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+// 128-B staged rows read with transposing reads (rows 8g + 0..3 of lane group
+// g at one 32-B segment): segments XOR-swizzled by bits 1 and 3 of the row put
+// each half wave's 8 rows in 8 distinct 32-B bank windows.
+__device__ __forceinline__ int tr_swz(int row) { return ((row >> 1) & 1) | ((row >> 2) & 2); }
+__device__ __forceinline__ int tr_off(int row, int col) {
+  return row * 128 + (((col >> 4) ^ tr_swz(row)) << 5) + ((col & 15) << 1);
+}
+
+// ---------------------------------------------------------------- B^T
+__global__ __launch_bounds__(256) void bt_kernel(int N, int r, const uint16_t* __restrict__ B,
+                                                 int64_t ldb, uint16_t* __restrict__ Bt,
+                                                 int64_t ldbt) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)r * N) return;
+  const int j = (int)(e / N), n = (int)(e % N);
+  Bt[(int64_t)j * ldbt + n] = B[(int64_t)n * ldb + j];
+}
+
+// ---------------------------------------------------------------- projection
+// P^T[j, m] = sum_c U[j, c] Z[m, c] for a tile of BT tokens, both operands
+// contraction-contiguous.  Job 0: Z = X, U = A (T); job 1: Z = dY, U = B^T (G).
+struct ProjJob {
+  const uint16_t* Z;
+  int64_t ldz;
+  int C;
+  const uint16_t* U;
+  int64_t ldu;
+  uint16_t* Pt;
+};
+
+template <int RP>
+struct Prj {
+  static constexpr int BT = 32, NW = 4, NT = NW * kWave, RB = RP / 16;
+  static constexpr int kRows = BT + RP;          // staged rows per stage: tokens, then ranks
+  static constexpr int kStageB = kRows * 128;    // 64 contraction values per row
+  static constexpr int kLoads = kRows / 8;       // 1-KiB loads per stage; the first 4 are Z
+  static constexpr int kUL = (RP / 8 + NW - 1) / NW;  // U load slots per wave
+  static constexpr int kLo = kLoads / NW, kHi = kLo + (kLoads % NW != 0 ? 1 : 0);
+  static constexpr int STAGES = clampi(96 * 1024 / kStageB, 2, 8);
+  static constexpr int kRedB = 2 * RB * kWave * 16;
+  static constexpr int kLds = cmaxi(STAGES * kStageB, kRedB);
+  static_assert(BT == 32 && NW == 4, "one Z load per wave per stage");
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+};
+
+// Wait until this wave's loads of all but its Newer most recent stages have
+// landed.  Load q of a stage is issued by wave q % NW.
+template <int Lo, int Hi, int Loads, int NW, int Newer>
+__device__ __forceinline__ void wait_own(int wave) {
+  if constexpr (Hi != Lo) {
+    if (wave < Loads % NW) {
+      wait_vmcnt<Newer * Hi>();
+      return;
+    }
+  }
+  wait_vmcnt<Newer * Lo>();
+}
+
+template <int RP>
+__global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, ProjJob j0, ProjJob j1,
+                                                           int64_t ldp) {
+  using P = Prj<RP>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const ProjJob jb = blockIdx.y == 0 ? j0 : j1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 15, lk = lane >> 4;
+  const int m0 = blockIdx.x * P::BT;
+  const int C = jb.C;
+
+  // Z rows of the tile (rows past M read zeros); U rows past r read zeros.
+  const int zrows = max(0, min(P::BT, M - m0));
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(jb.Z + (int64_t)m0 * jb.ldz), 0, (int)(zrows * jb.ldz * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ru =
+      __builtin_amdgcn_make_buffer_rsrc((void*)jb.U, 0, (int)(r * jb.ldu * 2), 0x00020000);
+  // Lane i of a 1-KiB load writes row 8q + i / 8, physical chunk i % 8.
+  const int lrl = lane >> 3;
+  const int lch = (lane & 7) ^ lrl;
+  const uint32_t vz = (uint32_t)((8 * wave + lrl) * jb.ldz * 2 + lch * 16);
+  const uint32_t vu = (uint32_t)((8 * wave + lrl) * jb.ldu * 2 + lch * 16);
+  const uint32_t su = (uint32_t)(8 * P::NW * jb.ldu * 2);
+
+  auto issue = [&](int st) {
+    unsigned char* base = smem + (st % P::STAGES) * P::kStageB;
+    const int c0 = st * 64;
+    const bool kin = c0 + lch * 8 < C;
+    const uint32_t cb = (uint32_t)c0 * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(base + wave * 1024), 16,
+                                             off_or_oob(kin, vz + sgpr(cb)), 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < P::kUL; ++s) {
+      const int p = wave + s * P::NW;  // U load index (stage load 4 + p)
+      if (p < RP / 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ru, (lds_void*)(base + (4 + p) * 1024), 16, off_or_oob(kin, vu + sgpr(s * su + cb)),
+            0, 0, 0);
+    }
+  };
+
+  // Wave w: token block w & 1, k32 half w >> 1 of every stage.
+  const int tb = wave & 1, half = wave >> 1;
+  f32x4 acc[P::RB];
+#pragma unroll
+  for (int i = 0; i < P::RB; ++i) acc[i] = zero4();
+
+  const int nk = (C + 63) / 64;
+#pragma unroll
+  for (int s = 0; s < P::STAGES - 1; ++s) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_own<P::kLo, P::kHi, P::kLoads, P::NW, P::STAGES - 2>(wave);
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + P::STAGES - 1);
+    const unsigned char* sb = smem + (kt % P::STAGES) * P::kStageB;
+    const int ch = 4 * half + lk;
+    const u32x4 z = *reinterpret_cast<const u32x4*>(sb + row_off(16 * tb + lrow, ch));
+#pragma unroll
+    for (int i = 0; i < P::RB; ++i) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(sb + row_off(P::BT + 16 * i + lrow, ch));
+      acc[i] = mfma16x16x32(u, z, acc[i]);
+    }
+  }
+  // Loads of the stages past the end (zeros) may still be landing in the ring.
+  wait_vmcnt<0>();
+  wait_lgkm0();
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < P::RB; ++i) red[(tb * P::RB + i) * kWave + lane] = acc[i];
+  }
+  __syncthreads();
+  if (half == 0) {
+    const int64_t m = m0 + 16 * tb + lrow;  // < ldp: the grid covers ldp / BT tiles
+#pragma unroll
+    for (int i = 0; i < P::RB; ++i) {
+      const f32x4 o = red[(tb * P::RB + i) * kWave + lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = 16 * i + 4 * lk + q;
+        if (j < r) jb.Pt[(int64_t)j * ldp + m] = f2bf(acc[i][q] + o[q]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- token contraction
+// Partial sums over one token range of out[j, c] = sum_m P^T[j, m] Q[m, c]
+// for a 64-column tile of Q.  Job 0: Q = X, P^T = G^T (dA, partials stored
+// [S][RP][K]); job 1: Q = dY, P^T = T^T (dB, partials stored [S][N][RP]).
+struct TcJob {
+  const uint16_t* Q;
+  int64_t ldq;
+  int C;
+  const uint16_t* Pt;
+  float* part;
+};
+
+template <int RP>
+struct Tc {
+  static constexpr int BC = 64, BMT = 64, NW = 4, NT = NW * kWave, RB = RP / 16;
+  static constexpr int kQB = BMT * BC * 2;       // Q stage: 64 token rows of 64 columns
+  static constexpr int kPB = RP * BMT * 2;       // P stage: RP rank rows of 64 tokens
+  static constexpr int kStageB = kQB + kPB;
+  static constexpr int kLoads = 8 + RP / 8;      // 1-KiB loads per stage; the first 8 are Q
+  static constexpr int kPL = (RP / 8 + NW - 1) / NW;  // P load slots per wave
+  static constexpr int kLo = kLoads / NW, kHi = kLo + (kLoads % NW != 0 ? 1 : 0);
+  static constexpr int STAGES = clampi(96 * 1024 / kStageB, 2, 4);
+  static constexpr int kLds = STAGES * kStageB;
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+};
+
+template <int RP>
+__global__ __launch_bounds__(Tc<RP>::NT) void tc_kernel(int M, int r, TcJob j0, TcJob j1,
+                                                        int64_t ldp, int tiles0, int tiles1,
+                                                        int tps) {
+  using T = Tc<RP>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 15, lk = lane >> 4;
+  const int per = tiles0 + tiles1;
+  const int split = blockIdx.x / per, rem = blockIdx.x % per;
+  const int job = rem < tiles0 ? 0 : 1;
+  const TcJob jb = job == 0 ? j0 : j1;
+  const int c0 = (job == 0 ? rem : rem - tiles0) * T::BC;
+  const int t0 = split * tps, t1 = min(M, t0 + tps);
+  const int C = jb.C;
+
+  // Q load q < 8 covers token rows 8q .. 8q + 7 of the stage (lane i: row
+  // 8q + i / 8, physical chunk i % 8, fetching the chunk the segment swizzle
+  // puts there); P load p covers rank rows 8p .. 8p + 7.
+  const int lrl = lane >> 3, pc = lane & 7;
+  const int qrow = 8 * wave + lrl;  // + 32 for the second Q slot: same swizzle
+  const int qch = 2 * ((pc >> 1) ^ tr_swz(qrow)) + (pc & 1);
+  const uint32_t vq = (uint32_t)(qrow * jb.ldq * 2 + qch * 16);
+  const uint32_t sq = (uint32_t)(32 * jb.ldq * 2);
+  const int pch = pc ^ lrl;
+  const uint32_t vp = (uint32_t)((8 * wave + lrl) * ldp * 2 + pch * 16);
+  const uint32_t sp = (uint32_t)(8 * T::NW * ldp * 2);
+
+  auto issue = [&](int st) {
+    unsigned char* base = smem + (st % T::STAGES) * T::kStageB;
+    const int t = t0 + st * T::BMT;
+    const bool live = t < t1;  // wave-uniform; stages past the range read zeros
+    const int qrows = live ? min(T::BMT, M - t) : 0;
+    // From column c0 of row t to the last valid element of row t + qrows - 1:
+    // rows past M read zeros and no read leaves Q.  Columns past C on earlier
+    // rows read the next row; they only reach columns that are never stored.
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(jb.Q + (int64_t)(live ? t : 0) * jb.ldq + c0), 0,
+        qrows > 0 ? (int)(((qrows - 1) * jb.ldq + (C - c0)) * 2) : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(jb.Pt + (live ? t : 0)), 0, live ? (int)((r * ldp - t) * 2) : 0, 0x00020000);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(base + (wave + s * T::NW) * 1024),
+                                               16, vq + sgpr(s * sq), 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < T::kPL; ++s) {
+      const int p = wave + s * T::NW;  // stage load 8 + p
+      if (p < RP / 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rp, (lds_void*)(base + T::kQB + p * 1024), 16, vp + sgpr(s * sp), 0, 0, 0);
+    }
+  };
+
+  f32x4 acc[T::RB];
+#pragma unroll
+  for (int i = 0; i < T::RB; ++i) acc[i] = zero4();
+
+  const int nst = t1 > t0 ? (t1 - t0 + T::BMT - 1) / T::BMT : 0;
+#pragma unroll
+  for (int s = 0; s < T::STAGES - 1; ++s) issue(s);
+  const int qcol = 16 * wave + 4 * (lrow & 3);  // wave w owns columns 16w .. 16w + 15
+  for (int kt = 0; kt < nst; ++kt) {
+    wait_own<T::kLo, T::kHi, T::kLoads, T::NW, T::STAGES - 2>(wave);
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + T::STAGES - 1);
+    const unsigned char* sb = smem + (kt % T::STAGES) * T::kStageB;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 32 * u + 8 * lk + (lrow >> 2);
+      const u32x2 lo = lds_read_tr16(sb + tr_off(row, qcol));
+      const u32x2 hi = lds_read_tr16(sb + tr_off(row + 4, qcol));
+      const u32x4 q = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int i = 0; i < T::RB; ++i) {
+        const u32x4 p =
+            *reinterpret_cast<const u32x4*>(sb + T::kQB + row_off(16 * i + lrow, 4 * u + lk));
+        acc[i] = mfma16x16x32(p, q, acc[i]);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+
+  // acc[i] lane: column c0 + 16 w + lrow, ranks 16 i + 4 lk + 0..3.
+  const int c = c0 + 16 * wave + lrow;
+  if (c >= C) return;
+  if (job == 0) {
+    float* part = jb.part + (int64_t)split * RP * C;
+#pragma unroll
+    for (int i = 0; i < T::RB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part[(int64_t)(16 * i + 4 * lk + q) * C + c] = acc[i][q];
+  } else {
+    float* part = jb.part + ((int64_t)split * C + c) * RP;
+#pragma unroll
+    for (int i = 0; i < T::RB; ++i) *reinterpret_cast<f32x4*>(part + 16 * i + 4 * lk) = acc[i];
+  }
+}
+
+// ---------------------------------------------------------------- reduce
+// dA[j, k] = round(s * sum_split partA[split][j][k]) and
+// dB[n, j] = round(s * sum_split partB[split][n][j]), splits added in order.
+// One thread per 4 consecutive outputs of a row.
+__global__ __launch_bounds__(256) void red_kernel(int S, int r, int RP, int K, int N,
+                                                  const float* __restrict__ pa,
+                                                  const float* __restrict__ pb, float scale,
+                                                  uint16_t* __restrict__ dA, int64_t ldda,
+                                                  uint16_t* __restrict__ dB, int64_t lddb,
+                                                  int64_t na) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < na) {
+    const int k4 = K / 4;
+    const int j = (int)(e / k4), k = (int)(e % k4) * 4;
+    f32x4 s4 = zero4();
+    for (int sp = 0; sp < S; ++sp)
+      s4 += *reinterpret_cast<const f32x4*>(pa + ((int64_t)sp * RP + j) * K + k);
+    uint32_t* out = reinterpret_cast<uint32_t*>(dA + (int64_t)j * ldda + k);
+    out[0] = pack_bf2(scale * s4[0], scale * s4[1]);
+    out[1] = pack_bf2(scale * s4[2], scale * s4[3]);
+    return;
+  }
+  const int64_t f = e - na;
+  const int r4 = (r + 3) / 4;
+  if (f >= (int64_t)N * r4) return;
+  const int n = (int)(f / r4), j = (int)(f % r4) * 4;
+  f32x4 s4 = zero4();
+  for (int sp = 0; sp < S; ++sp)
+    s4 += *reinterpret_cast<const f32x4*>(pb + ((int64_t)sp * N + n) * RP + j);
+  uint16_t* out = dB + (int64_t)n * lddb + j;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (j + q < r) out[q] = f2bf(scale * s4[q]);
+}
+
+template <int RP>
+hipError_t launch_proj_tc(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, hipStream_t s) {
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K, r = (int)a.r;
+  const uint16_t* Bt = reinterpret_cast<const uint16_t*>(ws + p.off_bt);
+  uint16_t* Tt = reinterpret_cast<uint16_t*>(ws + p.off_tt);
+  uint16_t* Gt = reinterpret_cast<uint16_t*>(ws + p.off_gt);
+  {
+    ProjJob jt{static_cast<const uint16_t*>(a.X), a.ldx, K, static_cast<const uint16_t*>(a.A),
+               a.lda, Tt};
+    ProjJob jg{static_cast<const uint16_t*>(a.dY), a.lddy, N, Bt, p.ldbt, Gt};
+    auto kern = proj_kernel<RP>;
+    static std::atomic<uint64_t> done{0};
+    if (hipError_t e = ensure_lds(kern, Prj<RP>::kLds, done); e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(p.ldp / Prj<RP>::BT), 2), dim3(Prj<RP>::NT),
+                       Prj<RP>::kLds, s, M, r, jt, jg, p.ldp);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  {
+    TcJob ja{static_cast<const uint16_t*>(a.X), a.ldx, K, Gt,
+             reinterpret_cast<float*>(ws + p.off_pa)};
+    TcJob jbb{static_cast<const uint16_t*>(a.dY), a.lddy, N, Tt,
+              reinterpret_cast<float*>(ws + p.off_pb)};
+    const int tiles0 = (K + 63) / 64, tiles1 = (N + 63) / 64;
+    const int64_t grid = (int64_t)(tiles0 + tiles1) * p.S;
+    if (grid > 0) {
+      auto kern = tc_kernel<RP>;
+      static std::atomic<uint64_t> done{0};
+      if (hipError_t e = ensure_lds(kern, Tc<RP>::kLds, done); e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Tc<RP>::NT), Tc<RP>::kLds, s, M, r, ja,
+                         jbb, p.ldp, tiles0, tiles1, (int)p.tps);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+}  // namespace
+
+BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
+  BwdPlan p{};
+  const int64_t RP = pad_rank(r);
+  p.ldbt = (N + 7) / 8 * 8;
+  p.ldp = (M + 63) / 64 * 64;
+  // Token ranges: aim at ~512 workgroups for the token contraction, keep the
+  // fp32 partials (S * RP * (K + N) * 4 bytes) within 1/8 of the bytes of X
+  // and dY that it streams (M * (K + N) * 2), and never split below one
+  // 64-token stage.
+  const int64_t stages = p.ldp / 64;
+  const int64_t tiles = (K + 63) / 64 + (N + 63) / 64;
+  int64_t S = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
+  S = std::min<int64_t>(S, std::max<int64_t>(1, M / (16 * RP)));
+  S = std::max<int64_t>(1, std::min<int64_t>(S, stages));
+  const int64_t per = stages > 0 ? (stages + S - 1) / S : 1;  // stages per range
+  p.tps = per * 64;
+  p.S = M > 0 ? (int)((M + p.tps - 1) / p.tps) : 0;
+  int64_t off = 0;
+  p.off_bt = off; off = align256(off + r * p.ldbt * 2);
+  p.off_tt = off; off = align256(off + r * p.ldp * 2);
+  p.off_gt = off; off = align256(off + r * p.ldp * 2);
+  p.off_pa = off; off = align256(off + (int64_t)p.S * RP * K * 4);
+  p.off_pb = off; off = align256(off + (int64_t)p.S * N * RP * 4);
+  p.bytes = off;
+  return p;
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, void* workspace, hipStream_t s) {
+  const BwdPlan p = bwd_plan(a.M, a.N, a.K, a.r);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const int N = (int)a.N, K = (int)a.K, r = (int)a.r;
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
+  // 1. B^T (also the dX kernel's down-projection operand).
+  if ((int64_t)r * N > 0) {
+    hipLaunchKernelGGL(bt_kernel, dim3((unsigned)(((int64_t)r * N + 255) / 256)), dim3(256), 0, s,
+                       N, r, static_cast<const uint16_t*>(a.B), a.ldb, Bt, p.ldbt);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  // 2-3. T, G and the partial sums (nothing to do without tokens).
+  if (a.M > 0) {
+    hipError_t e;
+    switch (pad_rank(a.r)) {
+      case 16: e = launch_proj_tc<16>(a, p, ws, s); break;
+      case 32: e = launch_proj_tc<32>(a, p, ws, s); break;
+      case 64: e = launch_proj_tc<64>(a, p, ws, s); break;
+      case 128: e = launch_proj_tc<128>(a, p, ws, s); break;
+      default: e = launch_proj_tc<256>(a, p, ws, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  // 4. dA, dB (zeros when there are no tokens).
+  {
+    const int64_t na = (int64_t)r * (K / 4);
+    const int64_t total = na + (int64_t)N * ((r + 3) / 4);
+    if (total > 0) {
+      hipLaunchKernelGGL(red_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p.S, r,
+                         pad_rank(a.r), K, N, reinterpret_cast<const float*>(ws + p.off_pa),
+                         reinterpret_cast<const float*>(ws + p.off_pb), a.scale,
+                         static_cast<uint16_t*>(a.dA), a.ldda, static_cast<uint16_t*>(a.dB),
+                         a.lddb, na);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+  }
+  // 5. dX = dY W + s (dY B) A: the forward of dY in NN form.
+  if (a.dX != nullptr && a.M > 0 && a.K > 0) {
+    FwdArgs f{a.M, a.K, a.N, a.r, a.dY, a.lddy, a.W, a.ldw, Bt, p.ldbt, a.A, a.lda, a.scale,
+              a.dX, a.lddx};
+    return launch_fwd_tiled_bf16_nn(f, s);
+  }
+  return hipSuccess;
+}
+
+}  // namespace lora

@@ -29,7 +29,6 @@ namespace {
 
 constexpr uint32_t kDecOob = 0x80000000u;  // offset past any resource's range
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // AL: A (and, with XL, the single X row) reach the waves through LDS: each
 // wave stages the rows of its own K range with 16-B-per-lane DMA loads
@@ -55,12 +54,6 @@ struct Dec {
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int MB, int RB, int U, int NW, bool AL, bool XL>

@@ -44,17 +44,44 @@ struct MergeArgs {
   void* Wi; int64_t ldwi;
 };
 
+struct BwdArgs {
+  int64_t M, N, K, r;
+  const void* X; int64_t ldx;
+  const void* W; int64_t ldw;
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  const void* dY; int64_t lddy;
+  float scale;
+  void* dX; int64_t lddx;   // may be null: no input gradient
+  void* dA; int64_t ldda;
+  void* dB; int64_t lddb;
+};
+
+// Workspace layout of the backward (byte offsets from a 256-B aligned base):
+// B^T [r, ldbt] bf16, T^T and G^T [r, ldp] bf16, the fp32 partial sums of dA
+// [S][RP][K] and of dB [S][N][RP] over S token ranges of tps tokens.
+struct BwdPlan {
+  int S;
+  int64_t tps, ldbt, ldp;
+  int64_t off_bt, off_tt, off_gt, off_pa, off_pb, bytes;
+};
+
 // Rank padded to the MFMA-friendly size the kernels are instantiated for.
 inline int pad_rank(int64_t r) {
   return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : r <= 128 ? 128 : 256;
 }
 
 hipError_t launch_fwd_tiled_bf16(const FwdArgs& a, hipStream_t s);
+// NN form: a.W is [K, N] (ldw >= N) and a.B is [r, N] (ldb >= N); otherwise
+// as launch_fwd_tiled_bf16.  Requires N % 8 == 0 in addition.
+hipError_t launch_fwd_tiled_bf16_nn(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_tiled_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge_bf16(const MergeArgs& a, hipStream_t s);
 hipError_t launch_merge_f32(const MergeArgs& a, hipStream_t s);
 hipError_t launch_merge_bf16_batch(const MergeArgs* a, int count, hipStream_t s);
+BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r);
+hipError_t launch_bwd_bf16(const BwdArgs& a, void* workspace, hipStream_t s);
 
 // Largest rank the decode kernel is instantiated for.
 constexpr int kDecodeMaxRank = 32;

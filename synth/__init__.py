@@ -10,8 +10,9 @@ Recipe (stated once, used everywhere):
     the pages' ``N(0, v)`` is read as mean 0, *variance* v.
   * narrowed to float32 with round-to-nearest-even (numpy ``astype``), then,
     for bf16 workloads, to bf16 with round-to-nearest-even on the fp32 bits.
-  * tensor ids: X=0, W/W0=1, A=2, B=3; merge cycle c draws A with id 10c+2
-    and B with id 10c+3 (cycle 0 therefore uses 2 and 3).
+  * tensor ids: X=0, W/W0=1, A=2, B=3, dY (the output gradient of a
+    backward case, N(0, 1)) = 4; merge cycle c draws A with id 10c+2 and B
+    with id 10c+3 (cycle 0 therefore uses 2 and 3).
 
 bf16 tensors are returned as ``numpy.uint16`` bit patterns; fp32 tensors as
 ``numpy.float32``.  Both sides consume exactly these values.
@@ -24,7 +25,7 @@ from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
-TX, TW, TA, TB = 0, 1, 2, 3
+TX, TW, TA, TB, TDY = 0, 1, 2, 3, 4
 
 
 def _rng(group: int, case: int, tensor: int) -> np.random.Generator:
@@ -118,6 +119,8 @@ class FwdCase:
             out["A"] = normal(self.group, self.case, TA, (self.r, self.K), va, self.dtype)
         if "B" in parts:
             out["B"] = normal(self.group, self.case, TB, (self.N, self.r), self.var_b, self.dtype)
+        if "D" in parts:
+            out["dY"] = normal(self.group, self.case, TDY, (self.M, self.N), 1.0, self.dtype)
         return out
 
 
@@ -212,6 +215,11 @@ def device_normal(group: int, case: int, tensor: int, shape, var: float, dtype: 
     x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
     x.mul_(math.sqrt(var))
     return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def dy_on_device(c: FwdCase, device="cuda"):
+    """The output gradient of a backward case, drawn on the device."""
+    return device_normal(c.group, c.case, TDY, (c.M, c.N), 1.0, c.dtype, device)
 
 
 def fwd_case_on_device(c: FwdCase, device="cuda"):

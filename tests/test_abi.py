@@ -33,8 +33,8 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 3
-    for s in range(9):
+    assert rg.abi_version() == 4
+    for s in range(10):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
 
@@ -198,3 +198,69 @@ def test_torch_wrapper_rejects_cpu_tensors():
     with pytest.raises(TypeError):
         rg.fwd(X.half(), torch.zeros(8, 8).half(), torch.zeros(2, 8).half(),
                torch.zeros(8, 2).half(), 1.0)
+
+
+# Backward: a consistent argument set and single-field variations.  Every case
+# fails validation, so nothing is launched.
+PDX, PDA, PDB, PWS = (0x60000000 + 0x10000000 * i for i in range(4))
+
+
+def _bwd(**kw):
+    a = dict(dtype=rg.LORA_BF16, M=64, N=64, K=64, r=16, X=PX, ldx=64, W=PW, ldw=64, A=PA, lda=64,
+             B=PB, ldb=16, dY=PY, lddy=64, scale=2.0, dX=PDX, lddx=64, dA=PDA, ldda=64, dB=PDB,
+             lddb=16, ws=PWS, ws_bytes=1 << 24)
+    a.update(kw)
+    return rg.bwd_raw(a["dtype"], a["M"], a["N"], a["K"], a["r"], a["X"], a["ldx"], a["W"],
+                      a["ldw"], a["A"], a["lda"], a["B"], a["ldb"], a["dY"], a["lddy"], a["scale"],
+                      a["dX"], a["lddx"], a["dA"], a["ldda"], a["dB"], a["lddb"], a["ws"],
+                      a["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=rg.LORA_F32), rg.LORA_ERR_UNSUPPORTED),
+    (dict(dtype=4), rg.LORA_ERR_DTYPE),
+    (dict(M=-1), rg.LORA_ERR_SHAPE),
+    (dict(r=0), rg.LORA_ERR_SHAPE),
+    (dict(r=257, ldb=257, lddb=257), rg.LORA_ERR_UNSUPPORTED),
+    (dict(M=1 << 24, r=128, ldb=128, lddb=128), rg.LORA_ERR_UNSUPPORTED),  # r * M past 2^30
+    (dict(X=0), rg.LORA_ERR_NULL),
+    (dict(A=0), rg.LORA_ERR_NULL),
+    (dict(B=0), rg.LORA_ERR_NULL),
+    (dict(dY=0), rg.LORA_ERR_NULL),
+    (dict(W=0), rg.LORA_ERR_NULL),                      # W needed for dX
+    (dict(dA=0), rg.LORA_ERR_NULL),
+    (dict(dB=0), rg.LORA_ERR_NULL),
+    (dict(ldx=56), rg.LORA_ERR_STRIDE),
+    (dict(lddy=32), rg.LORA_ERR_STRIDE),
+    (dict(lddx=8), rg.LORA_ERR_STRIDE),
+    (dict(lddb=15), rg.LORA_ERR_STRIDE),
+    (dict(ldda=63), rg.LORA_ERR_STRIDE),
+    (dict(ldx=1 << 22), rg.LORA_ERR_UNSUPPORTED),
+    (dict(K=60, ldx=64, ldw=64, lda=64, ldda=64, lddx=64), rg.LORA_ERR_ALIGN),   # K % 8
+    (dict(N=60, lddy=64), rg.LORA_ERR_ALIGN),                                    # N % 8
+    (dict(lddy=68), rg.LORA_ERR_ALIGN),
+    (dict(X=PX + 2), rg.LORA_ERR_ALIGN),
+    (dict(dA=PDA + 8), rg.LORA_ERR_ALIGN),
+    (dict(dB=PDB + 1), rg.LORA_ERR_ALIGN),
+    (dict(ws=0), rg.LORA_ERR_WORKSPACE),
+    (dict(ws=PWS + 16), rg.LORA_ERR_WORKSPACE),          # not 256-B aligned
+    (dict(ws_bytes=100), rg.LORA_ERR_WORKSPACE),
+    (dict(dX=PX), rg.LORA_ERR_ALIAS),                    # dX over X
+    (dict(dA=PA), rg.LORA_ERR_ALIAS),                    # dA over A
+    (dict(dB=PDA + 64), rg.LORA_ERR_ALIAS),              # dB inside dA
+    (dict(ws=PY), rg.LORA_ERR_ALIAS),                    # workspace over dY
+])
+def test_bwd_rejects_before_any_hip_call(kw, want):
+    assert _bwd(**kw) == want
+
+
+def test_bwd_workspace_size():
+    assert rg.bwd_workspace_size(rg.LORA_F32, 64, 64, 64, 16) == -1
+    assert rg.bwd_workspace_size(rg.LORA_BF16, 64, 64, 64, 0) == -1
+    n = rg.bwd_workspace_size(rg.LORA_BF16, 4096, 1024, 1024, 16)
+    assert n > 0 and n % 256 == 0
+    # grows with the tokens only through T, G and the token ranges: bounded
+    assert rg.bwd_workspace_size(rg.LORA_BF16, 1 << 20, 1024, 1024, 16) < (1 << 30)
+    # a workspace one byte short is refused
+    assert _bwd(M=4096, N=1024, K=1024, ldx=1024, ldw=1024, lda=1024, lddy=1024, lddx=1024,
+                ldda=1024, ws_bytes=n - 1) == rg.LORA_ERR_WORKSPACE

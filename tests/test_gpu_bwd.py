@@ -1,0 +1,167 @@
+"""Parity of the HIP backward (lora_bwd) against the fp64 oracle, through the
+C ABI, on seeded inputs.
+
+Bar: the forward's bf16 bar applied to each gradient, relative Frobenius error
+<= 1e-2 for dX, dA and dB (bf16 inputs, fp32 accumulation, bf16 outputs);
+bitwise equality with the oracle's rounding where every intermediate is
+exactly representable (small-integer inputs), and between repeated calls (the
+token ranges are added in a fixed order, no atomics).  Full-size workloads are
+checked on every dA and dB entry and on sampled dX rows (row m of dX depends
+on row m of dY only).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import TOL, as_f64, rel_fro, sample_rows, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, case, M, N, K, r, dtype="bf16"):
+    return synth.FwdCase(name, 6, case, M, N, K, r, 2.0 * r, dtype)
+
+
+def _run(rg, t, scale, want_dx=True):
+    import torch
+    X, W, A, B, dY = (to_dev(t[k]) for k in ("X", "W", "A", "B", "dY"))
+    dX, dA, dB = rg.bwd(X, W if want_dx else None, A, B, dY, scale, want_dx=want_dx)
+    torch.cuda.synchronize()
+    return (to_host(dX) if dX is not None else None), to_host(dA), to_host(dB)
+
+
+def _check(name, got, ref):
+    errs = [rel_fro(as_f64(g), r) for g, r in zip(got, ref)]
+    print(f"{name}: rel_fro dX={errs[0]:.3e} dA={errs[1]:.3e} dB={errs[2]:.3e}")
+    for g in got:
+        assert np.isfinite(as_f64(g)).all()
+    assert max(errs) <= TOL["bf16"], errs
+
+
+# Ragged shapes spanning several tiles, token ranges and every padded rank
+# (16, 32, 64, 128, 256); N and K multiples of 8 as the ABI requires.
+SHAPES = [
+    ("b_m64_n64_k64_r16", 64, 64, 64, 16),
+    ("b_m300_n136_k264_r5", 300, 136, 264, 5),
+    ("b_m1000_n512_k768_r16", 1000, 512, 768, 16),
+    ("b_m513_n256_k384_r33", 513, 256, 384, 33),
+    ("b_m200_n392_k200_r100", 200, 392, 200, 100),
+    ("b_m130_n256_k520_r130", 130, 256, 520, 130),
+    ("b_m1_n512_k256_r16", 1, 512, 256, 16),
+    ("b_m63_n8_k8_r3", 63, 8, 8, 3),
+    ("b_m2049_n128_k96_r24", 2049, 128, 96, 24),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_bwd_ragged_full(gpu_lib, shape):
+    name, M, N, K, r = shape
+    c = _case(name, SHAPES.index(shape), M, N, K, r)
+    t = c.make("XWABD")
+    got = _run(gpu_lib, t, c.scale)
+    ref = oracle.bwd(t["X"], t["W"], t["A"], t["B"], t["dY"], c.scale)
+    _check(name, got, ref)
+
+
+def test_bwd_mid_full(gpu_lib):
+    """The mid-size workload (X[4096,1024], W[1024,1024], r 16) in full."""
+    c = synth.MID
+    t = c.make("XWABD")
+    got = _run(gpu_lib, t, c.scale)
+    ref = oracle.bwd(t["X"], t["W"], t["A"], t["B"], t["dY"], c.scale)
+    _check(c.name, got, ref)
+
+
+@pytest.mark.parametrize("c", [synth.QPROJ, _case("b_m4096_n512_k4096_r16", 20, 4096, 512, 4096, 16),
+                               _case("b_m4096_n256_k4096_r128", 21, 4096, 256, 4096, 128)],
+                         ids=lambda c: c.name)
+def test_bwd_large_sampled_rows(gpu_lib, c):
+    """256 x 256 (rank <= 32) and grouped rank-128 dX tiles at full size: all
+    of dA and dB, sampled rows of dX."""
+    t = c.make("XWABD")
+    got = _run(gpu_lib, t, c.scale)
+    rows = sample_rows(c.M, 24, seed=c.case)
+    dys = np.ascontiguousarray(t["dY"][rows])
+    _, dA, dB = oracle.bwd(t["X"], t["W"], t["A"], t["B"], t["dY"], c.scale, dx_rows=(0, 0))
+    dX, _, _ = oracle.bwd(np.ascontiguousarray(t["X"][rows]), t["W"], t["A"], t["B"], dys, c.scale)
+    _check(c.name, (got[0][rows], got[1], got[2]), (dX, dA, dB))
+
+
+def test_bwd_integer_inputs_bitwise(gpu_lib):
+    """Entries in {-1, 0, 1} and scale 2: T (|T| <= K = 192) and G
+    (|G| <= N = 128) are integers exact in bf16, every fp32 sum is exact, so
+    each gradient is the oracle's exact value rounded once to bf16."""
+    M, N, K, r = 200, 128, 192, 16
+    rng = np.random.default_rng(5)
+
+    def ints(shape):
+        return synth.f32_to_bf16_bits(rng.integers(-1, 2, size=shape).astype(np.float32))
+
+    t = {"X": ints((M, K)), "W": ints((N, K)), "A": ints((r, K)), "B": ints((N, r)),
+         "dY": ints((M, N))}
+    got = _run(gpu_lib, t, 2.0)
+    ref = oracle.bwd(t["X"], t["W"], t["A"], t["B"], t["dY"], 2.0)
+    for g, e in zip(got, ref):
+        assert np.array_equal(g, oracle.round_bf16(e))
+
+
+def test_bwd_without_dx_and_repeatable(gpu_lib):
+    c = _case("b_m700_n264_k328_r16", 30, 700, 264, 328, 16)
+    t = c.make("XWABD")
+    full = _run(gpu_lib, t, c.scale)
+    again = _run(gpu_lib, t, c.scale)
+    part = _run(gpu_lib, t, c.scale, want_dx=False)
+    assert part[0] is None
+    for a, b in zip(full, again):
+        assert np.array_equal(a, b)
+    assert np.array_equal(part[1], full[1]) and np.array_equal(part[2], full[2])
+
+
+def test_bwd_no_tokens_writes_zero_gradients(gpu_lib):
+    import torch
+    dev = "cuda"
+    K, N, r = 64, 48, 8
+    X = torch.empty((0, K), dtype=torch.bfloat16, device=dev)
+    dY = torch.empty((0, N), dtype=torch.bfloat16, device=dev)
+    W = torch.randn((N, K), device=dev).to(torch.bfloat16)
+    A = torch.randn((r, K), device=dev).to(torch.bfloat16)
+    B = torch.randn((N, r), device=dev).to(torch.bfloat16)
+    dX, dA, dB = gpu_lib.bwd(X, W, A, B, dY, 1.5)
+    torch.cuda.synchronize()
+    assert dX.shape == (0, K)
+    assert (dA.float() == 0).all() and (dB.float() == 0).all()
+
+
+def test_bwd_strided_operands(gpu_lib):
+    """Every operand a row-padded view; padding never read or written."""
+    import torch
+    M, N, K, r = 257, 136, 200, 12
+    c = _case("b_strided", 31, M, N, K, r)
+    t = c.make("XWABD")
+
+    def padded(a, extra, fill=float("nan")):
+        d = to_dev(a)
+        big = torch.full((d.shape[0], d.shape[1] + extra), fill, dtype=d.dtype, device=d.device)
+        big[:, : d.shape[1]] = d
+        return big[:, : d.shape[1]]
+
+    X, W, A, dY = (padded(t[k], 24) for k in ("X", "W", "A", "dY"))
+    B = padded(t["B"], 5)
+    dXb = torch.full((M, K + 16), 7.0, dtype=torch.bfloat16, device="cuda")
+    dAb = torch.full((r, K + 8), 7.0, dtype=torch.bfloat16, device="cuda")
+    dBb = torch.full((N, r + 3), 7.0, dtype=torch.bfloat16, device="cuda")
+    need = gpu_lib.bwd_workspace_size(gpu_lib.LORA_BF16, M, N, K, r)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    p = gpu_lib._mat
+    st = gpu_lib.bwd_raw(gpu_lib.LORA_BF16, M, N, K, r, *p(X, "X"), *p(W, "W"), *p(A, "A"),
+                         *p(B, "B"), *p(dY, "dY"), c.scale, *p(dXb[:, :K], "dX"),
+                         *p(dAb[:, :K], "dA"), *p(dBb[:, :r], "dB"), ws.data_ptr(), need,
+                         gpu_lib._stream(X.device))
+    assert st == gpu_lib.LORA_OK
+    torch.cuda.synchronize()
+    got = (to_host(dXb[:, :K]), to_host(dAb[:, :K]), to_host(dBb[:, :r]))
+    ref = oracle.bwd(t["X"], t["W"], t["A"], t["B"], t["dY"], c.scale)
+    _check("b_strided", got, ref)
+    assert (dXb[:, K:].float() == 7).all() and (dAb[:, K:].float() == 7).all()
+    assert (dBb[:, r:].float() == 7).all()
