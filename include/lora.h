@@ -223,7 +223,9 @@ int lora_merge_inplace(int dtype, int64_t N, int64_t K, int64_t r,
  *   workspace     device scratch of workspace_bytes >= lora_bwd_workspace_size,
  *                 256-byte aligned, owned by the caller; its content on entry
  *                 is ignored and on return is unspecified.  Calls in flight at
- *                 the same time need separate workspaces.
+ *                 the same time need separate workspaces.  It holds a
+ *                 transposed copy of W (N * K * 2 bytes), T and G, and fp32
+ *                 partial sums of dA and dB over token ranges.
  *   stream        hipStream_t as void*.
  * ldx, lda, ldda, lddy and ldw multiples of 8; X, W, A, dY, dA 16-byte
  * aligned.  Outputs and the workspace must not overlap any input or each

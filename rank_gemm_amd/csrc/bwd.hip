@@ -6,7 +6,7 @@
 // hand-written Triton kernels", section "BWD kernel speedup") is
 //   T  = X A^T   [M, r]           G  = dY B    [M, r]
 //   dX = dY W + s G A             the forward of dY with W' = W^T, A' = B^T,
-//                                 B' = A^T: the tiled kernel's NN form
+//                                 B' = A^T, on the tiled forward kernel
 //   dA = s G^T X  [r, K]          dB = s dY^T T  [N, r]
 // dA and dB contract over the tokens.  That page found a loop over the whole
 // sequence inside one program per output block starves the GPU, and moved dA
@@ -15,11 +15,15 @@
 // adds in a fixed order: every CU has work and the result is deterministic.
 //
 // Launches, in stream order, all through the caller's workspace:
-//   1. bt_kernel     B^T [r, N] bf16 (small)
+//   1. prep_kernel   W^T [K, N] (when dX is wanted), B^T [r, N], A^T [K, r]
 //   2. proj_kernel   T^T = A X^T and G^T = B^T dY^T, [r, Mp] bf16 each
 //   3. tc_kernel     dA and dB partial sums per token range, fp32
 //   4. red_kernel    dA, dB = round(s * ordered sum of the partials)
-//   5. dX: the tiled forward kernel in NN form on (dY, W, B^T, A)
+//   5. dX: the tiled forward kernel on (dY, W^T, B^T, A^T)
+// W^T is rewritten on every call (2 |W| bytes of traffic): the forward
+// kernel's contiguous-contraction operand reads run faster than reading W
+// as stored through transposing LDS reads, by more than the copy costs
+// (measured on X[4096,1024] W[1024,1024] and on X[8192,2560] W[4096,2560]).
 #include "common.h"
 #include "kernels.h"
 
@@ -43,14 +47,57 @@ __device__ __forceinline__ int tr_off(int row, int col) {
   return row * 128 + (((col >> 4) ^ tr_swz(row)) << 5) + ((col & 15) << 1);
 }
 
-// ---------------------------------------------------------------- B^T
-__global__ __launch_bounds__(256) void bt_kernel(int N, int r, const uint16_t* __restrict__ B,
-                                                 int64_t ldb, uint16_t* __restrict__ Bt,
-                                                 int64_t ldbt) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)r * N) return;
-  const int j = (int)(e / N), n = (int)(e % N);
-  Bt[(int64_t)j * ldbt + n] = B[(int64_t)n * ldb + j];
+// ---------------------------------------------------------------- transposes
+// Workgroups [0, wtiles): 64 x 64 tiles of W^T (16-B loads of W rows into
+// LDS, 16-B stores of W^T rows; N and K are multiples of 8, so a chunk is
+// either wholly inside or wholly outside).  The rest: B^T and A^T, one
+// element per thread.
+struct PrepArgs {
+  int N, K, r, wtiles_k, wtiles;
+  const uint16_t* W; int64_t ldw; uint16_t* Wt; int64_t ldwt;
+  const uint16_t* B; int64_t ldb; uint16_t* Bt; int64_t ldbt;
+  const uint16_t* A; int64_t lda; uint16_t* At; int64_t ldat;
+};
+
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-B rows
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (b < a.wtiles) {
+    const int n0 = (b / a.wtiles_k) * 64, k0 = (b % a.wtiles_k) * 64;
+#pragma unroll
+    for (int c = tid; c < 512; c += 256) {
+      const int row = c >> 3, ch = c & 7;
+      const int n = n0 + row, k = k0 + ch * 8;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (n < a.N && k < a.K) v = *reinterpret_cast<const u32x4*>(a.W + (int64_t)n * a.ldw + k);
+      *reinterpret_cast<u32x4*>(&tile[row][ch * 8]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = tid; c < 512; c += 256) {
+      const int row = c >> 3, ch = c & 7;  // row: k offset, ch: chunk of 8 n
+      const int k = k0 + row, n = n0 + ch * 8;
+      if (k >= a.K || n >= a.N) continue;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = uint32_t(tile[ch * 8 + 2 * q][row]) | (uint32_t(tile[ch * 8 + 2 * q + 1][row]) << 16);
+      *reinterpret_cast<u32x4*>(a.Wt + (int64_t)k * a.ldwt + n) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    return;
+  }
+  int64_t e = (int64_t)(b - a.wtiles) * 256 + tid;
+  const int64_t nb = (int64_t)a.r * a.N;
+  if (e < nb) {
+    const int j = (int)(e / a.N), n = (int)(e % a.N);
+    a.Bt[(int64_t)j * a.ldbt + n] = a.B[(int64_t)n * a.ldb + j];
+    return;
+  }
+  e -= nb;
+  if (e < (int64_t)a.K * a.r) {
+    const int k = (int)(e / a.r), j = (int)(e % a.r);
+    a.At[(int64_t)k * a.ldat + j] = a.A[(int64_t)j * a.lda + k];
+  }
 }
 
 // ---------------------------------------------------------------- projection
@@ -310,22 +357,36 @@ __global__ __launch_bounds__(Tc<RP>::NT) void tc_kernel(int M, int r, TcJob j0, 
 }
 
 // ---------------------------------------------------------------- reduce
+// Sum of S float4 partials p[0], p[stride], ... added in index order; the
+// loads are issued eight at a time so their latencies overlap.
+__device__ __forceinline__ f32x4 ordered_sum(const float* __restrict__ p, int64_t stride, int S) {
+  f32x4 s4 = zero4();
+  int sp = 0;
+  for (; sp + 8 <= S; sp += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(p + (sp + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s4 += v[u];
+  }
+  for (; sp < S; ++sp) s4 += *reinterpret_cast<const f32x4*>(p + sp * stride);
+  return s4;
+}
+
 // dA[j, k] = round(s * sum_split partA[split][j][k]) and
 // dB[n, j] = round(s * sum_split partB[split][n][j]), splits added in order.
 // One thread per 4 consecutive outputs of a row.
-__global__ __launch_bounds__(256) void red_kernel(int S, int r, int RP, int K, int N,
+__global__ __launch_bounds__(64) void red_kernel(int S, int r, int RP, int K, int N,
                                                   const float* __restrict__ pa,
                                                   const float* __restrict__ pb, float scale,
                                                   uint16_t* __restrict__ dA, int64_t ldda,
                                                   uint16_t* __restrict__ dB, int64_t lddb,
                                                   int64_t na) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t e = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (e < na) {
     const int k4 = K / 4;
     const int j = (int)(e / k4), k = (int)(e % k4) * 4;
-    f32x4 s4 = zero4();
-    for (int sp = 0; sp < S; ++sp)
-      s4 += *reinterpret_cast<const f32x4*>(pa + ((int64_t)sp * RP + j) * K + k);
+    const f32x4 s4 = ordered_sum(pa + (int64_t)j * K + k, (int64_t)RP * K, S);
     uint32_t* out = reinterpret_cast<uint32_t*>(dA + (int64_t)j * ldda + k);
     out[0] = pack_bf2(scale * s4[0], scale * s4[1]);
     out[1] = pack_bf2(scale * s4[2], scale * s4[3]);
@@ -335,9 +396,7 @@ __global__ __launch_bounds__(256) void red_kernel(int S, int r, int RP, int K, i
   const int r4 = (r + 3) / 4;
   if (f >= (int64_t)N * r4) return;
   const int n = (int)(f / r4), j = (int)(f % r4) * 4;
-  f32x4 s4 = zero4();
-  for (int sp = 0; sp < S; ++sp)
-    s4 += *reinterpret_cast<const f32x4*>(pb + ((int64_t)sp * N + n) * RP + j);
+  const f32x4 s4 = ordered_sum(pb + (int64_t)n * RP + j, (int64_t)N * RP, S);
   uint16_t* out = dB + (int64_t)n * lddb + j;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -401,7 +460,11 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t per = stages > 0 ? (stages + S - 1) / S : 1;  // stages per range
   p.tps = per * 64;
   p.S = M > 0 ? (int)((M + p.tps - 1) / p.tps) : 0;
+  p.ldwt = N;   // N % 8 == 0
+  p.ldat = r;
   int64_t off = 0;
+  p.off_wt = off; off = align256(off + K * N * 2);
+  p.off_at = off; off = align256(off + K * r * 2);
   p.off_bt = off; off = align256(off + r * p.ldbt * 2);
   p.off_tt = off; off = align256(off + r * p.ldp * 2);
   p.off_gt = off; off = align256(off + r * p.ldp * 2);
@@ -415,12 +478,23 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, void* workspace, hipStream_t s) {
   const BwdPlan p = bwd_plan(a.M, a.N, a.K, a.r);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const int N = (int)a.N, K = (int)a.K, r = (int)a.r;
+  const bool want_dx = a.dX != nullptr && a.M > 0 && a.K > 0;
+  uint16_t* Wt = reinterpret_cast<uint16_t*>(ws + p.off_wt);
+  uint16_t* At = reinterpret_cast<uint16_t*>(ws + p.off_at);
   uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
-  // 1. B^T (also the dX kernel's down-projection operand).
-  if ((int64_t)r * N > 0) {
-    hipLaunchKernelGGL(bt_kernel, dim3((unsigned)(((int64_t)r * N + 255) / 256)), dim3(256), 0, s,
-                       N, r, static_cast<const uint16_t*>(a.B), a.ldb, Bt, p.ldbt);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  // 1. W^T, B^T (the projection's and the dX kernel's operand) and A^T.
+  {
+    PrepArgs pa{N, K, r, (K + 63) / 64, 0, static_cast<const uint16_t*>(a.W), a.ldw, Wt, p.ldwt,
+                static_cast<const uint16_t*>(a.B), a.ldb, Bt, p.ldbt,
+                static_cast<const uint16_t*>(a.A), a.lda, At, p.ldat};
+    if (want_dx) pa.wtiles = ((N + 63) / 64) * pa.wtiles_k;
+    const int64_t small = (int64_t)r * N + (want_dx ? (int64_t)K * r : 0);
+    const int64_t grid = pa.wtiles + (small + 255) / 256;
+    if (!want_dx) pa.K = 0;  // no A^T either
+    if (grid > 0) {
+      hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(256), 0, s, pa);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
   }
   // 2-3. T, G and the partial sums (nothing to do without tokens).
   if (a.M > 0) {
@@ -439,7 +513,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, void* workspace, hipStream_t s) {
     const int64_t na = (int64_t)r * (K / 4);
     const int64_t total = na + (int64_t)N * ((r + 3) / 4);
     if (total > 0) {
-      hipLaunchKernelGGL(red_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p.S, r,
+      hipLaunchKernelGGL(red_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64), 0, s, p.S, r,
                          pad_rank(a.r), K, N, reinterpret_cast<const float*>(ws + p.off_pa),
                          reinterpret_cast<const float*>(ws + p.off_pb), a.scale,
                          static_cast<uint16_t*>(a.dA), a.ldda, static_cast<uint16_t*>(a.dB),
@@ -447,11 +521,12 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, void* workspace, hipStream_t s) {
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
   }
-  // 5. dX = dY W + s (dY B) A: the forward of dY in NN form.
-  if (a.dX != nullptr && a.M > 0 && a.K > 0) {
-    FwdArgs f{a.M, a.K, a.N, a.r, a.dY, a.lddy, a.W, a.ldw, Bt, p.ldbt, a.A, a.lda, a.scale,
+  // 5. dX = dY W + s (dY B) A: the forward of dY with W' = W^T, A' = B^T,
+  //    B' = A^T.
+  if (want_dx) {
+    FwdArgs f{a.M, a.K, a.N, a.r, a.dY, a.lddy, Wt, p.ldwt, Bt, p.ldbt, At, p.ldat, a.scale,
               a.dX, a.lddx};
-    return launch_fwd_tiled_bf16_nn(f, s);
+    return launch_fwd_tiled_bf16(f, s);
   }
   return hipSuccess;
 }

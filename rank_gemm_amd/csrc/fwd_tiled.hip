@@ -23,13 +23,6 @@
 //     T -> scale * T -> bf16 -> LDS; B[BN x RP] -> LDS (zero padded)
 //     acc += (s T) B^T               (MFMA over the rank)
 //     acc -> bf16 -> LDS -> coalesced 16-B stores of Y.
-//
-// The same kernel in "NN" form takes W as [K, N] (contraction-major, i.e. the
-// transpose of the nn.Linear layout) and the up-projection as [r, N]: the W
-// stage is then BK rows of BN output columns, read into MFMA operands with
-// transposing LDS reads.  The layer's input gradient is this form:
-// dX = dY W + s (dY B) A is the forward of dY with W' = W^T, A' = B^T,
-// B' = A^T, and W, A are used as stored.
 #include <type_traits>
 
 #include "common.h"
@@ -55,16 +48,6 @@ __device__ __forceinline__ int stage_off(int row, int chunk) {
   return row * (BK * 2) + ((chunk ^ swz<BK>(row)) << 4);
 }
 
-// NN-form W stage: row k holds BN output columns (BN * 2 bytes, BN >= 128).
-// 32-B segments (16 columns) are XOR-swizzled with a function of row & 15 so
-// that one transposing read (rows 8g + 0..3 at one segment for lane groups
-// g = 0..3, see common.h) touches 8 distinct 32-B bank windows per half wave.
-__device__ __forceinline__ int nn_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-template <int BN>
-__device__ __forceinline__ int nn_off(int row, int col) {
-  return row * (BN * 2) + (((col >> 4) ^ nn_swz(row)) << 5) + ((col & 15) << 1);
-}
-
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_>
@@ -88,10 +71,6 @@ struct Cfg {
   // Loads per stage: waves below kAN % NW issue one A load more than the rest.
   static constexpr int kLoadsLo = kXL + kWL + kAN / NW;
   static constexpr int kLoadsHi = kLoadsLo + (kAN % NW != 0 ? 1 : 0);
-  // NN form: W stage rows per 1-KiB load, and whether the swizzle of a lane's
-  // row is the same for all of its load slots (slot stride a multiple of 16 rows).
-  static constexpr int kNRpl = 512 / BN;
-  static constexpr bool kNNOk = BN >= 128 && (NW * kNRpl) % 16 == 0;
   static constexpr int kTS = RP + 8;                // epilogue T / B row stride (elements)
   static constexpr int kEpiB = (BM + BN) * kTS * 2;
   static constexpr int kYS = BN + 8;                // output staging row stride (elements)
@@ -170,23 +149,6 @@ __device__ __forceinline__ constexpr int t_frag(int sl) {
   return 0;
 }
 
-// W operand of output column block col0 (16 columns) at logical chunk cc
-// (k = 8 cc .. 8 cc + 7 of the stage).  Row-major W: one 16-B read of row
-// col0 + lane % 16.  NN form: two transposing reads of rows 8 cc + 0..3 and
-// 8 cc + 4..7, lane i of each 16-lane group addressing row + i / 4, column
-// col0 + 4 (i % 4).
-template <class C, bool NN>
-__device__ __forceinline__ u32x4 w_frag(const unsigned char* ws, int col0, int cc, int lrow) {
-  if constexpr (!NN) {
-    return *reinterpret_cast<const u32x4*>(ws + stage_off<C::BK>(col0 + lrow, cc));
-  } else {
-    const int row = 8 * cc + (lrow >> 2), col = col0 + 4 * (lrow & 3);
-    const u32x2 lo = lds_read_tr16(ws + nn_off<C::BN>(row, col));
-    const u32x2 hi = lds_read_tr16(ws + nn_off<C::BN>(row + 4, col));
-    return u32x4{lo.x, lo.y, hi.x, hi.y};
-  }
-}
-
 template <class C>
 __device__ __forceinline__ void t_update_ab(const u32x4 (&a)[C::TM], const u32x4 (&t)[C::kTF],
                                             f32x4 (&tacc)[C::kTSlots]) {
@@ -217,19 +179,12 @@ __device__ __forceinline__ void wait_stages(int wave) {
 // slots and (waves below kAN) its A slot.  Slot s of a matrix is the wave's
 // slot 0 plus s * NW 1-KiB loads, i.e. a wave-uniform byte stride.  Lanes
 // whose 16-B chunk lies past K read zeros.
-// NN form: the W rows of a stage are k0 .. k0 + BK - 1 of the [K, N] matrix;
-// the resource is rebased at row k0 (wnn points at column n0 of row 0) and
-// ends at the last valid element (column N - 1 of the stage's last row below
-// K): rows past K read zeros, and no read leaves the matrix.  Columns past N
-// on earlier rows read the next row's values; they only reach output columns
-// that are never stored.
-template <class C, bool WT = true, bool NN = false>
+template <class C, bool WT = true>
 __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0, int K, int wave,
                                             int lchunk, __amdgpu_buffer_rsrc_t rx,
                                             __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
                                             uint32_t vx, uint32_t vw, uint32_t va, uint32_t sx,
-                                            uint32_t sw, uint32_t sa, const uint16_t* wnn,
-                                            int64_t ldw, int ncols) {
+                                            uint32_t sw, uint32_t sa) {
   const bool kin = k0 + lchunk * 8 < K;
   const uint32_t kb = (uint32_t)k0 * 2;
   unsigned char* base = smem + buf * C::kStageB;
@@ -238,23 +193,11 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
   for (int s = 0; s < C::kXL; ++s)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(base + (wave + s * C::NW) * 1024), 16,
                                              off_or_oob(kin, vx + sgpr(s * sx + kb)), 0, 0, 0);
-  if constexpr (NN) {
-    const int rows = min(C::BK, K - k0);
-    const __amdgpu_buffer_rsrc_t rwk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(wnn + (int64_t)k0 * ldw), 0, rows > 0 ? (int)(((rows - 1) * ldw + ncols) * 2) : 0,
-        0x00020000);
 #pragma unroll
-    for (int s = 0; s < C::kWL; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rwk, (lds_void*)(base + C::BM * kRowB + (wave + s * C::NW) * 1024), 16,
-          vw + sgpr(s * sw), 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int s = 0; s < C::kWL; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, (lds_void*)(base + C::BM * kRowB + (wave + s * C::NW) * 1024), 16,
-          off_or_oob(kin, vw + sgpr(s * sw + kb)), 0, 0, 0);
-  }
+  for (int s = 0; s < C::kWL; ++s)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rw, (lds_void*)(base + C::BM * kRowB + (wave + s * C::NW) * 1024), 16,
+        off_or_oob(kin, vw + sgpr(s * sw + kb)), 0, 0, 0);
   if constexpr (!WT) return;  // T already known: no A rows
 #pragma unroll
   for (int s = 0; s < C::kAL; ++s)
@@ -270,7 +213,7 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
 // the K loop without A loads or T MFMAs and reuse it.  For large ranks this
 // removes the per-tile recomputation of T (2 M K r flop per N tile, as much
 // as the base contraction when r = BN).  tiles_n then counts groups of G.
-template <class C, int G, bool NN>
+template <class C, int G>
 __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
@@ -336,21 +279,10 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int lrow_in_load = lane / C::kChunks;
   const int lchunk = (lane % C::kChunks) ^ swz<BK>(lrow_in_load);
   const uint32_t vx = (uint32_t)((wave * kRPL + lrow_in_load) * ldx * 2 + lchunk * 16);
-  uint32_t vw = (uint32_t)((wave * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
-  uint32_t sw = (uint32_t)(NW * kRPL * ldw * 2);
-  if constexpr (NN) {
-    // Lane i of a 1-KiB W load writes stage row wave * kNRpl + i / (BN / 8)
-    // (plus the slot's multiple of 16 rows), physical 16-B chunk i % (BN / 8),
-    // so it fetches the logical chunk that the row's segment swizzle puts there.
-    static_assert(C::kNNOk, "NN form needs BN >= 128 and 16-row load slots");
-    constexpr int kCpr = BN / 8;
-    const int row = wave * C::kNRpl + lane / kCpr, pch = lane % kCpr;
-    const int lc = 2 * ((pch >> 1) ^ nn_swz(row)) + (pch & 1);
-    vw = (uint32_t)(row * ldw * 2 + lc * 16);
-    sw = (uint32_t)(NW * C::kNRpl * ldw * 2);
-  }
+  const uint32_t vw = (uint32_t)((wave * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
   const uint32_t va = (uint32_t)((wave * kRPL + lrow_in_load) * lda * 2 + lchunk * 16);
   const uint32_t sx = (uint32_t)(NW * kRPL * ldx * 2);  // byte stride between a wave's slots
+  const uint32_t sw = (uint32_t)(NW * kRPL * ldw * 2);
   const uint32_t sa = (uint32_t)(NW * kRPL * lda * 2);
 
   const int rot = ring_rot<C>(wn);
@@ -364,9 +296,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   if (n0 >= N) break;  // uniform: the group's last tiles may lie past N
   const int wrows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (NN ? (int64_t)n0 : (int64_t)n0 * ldw)), 0, NN ? 0 : (int)(wrows * ldw * 2),
-      0x00020000);
-  const uint16_t* wnn = W + n0;  // NN form: column n0 of row 0
+      (void*)(W + (int64_t)n0 * ldw), 0, (int)(wrows * ldw * 2), 0x00020000);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -390,11 +320,10 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int nk = (K + BK - 1) / BK;
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
-    issue_stage<C, WT, NN>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa,
-                           wnn, ldw, N - n0);
+    issue_stage<C, WT>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
 
   const int xrow0 = wm * TM * 16 + lrow;  // + 16 * ring_row_block(k) for ring slot k
-  const int wcol0 = wn * TN * 16;  // first output column of the wave
+  const int wrow0 = wn * TN * 16 + lrow;
   Frags<C> cur;
   wait_stages<C, STAGES - 1, WT>(wave);
   __builtin_amdgcn_s_barrier();
@@ -407,7 +336,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       cur.a[i] = *reinterpret_cast<const u32x4*>(
           xs + stage_off<BK>(xrow0 + ring_row_block<C>(i, rot) * 16, lk));
 #pragma unroll
-    for (int j = 0; j < TN; ++j) cur.b[j] = w_frag<C, NN>(ws, wcol0 + j * 16, lk, lrow);
+    for (int j = 0; j < TN; ++j)
+      cur.b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, lk));
     if constexpr (WT) {
 #pragma unroll
       for (int u = 0; u < C::kTF; ++u)
@@ -430,8 +360,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       wait_stages<C, STAGES - 2, WT>(wave);
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      issue_stage<C, WT, NN>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw,
-                             va, sx, sw, sa, wnn, ldw, N - n0);
+      issue_stage<C, WT>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx,
+                     sw, sa);
     }
     const unsigned char* xs = smem + (sync ? nslot : rslot) * C::kStageB;
     const unsigned char* ws = xs + BM * kRowB;
@@ -439,7 +369,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     const int cc = (sync ? 0 : (u + 1) * 4) + lk;  // logical 16-B chunk of the next substep
     // After the final substep the reads fetch a zero stage (never used).
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bx[j] = w_frag<C, NN>(ws, wcol0 + j * 16, cc, lrow);
+    for (int j = 0; j < TN; ++j)
+      bx[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, cc));
     if constexpr (WT) {
 #pragma unroll
       for (int f = 0; f < C::kTF; ++f)
@@ -517,10 +448,9 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
   }
   for (int e = tid; e < BN * RP; e += C::NT) {
-    // NN form: the up-projection is stored [r, N]; walk it row by row.
-    const int n = NN ? e % BN : e / RP, j = NN ? e / BN : e % RP;
+    const int n = e / RP, j = e % RP;
     uint16_t v = 0;
-    if (j < r && n0 + n < N) v = NN ? B[(int64_t)j * ldb + n0 + n] : B[(int64_t)(n0 + n) * ldb + j];
+    if (j < r && n0 + n < N) v = B[(int64_t)(n0 + n) * ldb + j];
     bs[n * C::kTS + j] = v;
   }
   __syncthreads();
@@ -588,7 +518,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }  // tiles of the group
 }
 
-template <class C, int G = 1, bool NN = false>
+template <class C, int G = 1>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
   const int tiles_n = (int)((a.N + C::BN * G - 1) / (C::BN * G));  // groups of G N tiles
@@ -607,7 +537,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
     if (ok1 && (!ok2 || f1 <= f2)) map_mode = 1;
     else if (ok2) map_mode = 2;
   }
-  auto kern = fwd_tiled_bf16_kernel<C, G, NN>;
+  auto kern = fwd_tiled_bf16_kernel<C, G>;
   constexpr int lds = G > 1 ? C::kLdsG : C::kLds;
   static_assert(lds <= 160 * 1024, "LDS budget");
   static std::atomic<uint64_t> attr_done{0};
@@ -635,25 +565,23 @@ using Tall = Cfg<64, 32, 4, 1, RP, 8, 64>;
 template <int RP>
 using Mid = Cfg<128, 128, 4, 2, RP, 2, 64>;
 
-template <int RP, bool NN = false>
+template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
-  if constexpr (RP <= 32 && !NN) {
+  if constexpr (RP <= 32) {
     if (a.M <= 64) return launch<Tall<RP>>(a, s);
   }
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  // (NN form: the two transposing W reads per fragment push the rank-64
-  // 256 x 256 tile past the register file, so it stops at rank 32.)
-  if constexpr (RP <= (NN ? 32 : 64)) {
-    if (big_tiles >= 256) return launch<Big<RP>, 1, NN>(a, s);
+  if constexpr (RP <= 64) {
+    if (big_tiles >= 256) return launch<Big<RP>>(a, s);
   }
   if constexpr (RP == 128) {
     // Rank 128 on 128 x 128 tiles: compute T once per 4 N tiles, when that
     // still leaves a few workgroups per CU.  (Rank 256 does not fit the LDS
     // budget with T kept; rank <= 64 takes 256 x 256 tiles at this size.)
     const int64_t mid_tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    if (a.N > 3 * 128 && mid_tiles >= 4 * 256) return launch<Mid<RP>, 4, NN>(a, s);
+    if (a.N > 3 * 128 && mid_tiles >= 4 * 256) return launch<Mid<RP>, 4>(a, s);
   }
-  return launch<Mid<RP>, 1, NN>(a, s);
+  return launch<Mid<RP>>(a, s);
 }
 
 }  // namespace
@@ -665,16 +593,6 @@ hipError_t launch_fwd_tiled_bf16(const FwdArgs& a, hipStream_t s) {
     case 64: return launch_rp<64>(a, s);
     case 128: return launch_rp<128>(a, s);
     default: return launch_rp<256>(a, s);
-  }
-}
-
-hipError_t launch_fwd_tiled_bf16_nn(const FwdArgs& a, hipStream_t s) {
-  switch (pad_rank(a.r)) {
-    case 16: return launch_rp<16, true>(a, s);
-    case 32: return launch_rp<32, true>(a, s);
-    case 64: return launch_rp<64, true>(a, s);
-    case 128: return launch_rp<128, true>(a, s);
-    default: return launch_rp<256, true>(a, s);
   }
 }
 

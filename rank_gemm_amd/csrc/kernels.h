@@ -58,12 +58,13 @@ struct BwdArgs {
 };
 
 // Workspace layout of the backward (byte offsets from a 256-B aligned base):
-// B^T [r, ldbt] bf16, T^T and G^T [r, ldp] bf16, the fp32 partial sums of dA
-// [S][RP][K] and of dB [S][N][RP] over S token ranges of tps tokens.
+// W^T [K, ldwt], A^T [K, ldat], B^T [r, ldbt], T^T and G^T [r, ldp], all
+// bf16, and the fp32 partial sums of dA [S][RP][K] and of dB [S][N][RP] over
+// S token ranges of tps tokens.
 struct BwdPlan {
   int S;
-  int64_t tps, ldbt, ldp;
-  int64_t off_bt, off_tt, off_gt, off_pa, off_pb, bytes;
+  int64_t tps, ldwt, ldat, ldbt, ldp;
+  int64_t off_wt, off_at, off_bt, off_tt, off_gt, off_pa, off_pb, bytes;
 };
 
 // Rank padded to the MFMA-friendly size the kernels are instantiated for.
@@ -72,9 +73,6 @@ inline int pad_rank(int64_t r) {
 }
 
 hipError_t launch_fwd_tiled_bf16(const FwdArgs& a, hipStream_t s);
-// NN form: a.W is [K, N] (ldw >= N) and a.B is [r, N] (ldb >= N); otherwise
-// as launch_fwd_tiled_bf16.  Requires N % 8 == 0 in addition.
-hipError_t launch_fwd_tiled_bf16_nn(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_tiled_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge_bf16(const MergeArgs& a, hipStream_t s);
