@@ -16,10 +16,12 @@
 //
 // Launches, in stream order, all through the caller's workspace:
 //   1. prep_kernel   W^T [K, N] (when dX is wanted), B^T [r, N], A^T [K, r]
-//   2. proj_kernel   T^T = A X^T and G^T = B^T dY^T, [r, Mp] bf16 each
-//   3. tc_kernel     dA and dB partial sums per token range, fp32
-//   4. red_kernel    dA, dB = round(s * ordered sum of the partials)
-//   5. dX: the tiled forward kernel on (dY, W^T, B^T, A^T)
+//   2. dX: the tiled forward kernel on (dY, W^T, B^T, A^T); its rank
+//      intermediate is s dY B = s G, which it also stores as (s G)^T
+//   3. proj_kernel   (s T)^T = s A X^T, [r, Mp] bf16 (and (s G)^T when dX is
+//                    not computed)
+//   4. tc_kernel     dA and dB partial sums per token range, fp32
+//   5. red_kernel    dA, dB = round(ordered sum of the partials)
 // W^T is rewritten on every call (2 |W| bytes of traffic): the forward
 // kernel's contiguous-contraction operand reads run faster than reading W
 // as stored through transposing LDS reads, by more than the copy costs
@@ -101,8 +103,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------- projection
-// P^T[j, m] = sum_c U[j, c] Z[m, c] for a tile of BT tokens, both operands
-// contraction-contiguous.  Job 0: Z = X, U = A (T); job 1: Z = dY, U = B^T (G).
+// P^T[j, m] = round(scale * sum_c Z[m, c] U[j, c]) for a tile of BT tokens,
+// both operands contraction-contiguous.  Job 0: Z = X, U = A (s T); job 1:
+// Z = dY, U = B^T (s G, when the input gradient is not computed; otherwise the
+// dX kernel provides it).  Each wave owns 16 tokens and runs the contraction in
+// order, 32 at a time, with the operands in the same MFMA roles as the tiled
+// forward kernel's down-projection: both produce bitwise the same s G.
 struct ProjJob {
   const uint16_t* Z;
   int64_t ldz;
@@ -114,16 +120,15 @@ struct ProjJob {
 
 template <int RP>
 struct Prj {
-  static constexpr int BT = 32, NW = 4, NT = NW * kWave, RB = RP / 16;
+  static constexpr int BT = 64, NW = 4, NT = NW * kWave, RB = RP / 16;
   static constexpr int kRows = BT + RP;          // staged rows per stage: tokens, then ranks
   static constexpr int kStageB = kRows * 128;    // 64 contraction values per row
-  static constexpr int kLoads = kRows / 8;       // 1-KiB loads per stage; the first 4 are Z
+  static constexpr int kLoads = kRows / 8;       // 1-KiB loads per stage; the first 8 are Z
   static constexpr int kUL = (RP / 8 + NW - 1) / NW;  // U load slots per wave
   static constexpr int kLo = kLoads / NW, kHi = kLo + (kLoads % NW != 0 ? 1 : 0);
-  static constexpr int STAGES = clampi(96 * 1024 / kStageB, 2, 8);
-  static constexpr int kRedB = 2 * RB * kWave * 16;
-  static constexpr int kLds = cmaxi(STAGES * kStageB, kRedB);
-  static_assert(BT == 32 && NW == 4, "one Z load per wave per stage");
+  static constexpr int STAGES = clampi(64 * 1024 / kStageB, 2, 6);
+  static constexpr int kLds = STAGES * kStageB;
+  static_assert(BT == 16 * NW && BT % 8 == 0, "one 16-token block per wave, 8-row loads");
   static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
@@ -141,8 +146,8 @@ __device__ __forceinline__ void wait_own(int wave) {
 }
 
 template <int RP>
-__global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, ProjJob j0, ProjJob j1,
-                                                           int64_t ldp) {
+__global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, float scale, ProjJob j0,
+                                                           ProjJob j1, int64_t ldp) {
   using P = Prj<RP>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const ProjJob jb = blockIdx.y == 0 ? j0 : j1;
@@ -159,9 +164,11 @@ __global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, ProjJob
   const __amdgpu_buffer_rsrc_t ru =
       __builtin_amdgcn_make_buffer_rsrc((void*)jb.U, 0, (int)(r * jb.ldu * 2), 0x00020000);
   // Lane i of a 1-KiB load writes row 8q + i / 8, physical chunk i % 8.
+  // Wave w issues Z loads q = w and w + 4 and U loads 8 + w + 4 s.
   const int lrl = lane >> 3;
   const int lch = (lane & 7) ^ lrl;
   const uint32_t vz = (uint32_t)((8 * wave + lrl) * jb.ldz * 2 + lch * 16);
+  const uint32_t sz = (uint32_t)(8 * P::NW * jb.ldz * 2);
   const uint32_t vu = (uint32_t)((8 * wave + lrl) * jb.ldu * 2 + lch * 16);
   const uint32_t su = (uint32_t)(8 * P::NW * jb.ldu * 2);
 
@@ -170,20 +177,21 @@ __global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, ProjJob
     const int c0 = st * 64;
     const bool kin = c0 + lch * 8 < C;
     const uint32_t cb = (uint32_t)c0 * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(base + wave * 1024), 16,
-                                             off_or_oob(kin, vz + sgpr(cb)), 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(base + (wave + s * P::NW) * 1024),
+                                               16, off_or_oob(kin, vz + sgpr(s * sz + cb)), 0, 0,
+                                               0);
 #pragma unroll
     for (int s = 0; s < P::kUL; ++s) {
-      const int p = wave + s * P::NW;  // U load index (stage load 4 + p)
+      const int p = wave + s * P::NW;  // U load index (stage load 8 + p)
       if (p < RP / 8)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ru, (lds_void*)(base + (4 + p) * 1024), 16, off_or_oob(kin, vu + sgpr(s * su + cb)),
+            ru, (lds_void*)(base + (8 + p) * 1024), 16, off_or_oob(kin, vu + sgpr(s * su + cb)),
             0, 0, 0);
     }
   };
 
-  // Wave w: token block w & 1, k32 half w >> 1 of every stage.
-  const int tb = wave & 1, half = wave >> 1;
   f32x4 acc[P::RB];
 #pragma unroll
   for (int i = 0; i < P::RB; ++i) acc[i] = zero4();
@@ -197,34 +205,30 @@ __global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, ProjJob
     __builtin_amdgcn_s_barrier();
     issue(kt + P::STAGES - 1);
     const unsigned char* sb = smem + (kt % P::STAGES) * P::kStageB;
-    const int ch = 4 * half + lk;
-    const u32x4 z = *reinterpret_cast<const u32x4*>(sb + row_off(16 * tb + lrow, ch));
 #pragma unroll
-    for (int i = 0; i < P::RB; ++i) {
-      const u32x4 u = *reinterpret_cast<const u32x4*>(sb + row_off(P::BT + 16 * i + lrow, ch));
-      acc[i] = mfma16x16x32(u, z, acc[i]);
+    for (int u = 0; u < 2; ++u) {
+      const u32x4 z = *reinterpret_cast<const u32x4*>(sb + row_off(16 * wave + lrow, 4 * u + lk));
+#pragma unroll
+      for (int i = 0; i < P::RB; ++i) {
+        const u32x4 w =
+            *reinterpret_cast<const u32x4*>(sb + row_off(P::BT + 16 * i + lrow, 4 * u + lk));
+        acc[i] = mfma16x16x32(z, w, acc[i]);
+      }
     }
   }
   // Loads of the stages past the end (zeros) may still be landing in the ring.
   wait_vmcnt<0>();
-  wait_lgkm0();
-  __syncthreads();
-  f32x4* red = reinterpret_cast<f32x4*>(smem);
-  if (half == 1) {
+
+  // acc[i] lane: rank 16 i + lrow, tokens m0 + 16 w + 4 lk + 0..3 (< ldp: the
+  // grid covers ldp / BT tiles).
+  const int64_t m = m0 + 16 * wave + 4 * lk;
 #pragma unroll
-    for (int i = 0; i < P::RB; ++i) red[(tb * P::RB + i) * kWave + lane] = acc[i];
-  }
-  __syncthreads();
-  if (half == 0) {
-    const int64_t m = m0 + 16 * tb + lrow;  // < ldp: the grid covers ldp / BT tiles
-#pragma unroll
-    for (int i = 0; i < P::RB; ++i) {
-      const f32x4 o = red[(tb * P::RB + i) * kWave + lane];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = 16 * i + 4 * lk + q;
-        if (j < r) jb.Pt[(int64_t)j * ldp + m] = f2bf(acc[i][q] + o[q]);
-      }
+  for (int i = 0; i < P::RB; ++i) {
+    const int j = 16 * i + lrow;
+    if (j < r) {
+      uint32_t* o = reinterpret_cast<uint32_t*>(jb.Pt + (int64_t)j * ldp + m);
+      o[0] = pack_bf2(scale * acc[i][0], scale * acc[i][1]);
+      o[1] = pack_bf2(scale * acc[i][2], scale * acc[i][3]);
     }
   }
 }
@@ -373,12 +377,12 @@ __device__ __forceinline__ f32x4 ordered_sum(const float* __restrict__ p, int64_
   return s4;
 }
 
-// dA[j, k] = round(s * sum_split partA[split][j][k]) and
-// dB[n, j] = round(s * sum_split partB[split][n][j]), splits added in order.
-// One thread per 4 consecutive outputs of a row.
+// dA[j, k] = round(sum_split partA[split][j][k]) and
+// dB[n, j] = round(sum_split partB[split][n][j]), splits added in order (the
+// scale is already in s G and s T).  One thread per 4 consecutive outputs.
 __global__ __launch_bounds__(64) void red_kernel(int S, int r, int RP, int K, int N,
                                                   const float* __restrict__ pa,
-                                                  const float* __restrict__ pb, float scale,
+                                                  const float* __restrict__ pb,
                                                   uint16_t* __restrict__ dA, int64_t ldda,
                                                   uint16_t* __restrict__ dB, int64_t lddb,
                                                   int64_t na) {
@@ -388,8 +392,8 @@ __global__ __launch_bounds__(64) void red_kernel(int S, int r, int RP, int K, in
     const int j = (int)(e / k4), k = (int)(e % k4) * 4;
     const f32x4 s4 = ordered_sum(pa + (int64_t)j * K + k, (int64_t)RP * K, S);
     uint32_t* out = reinterpret_cast<uint32_t*>(dA + (int64_t)j * ldda + k);
-    out[0] = pack_bf2(scale * s4[0], scale * s4[1]);
-    out[1] = pack_bf2(scale * s4[2], scale * s4[3]);
+    out[0] = pack_bf2(s4[0], s4[1]);
+    out[1] = pack_bf2(s4[2], s4[3]);
     return;
   }
   const int64_t f = e - na;
@@ -400,11 +404,13 @@ __global__ __launch_bounds__(64) void red_kernel(int S, int r, int RP, int K, in
   uint16_t* out = dB + (int64_t)n * lddb + j;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (j + q < r) out[q] = f2bf(scale * s4[q]);
+    if (j + q < r) out[q] = f2bf(s4[q]);
 }
 
+// with_g: the projection also computes s G (the dX kernel did not).
 template <int RP>
-hipError_t launch_proj_tc(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, hipStream_t s) {
+hipError_t launch_proj_tc(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, bool with_g,
+                          hipStream_t s) {
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, r = (int)a.r;
   const uint16_t* Bt = reinterpret_cast<const uint16_t*>(ws + p.off_bt);
   uint16_t* Tt = reinterpret_cast<uint16_t*>(ws + p.off_tt);
@@ -416,8 +422,8 @@ hipError_t launch_proj_tc(const BwdArgs& a, const BwdPlan& p, unsigned char* ws,
     auto kern = proj_kernel<RP>;
     static std::atomic<uint64_t> done{0};
     if (hipError_t e = ensure_lds(kern, Prj<RP>::kLds, done); e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(p.ldp / Prj<RP>::BT), 2), dim3(Prj<RP>::NT),
-                       Prj<RP>::kLds, s, M, r, jt, jg, p.ldp);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(p.ldp / Prj<RP>::BT), with_g ? 2 : 1),
+                       dim3(Prj<RP>::NT), Prj<RP>::kLds, s, M, r, a.scale, jt, jg, p.ldp);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   {
@@ -496,37 +502,37 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, void* workspace, hipStream_t s) {
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
   }
-  // 2-3. T, G and the partial sums (nothing to do without tokens).
+  // 2. dX = dY W + s (dY B) A: the forward of dY with W' = W^T, A' = B^T,
+  //    B' = A^T; its rank intermediate s dY B = s G goes to the workspace.
+  if (want_dx) {
+    FwdArgs f{a.M, a.K, a.N, a.r, a.dY, a.lddy, Wt, p.ldwt, Bt, p.ldbt, At, p.ldat, a.scale,
+              a.dX, a.lddx, ws + p.off_gt, p.ldp};
+    if (hipError_t e = launch_fwd_tiled_bf16(f, s); e != hipSuccess) return e;
+  }
+  // 3-4. s T (and s G), then the partial sums (nothing to do without tokens).
   if (a.M > 0) {
     hipError_t e;
     switch (pad_rank(a.r)) {
-      case 16: e = launch_proj_tc<16>(a, p, ws, s); break;
-      case 32: e = launch_proj_tc<32>(a, p, ws, s); break;
-      case 64: e = launch_proj_tc<64>(a, p, ws, s); break;
-      case 128: e = launch_proj_tc<128>(a, p, ws, s); break;
-      default: e = launch_proj_tc<256>(a, p, ws, s); break;
+      case 16: e = launch_proj_tc<16>(a, p, ws, !want_dx, s); break;
+      case 32: e = launch_proj_tc<32>(a, p, ws, !want_dx, s); break;
+      case 64: e = launch_proj_tc<64>(a, p, ws, !want_dx, s); break;
+      case 128: e = launch_proj_tc<128>(a, p, ws, !want_dx, s); break;
+      default: e = launch_proj_tc<256>(a, p, ws, !want_dx, s); break;
     }
     if (e != hipSuccess) return e;
   }
-  // 4. dA, dB (zeros when there are no tokens).
+  // 5. dA, dB (zeros when there are no tokens).
   {
     const int64_t na = (int64_t)r * (K / 4);
     const int64_t total = na + (int64_t)N * ((r + 3) / 4);
     if (total > 0) {
       hipLaunchKernelGGL(red_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64), 0, s, p.S, r,
                          pad_rank(a.r), K, N, reinterpret_cast<const float*>(ws + p.off_pa),
-                         reinterpret_cast<const float*>(ws + p.off_pb), a.scale,
+                         reinterpret_cast<const float*>(ws + p.off_pb),
                          static_cast<uint16_t*>(a.dA), a.ldda, static_cast<uint16_t*>(a.dB),
                          a.lddb, na);
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
-  }
-  // 5. dX = dY W + s (dY B) A: the forward of dY with W' = W^T, A' = B^T,
-  //    B' = A^T.
-  if (want_dx) {
-    FwdArgs f{a.M, a.K, a.N, a.r, a.dY, a.lddy, Wt, p.ldwt, Bt, p.ldbt, At, p.ldat, a.scale,
-              a.dX, a.lddx};
-    return launch_fwd_tiled_bf16(f, s);
   }
   return hipSuccess;
 }

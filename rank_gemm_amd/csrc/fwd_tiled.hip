@@ -218,7 +218,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
-    int64_t ldy, int tiles_m, int tiles_n, int y_vec, int map_mode) {
+    int64_t ldy, int tiles_m, int tiles_n, int y_vec, int map_mode, uint16_t* __restrict__ tout,
+    int64_t ldt) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int BM = C::BM, BN = C::BN, RP = C::RP, TM = C::TM, TN = C::TN;
   constexpr int WN = C::WN, NW = C::NW, STAGES = C::STAGES;
@@ -455,6 +456,17 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
   __syncthreads();
 
+  // Optional side output: the scaled down-projection s T of this M tile, as
+  // the epilogue rounded it, stored transposed ([r, ldt], tokens contiguous)
+  // by the workgroup of the first N tile.  Rows past M hold zeros (X rows
+  // past M read as zeros).  The backward takes s dY B from here.
+  if (tout != nullptr && ng0 == 0 && g == 0) {
+    for (int e = tid; e < BM * r; e += C::NT) {
+      const int row = e % BM, j = e / BM;
+      if (m0 + row < ldt) tout[(int64_t)j * ldt + m0 + row] = ts[row * C::kTS + j];
+    }
+  }
+
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank.
   if constexpr (RP >= 32) {
 #pragma unroll
@@ -546,7 +558,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
                      (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.X), a.ldx,
                      static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
                      a.lda, static_cast<const uint16_t*>(a.B), a.ldb, a.scale,
-                     static_cast<uint16_t*>(a.Y), a.ldy, tiles_m, tiles_n, y_vec, map_mode);
+                     static_cast<uint16_t*>(a.Y), a.ldy, tiles_m, tiles_n, y_vec, map_mode,
+                     static_cast<uint16_t*>(a.tout), a.ldt);
   return hipGetLastError();
 }
 

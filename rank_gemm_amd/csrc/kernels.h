@@ -33,6 +33,10 @@ struct FwdArgs {
   const void* B; int64_t ldb;
   float scale;
   void* Y; int64_t ldy;
+  // Optional (tiled bf16 kernel only): when non-null, s T = s X A^T as
+  // rounded to bf16 is also written transposed, tout[j * ldt + m] for j < r
+  // and m < ldt (ldt >= M; rows past M are zeros).
+  void* tout = nullptr; int64_t ldt = 0;
 };
 
 struct MergeArgs {
