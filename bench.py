@@ -212,7 +212,7 @@ def bwd_flops(c):
 
 
 def run_bwd_case(rg, c, steps, warmup):
-    """One backward workload (lora_bwd: five launches), timed as a HIP graph
+    """One backward workload (lora_bwd: four launches), timed as a HIP graph
     of `steps` back-to-back backward passes and eagerly."""
     import torch
     import synth
@@ -237,7 +237,7 @@ def run_bwd_case(rg, c, steps, warmup):
     f = bwd_flops(c)
     return {
         "workload": "bwd_" + c.name,
-        "timing": "hip graph of back-to-back backward passes (5 launches each)",
+        "timing": "hip graph of back-to-back backward passes (4 launches each)",
         "pass_us_mean": round(ms * 1e3, 3),
         "eager_us_per_call": round(eager_ms * 1e3, 3),
         "tflops": round(f / (ms * 1e-3) / 1e12, 2),

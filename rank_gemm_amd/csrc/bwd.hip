@@ -14,14 +14,19 @@
 // token ranges, each range writing fp32 partial sums that a second kernel
 // adds in a fixed order: every CU has work and the result is deterministic.
 //
-// Launches, in stream order, all through the caller's workspace:
-//   1. prep_kernel   W^T [K, N] (when dX is wanted), B^T [r, N], A^T [K, r]
+// Launches, in stream order, all through the caller's workspace.  With dX:
+//   1. proj_kernel   (s T)^T = s A X^T, [r, Mp] bf16, and in the same grid
+//                    the preparation: W^T [K, N], B^T [r, N], A^T [K, r]
 //   2. dX: the tiled forward kernel on (dY, W^T, B^T, A^T); its rank
 //      intermediate is s dY B = s G, which it also stores as (s G)^T
-//   3. proj_kernel   (s T)^T = s A X^T, [r, Mp] bf16 (and (s G)^T when dX is
-//                    not computed)
-//   4. tc_kernel     dA and dB partial sums per token range, fp32
-//   5. red_kernel    dA, dB = round(ordered sum of the partials)
+//   3. tc_kernel     dA and dB partial sums per token range, fp32
+//   4. red_kernel    dA, dB = round(ordered sum of the partials)
+// Without dX: prep_kernel (B^T), proj_kernel (s T and s G), tc_kernel,
+// red_kernel.  With no tokens, red_kernel alone writes dA = 0 and dB = 0.
+// (Folding the reduction into the token contraction, the last workgroup of
+// a column tile adding the others' partials, needs an agent-scope release
+// fence per workgroup; on gfx950 that writes back the XCD's L2 and made the
+// contraction 8x slower than the separate reduce launch.)
 // W^T is rewritten on every call (2 |W| bytes of traffic): the forward
 // kernel's contiguous-contraction operand reads run faster than reading W
 // as stored through transposing LDS reads, by more than the copy costs
@@ -33,6 +38,7 @@ namespace lora {
 namespace {
 
 constexpr int cmaxi(int a, int b) { return a > b ? a : b; }
+constexpr int cmini(int a, int b) { return a < b ? a : b; }
 constexpr int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 
 // 128-B staged rows of 64 bf16 with 16-B chunks swizzled by row & 7: the MFMA
@@ -50,10 +56,11 @@ __device__ __forceinline__ int tr_off(int row, int col) {
 }
 
 // ---------------------------------------------------------------- transposes
-// Workgroups [0, wtiles): 64 x 64 tiles of W^T (16-B loads of W rows into
-// LDS, 16-B stores of W^T rows; N and K are multiples of 8, so a chunk is
-// either wholly inside or wholly outside).  The rest: B^T and A^T, one
-// element per thread.
+// Preparation work, in blocks of nt threads: blocks [0, wtiles) each write
+// a 64 x 64 tile of W^T (16-B loads of W rows into LDS, 16-B stores of W^T
+// rows; N and K are multiples of 8, so a chunk is either wholly inside or
+// wholly outside); the following blocks write B^T and A^T, one element per
+// thread.
 struct PrepArgs {
   int N, K, r, wtiles_k, wtiles;
   const uint16_t* W; int64_t ldw; uint16_t* Wt; int64_t ldwt;
@@ -61,13 +68,20 @@ struct PrepArgs {
   const uint16_t* A; int64_t lda; uint16_t* At; int64_t ldat;
 };
 
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-B rows
-  const int b = blockIdx.x, tid = threadIdx.x;
+typedef uint16_t PrepTile[64][72];  // 144-B rows
+constexpr int kPrepTileB = 64 * 72 * 2;
+
+// Blocks the preparation needs with nt threads per block.
+inline int64_t prep_blocks(const PrepArgs& a, int nt) {
+  const int64_t small = (int64_t)a.r * a.N + (int64_t)a.K * a.r;
+  return a.wtiles + (small + nt - 1) / nt;
+}
+
+__device__ __forceinline__ void prep_block(const PrepArgs& a, int b, int tid, int nt,
+                                           PrepTile& tile) {
   if (b < a.wtiles) {
     const int n0 = (b / a.wtiles_k) * 64, k0 = (b % a.wtiles_k) * 64;
-#pragma unroll
-    for (int c = tid; c < 512; c += 256) {
+    for (int c = tid; c < 512; c += nt) {
       const int row = c >> 3, ch = c & 7;
       const int n = n0 + row, k = k0 + ch * 8;
       u32x4 v = u32x4{0, 0, 0, 0};
@@ -75,8 +89,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       *reinterpret_cast<u32x4*>(&tile[row][ch * 8]) = v;
     }
     __syncthreads();
-#pragma unroll
-    for (int c = tid; c < 512; c += 256) {
+    for (int c = tid; c < 512; c += nt) {
       const int row = c >> 3, ch = c & 7;  // row: k offset, ch: chunk of 8 n
       const int k = k0 + row, n = n0 + ch * 8;
       if (k >= a.K || n >= a.N) continue;
@@ -88,7 +101,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
     return;
   }
-  int64_t e = (int64_t)(b - a.wtiles) * 256 + tid;
+  int64_t e = (int64_t)(b - a.wtiles) * nt + tid;
   const int64_t nb = (int64_t)a.r * a.N;
   if (e < nb) {
     const int j = (int)(e / a.N), n = (int)(e % a.N);
@@ -100,6 +113,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int k = (int)(e / a.r), j = (int)(e % a.r);
     a.At[(int64_t)k * a.ldat + j] = a.A[(int64_t)j * a.lda + k];
   }
+}
+
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+  __shared__ __attribute__((aligned(16))) PrepTile tile;
+  prep_block(a, blockIdx.x, threadIdx.x, 256, tile);
 }
 
 // ---------------------------------------------------------------- projection
@@ -118,17 +136,23 @@ struct ProjJob {
   uint16_t* Pt;
 };
 
-template <int RP>
+// NW_ waves per workgroup, BT = 16 NW_ tokens: fewer waves per workgroup for
+// fewer tokens, so that the grid still spreads over the CUs.
+template <int RP, int NW_>
 struct Prj {
-  static constexpr int BT = 64, NW = 4, NT = NW * kWave, RB = RP / 16;
+  static constexpr int NW = NW_, BT = 16 * NW, NT = NW * kWave, RB = RP / 16;
   static constexpr int kRows = BT + RP;          // staged rows per stage: tokens, then ranks
   static constexpr int kStageB = kRows * 128;    // 64 contraction values per row
-  static constexpr int kLoads = kRows / 8;       // 1-KiB loads per stage; the first 8 are Z
+  static constexpr int kZL = BT / 8;             // Z loads per stage (two per wave), first
+  static constexpr int kLoads = kRows / 8;       // 1-KiB loads per stage
   static constexpr int kUL = (RP / 8 + NW - 1) / NW;  // U load slots per wave
   static constexpr int kLo = kLoads / NW, kHi = kLo + (kLoads % NW != 0 ? 1 : 0);
-  static constexpr int STAGES = clampi(64 * 1024 / kStageB, 2, 6);
+  // Ring depth: up to 64 KiB, and the vmcnt of STAGES - 2 stages in flight
+  // within its 6-bit field.
+  static constexpr int STAGES = cmini(clampi(64 * 1024 / kStageB, 2, 6), 2 + 63 / kHi);
   static constexpr int kLds = STAGES * kStageB;
-  static_assert(BT == 16 * NW && BT % 8 == 0, "one 16-token block per wave, 8-row loads");
+  static_assert(kZL == 2 * NW, "two Z loads per wave");
+  static_assert((STAGES - 2) * kHi <= 63, "vmcnt range");
   static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
@@ -145,11 +169,19 @@ __device__ __forceinline__ void wait_own(int wave) {
   wait_vmcnt<Newer * Lo>();
 }
 
-template <int RP>
-__global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, float scale, ProjJob j0,
-                                                           ProjJob j1, int64_t ldp) {
-  using P = Prj<RP>;
+// Blocks x >= prep_from run the preparation work instead (one launch for
+// both when the projection does not need B^T); their LDS is the ring's.
+template <int RP, int NW>
+__global__ __launch_bounds__(NW * kWave) void proj_kernel(int M, int r, float scale,
+                                                               ProjJob j0, ProjJob j1,
+                                                               int64_t ldp, PrepArgs pa,
+                                                               int prep_from) {
+  using P = Prj<RP, NW>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  if ((int)blockIdx.x >= prep_from) {
+    prep_block(pa, blockIdx.x - prep_from, threadIdx.x, P::NT, *reinterpret_cast<PrepTile*>(smem));
+    return;
+  }
   const ProjJob jb = blockIdx.y == 0 ? j0 : j1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,7 +196,7 @@ __global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, float s
   const __amdgpu_buffer_rsrc_t ru =
       __builtin_amdgcn_make_buffer_rsrc((void*)jb.U, 0, (int)(r * jb.ldu * 2), 0x00020000);
   // Lane i of a 1-KiB load writes row 8q + i / 8, physical chunk i % 8.
-  // Wave w issues Z loads q = w and w + 4 and U loads 8 + w + 4 s.
+  // Wave w issues Z loads q = w and w + NW and U loads kZL + w + NW s.
   const int lrl = lane >> 3;
   const int lch = (lane & 7) ^ lrl;
   const uint32_t vz = (uint32_t)((8 * wave + lrl) * jb.ldz * 2 + lch * 16);
@@ -184,11 +216,11 @@ __global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, float s
                                                0);
 #pragma unroll
     for (int s = 0; s < P::kUL; ++s) {
-      const int p = wave + s * P::NW;  // U load index (stage load 8 + p)
+      const int p = wave + s * P::NW;  // U load index (stage load kZL + p)
       if (p < RP / 8)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ru, (lds_void*)(base + (8 + p) * 1024), 16, off_or_oob(kin, vu + sgpr(s * su + cb)),
-            0, 0, 0);
+            ru, (lds_void*)(base + (P::kZL + p) * 1024), 16,
+            off_or_oob(kin, vu + sgpr(s * su + cb)), 0, 0, 0);
     }
   };
 
@@ -231,6 +263,22 @@ __global__ __launch_bounds__(Prj<RP>::NT) void proj_kernel(int M, int r, float s
       o[1] = pack_bf2(scale * acc[i][2], scale * acc[i][3]);
     }
   }
+}
+
+// Sum of S float4 partials p[0], p[stride], ... added in index order; the
+// loads are issued eight at a time so their latencies overlap.
+__device__ __forceinline__ f32x4 ordered_sum(const float* __restrict__ p, int64_t stride, int S) {
+  f32x4 s4 = zero4();
+  int sp = 0;
+  for (; sp + 8 <= S; sp += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(p + (sp + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s4 += v[u];
+  }
+  for (; sp < S; ++sp) s4 += *reinterpret_cast<const f32x4*>(p + sp * stride);
+  return s4;
 }
 
 // ---------------------------------------------------------------- token contraction
@@ -346,37 +394,23 @@ __global__ __launch_bounds__(Tc<RP>::NT) void tc_kernel(int M, int r, TcJob j0, 
 
   // acc[i] lane: column c0 + 16 w + lrow, ranks 16 i + 4 lk + 0..3.
   const int c = c0 + 16 * wave + lrow;
-  if (c >= C) return;
-  if (job == 0) {
-    float* part = jb.part + (int64_t)split * RP * C;
+  if (c < C) {
+    if (job == 0) {
+      float* part = jb.part + (int64_t)split * RP * C;
 #pragma unroll
-    for (int i = 0; i < T::RB; ++i)
+      for (int i = 0; i < T::RB; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) part[(int64_t)(16 * i + 4 * lk + q) * C + c] = acc[i][q];
-  } else {
-    float* part = jb.part + ((int64_t)split * C + c) * RP;
+        for (int q = 0; q < 4; ++q) part[(int64_t)(16 * i + 4 * lk + q) * C + c] = acc[i][q];
+    } else {
+      float* part = jb.part + ((int64_t)split * C + c) * RP;
 #pragma unroll
-    for (int i = 0; i < T::RB; ++i) *reinterpret_cast<f32x4*>(part + 16 * i + 4 * lk) = acc[i];
+      for (int i = 0; i < T::RB; ++i) *reinterpret_cast<f32x4*>(part + 16 * i + 4 * lk) = acc[i];
+    }
   }
+
 }
 
 // ---------------------------------------------------------------- reduce
-// Sum of S float4 partials p[0], p[stride], ... added in index order; the
-// loads are issued eight at a time so their latencies overlap.
-__device__ __forceinline__ f32x4 ordered_sum(const float* __restrict__ p, int64_t stride, int S) {
-  f32x4 s4 = zero4();
-  int sp = 0;
-  for (; sp + 8 <= S; sp += 8) {
-    f32x4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(p + (sp + u) * stride);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s4 += v[u];
-  }
-  for (; sp < S; ++sp) s4 += *reinterpret_cast<const f32x4*>(p + sp * stride);
-  return s4;
-}
-
 // dA[j, k] = round(sum_split partA[split][j][k]) and
 // dB[n, j] = round(sum_split partB[split][n][j]), splits added in order (the
 // scale is already in s G and s T).  One thread per 4 consecutive outputs.
@@ -407,42 +441,87 @@ __global__ __launch_bounds__(64) void red_kernel(int S, int r, int RP, int K, in
     if (j + q < r) out[q] = f2bf(s4[q]);
 }
 
-// with_g: the projection also computes s G (the dX kernel did not).
+// The projection (jobs 1: s T; 2: s T and s G), optionally followed in the
+// same grid by the preparation blocks (only with one job: blocks of a second
+// job row would repeat them).
+template <int RP, int NW>
+hipError_t launch_proj(const BwdArgs& a, const BwdPlan& p, const ProjJob& jt, const ProjJob& jg,
+                       int jobs, const PrepArgs* pre, hipStream_t s) {
+  using P = Prj<RP, NW>;
+  auto kern = proj_kernel<RP, NW>;
+  const int lds = cmaxi(P::kLds, kPrepTileB);
+  static std::atomic<uint64_t> done{0};
+  if (hipError_t e = ensure_lds(kern, lds, done); e != hipSuccess) return e;
+  const int tiles = (int)(p.ldp / P::BT);
+  const int64_t extra = (pre != nullptr && jobs == 1) ? prep_blocks(*pre, P::NT) : 0;
+  const PrepArgs none{};
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles + extra), jobs), dim3(P::NT), lds, s, (int)a.M,
+                     (int)a.r, a.scale, jt, jg, p.ldp, extra > 0 ? *pre : none, tiles);
+  return hipGetLastError();
+}
+
 template <int RP>
-hipError_t launch_proj_tc(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, bool with_g,
-                          hipStream_t s) {
+hipError_t launch_proj_nw(const BwdArgs& a, const BwdPlan& p, const ProjJob& jt,
+                          const ProjJob& jg, int jobs, const PrepArgs* pre, hipStream_t s) {
+  // The most waves per workgroup that still gives 256 projection workgroups.
+  const int64_t tiles16 = p.ldp / 16 * jobs;
+  if (tiles16 >= 4 * 256) return launch_proj<RP, 4>(a, p, jt, jg, jobs, pre, s);
+  if (tiles16 >= 2 * 256) return launch_proj<RP, 2>(a, p, jt, jg, jobs, pre, s);
+  return launch_proj<RP, 1>(a, p, jt, jg, jobs, pre, s);
+}
+
+// Launches 1-3 for M > 0 (see the top of the file).
+template <int RP>
+hipError_t launch_rank(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, bool want_dx,
+                       const PrepArgs& pre, hipStream_t s) {
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, r = (int)a.r;
   const uint16_t* Bt = reinterpret_cast<const uint16_t*>(ws + p.off_bt);
   uint16_t* Tt = reinterpret_cast<uint16_t*>(ws + p.off_tt);
   uint16_t* Gt = reinterpret_cast<uint16_t*>(ws + p.off_gt);
-  {
-    ProjJob jt{static_cast<const uint16_t*>(a.X), a.ldx, K, static_cast<const uint16_t*>(a.A),
-               a.lda, Tt};
-    ProjJob jg{static_cast<const uint16_t*>(a.dY), a.lddy, N, Bt, p.ldbt, Gt};
-    auto kern = proj_kernel<RP>;
-    static std::atomic<uint64_t> done{0};
-    if (hipError_t e = ensure_lds(kern, Prj<RP>::kLds, done); e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(p.ldp / Prj<RP>::BT), with_g ? 2 : 1),
-                       dim3(Prj<RP>::NT), Prj<RP>::kLds, s, M, r, a.scale, jt, jg, p.ldp);
+  const ProjJob jt{static_cast<const uint16_t*>(a.X), a.ldx, K,
+                   static_cast<const uint16_t*>(a.A), a.lda, Tt};
+  const ProjJob jg{static_cast<const uint16_t*>(a.dY), a.lddy, N, Bt, p.ldbt, Gt};
+  if (want_dx) {
+    // 1. s T with the transposes; 2. dX, whose rank intermediate is s G.
+    if (hipError_t e = launch_proj_nw<RP>(a, p, jt, jg, 1, &pre, s); e != hipSuccess) return e;
+    const uint16_t* Wt = reinterpret_cast<const uint16_t*>(ws + p.off_wt);
+    const uint16_t* At = reinterpret_cast<const uint16_t*>(ws + p.off_at);
+    const FwdArgs f{a.M, a.K, a.N, a.r, a.dY, a.lddy, Wt, p.ldwt, Bt, p.ldbt, At, p.ldat,
+                    a.scale, a.dX, a.lddx, Gt, p.ldp};
+    if (hipError_t e = launch_fwd_tiled_bf16(f, s); e != hipSuccess) return e;
+  } else {
+    // 1. B^T; 2. s T and s G.
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks(pre, 256)), dim3(256), 0, s, pre);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if (hipError_t e = launch_proj_nw<RP>(a, p, jt, jg, 2, nullptr, s); e != hipSuccess) return e;
   }
-  {
-    TcJob ja{static_cast<const uint16_t*>(a.X), a.ldx, K, Gt,
-             reinterpret_cast<float*>(ws + p.off_pa)};
-    TcJob jbb{static_cast<const uint16_t*>(a.dY), a.lddy, N, Tt,
-              reinterpret_cast<float*>(ws + p.off_pb)};
-    const int tiles0 = (K + 63) / 64, tiles1 = (N + 63) / 64;
-    const int64_t grid = (int64_t)(tiles0 + tiles1) * p.S;
-    if (grid > 0) {
-      auto kern = tc_kernel<RP>;
-      static std::atomic<uint64_t> done{0};
-      if (hipError_t e = ensure_lds(kern, Tc<RP>::kLds, done); e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Tc<RP>::NT), Tc<RP>::kLds, s, M, r, ja,
-                         jbb, p.ldp, tiles0, tiles1, (int)p.tps);
-      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    }
-  }
-  return hipSuccess;
+  // 3. Token contraction, reduction included.
+  const int tiles0 = (K + 63) / 64, tiles1 = (N + 63) / 64;
+  const int64_t grid = (int64_t)(tiles0 + tiles1) * p.S;
+  if (grid == 0) return hipSuccess;
+  const TcJob ja{static_cast<const uint16_t*>(a.X), a.ldx, K, Gt,
+                 reinterpret_cast<float*>(ws + p.off_pa)};
+  const TcJob jb{static_cast<const uint16_t*>(a.dY), a.lddy, N, Tt,
+                 reinterpret_cast<float*>(ws + p.off_pb)};
+  auto kern = tc_kernel<RP>;
+  static std::atomic<uint64_t> done{0};
+  if (hipError_t e = ensure_lds(kern, Tc<RP>::kLds, done); e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Tc<RP>::NT), Tc<RP>::kLds, s, M, r, ja, jb,
+                     p.ldp, tiles0, tiles1, (int)p.tps);
+  return hipGetLastError();
+}
+
+// 4. dA = round(sum of partials), dB likewise; with S = 0 (no tokens) zeros.
+hipError_t launch_red(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, hipStream_t s) {
+  const int N = (int)a.N, K = (int)a.K, r = (int)a.r;
+  const int64_t na = (int64_t)r * (K / 4);
+  const int64_t total = na + (int64_t)N * ((r + 3) / 4);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(red_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64), 0, s, p.S, r,
+                     pad_rank(a.r), K, N, reinterpret_cast<const float*>(ws + p.off_pa),
+                     reinterpret_cast<const float*>(ws + p.off_pb), static_cast<uint16_t*>(a.dA),
+                     a.ldda, static_cast<uint16_t*>(a.dB), a.lddb, na);
+  return hipGetLastError();
 }
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
@@ -484,57 +563,25 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, void* workspace, hipStream_t s) {
   const BwdPlan p = bwd_plan(a.M, a.N, a.K, a.r);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const int N = (int)a.N, K = (int)a.K, r = (int)a.r;
-  const bool want_dx = a.dX != nullptr && a.M > 0 && a.K > 0;
-  uint16_t* Wt = reinterpret_cast<uint16_t*>(ws + p.off_wt);
-  uint16_t* At = reinterpret_cast<uint16_t*>(ws + p.off_at);
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
-  // 1. W^T, B^T (the projection's and the dX kernel's operand) and A^T.
-  {
-    PrepArgs pa{N, K, r, (K + 63) / 64, 0, static_cast<const uint16_t*>(a.W), a.ldw, Wt, p.ldwt,
-                static_cast<const uint16_t*>(a.B), a.ldb, Bt, p.ldbt,
-                static_cast<const uint16_t*>(a.A), a.lda, At, p.ldat};
-    if (want_dx) pa.wtiles = ((N + 63) / 64) * pa.wtiles_k;
-    const int64_t small = (int64_t)r * N + (want_dx ? (int64_t)K * r : 0);
-    const int64_t grid = pa.wtiles + (small + 255) / 256;
-    if (!want_dx) pa.K = 0;  // no A^T either
-    if (grid > 0) {
-      hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(256), 0, s, pa);
-      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    }
+  if (a.M == 0) return launch_red(a, p, ws, s);  // no tokens: p.S = 0, zeros
+  const bool want_dx = a.dX != nullptr && a.K > 0;
+  PrepArgs pre{N, want_dx ? K : 0, r, (K + 63) / 64, 0,
+               static_cast<const uint16_t*>(a.W), a.ldw, reinterpret_cast<uint16_t*>(ws + p.off_wt),
+               p.ldwt, static_cast<const uint16_t*>(a.B), a.ldb,
+               reinterpret_cast<uint16_t*>(ws + p.off_bt), p.ldbt,
+               static_cast<const uint16_t*>(a.A), a.lda, reinterpret_cast<uint16_t*>(ws + p.off_at),
+               p.ldat};
+  if (want_dx) pre.wtiles = ((N + 63) / 64) * pre.wtiles_k;
+  hipError_t e;
+  switch (pad_rank(a.r)) {
+    case 16: e = launch_rank<16>(a, p, ws, want_dx, pre, s); break;
+    case 32: e = launch_rank<32>(a, p, ws, want_dx, pre, s); break;
+    case 64: e = launch_rank<64>(a, p, ws, want_dx, pre, s); break;
+    case 128: e = launch_rank<128>(a, p, ws, want_dx, pre, s); break;
+    default: e = launch_rank<256>(a, p, ws, want_dx, pre, s); break;
   }
-  // 2. dX = dY W + s (dY B) A: the forward of dY with W' = W^T, A' = B^T,
-  //    B' = A^T; its rank intermediate s dY B = s G goes to the workspace.
-  if (want_dx) {
-    FwdArgs f{a.M, a.K, a.N, a.r, a.dY, a.lddy, Wt, p.ldwt, Bt, p.ldbt, At, p.ldat, a.scale,
-              a.dX, a.lddx, ws + p.off_gt, p.ldp};
-    if (hipError_t e = launch_fwd_tiled_bf16(f, s); e != hipSuccess) return e;
-  }
-  // 3-4. s T (and s G), then the partial sums (nothing to do without tokens).
-  if (a.M > 0) {
-    hipError_t e;
-    switch (pad_rank(a.r)) {
-      case 16: e = launch_proj_tc<16>(a, p, ws, !want_dx, s); break;
-      case 32: e = launch_proj_tc<32>(a, p, ws, !want_dx, s); break;
-      case 64: e = launch_proj_tc<64>(a, p, ws, !want_dx, s); break;
-      case 128: e = launch_proj_tc<128>(a, p, ws, !want_dx, s); break;
-      default: e = launch_proj_tc<256>(a, p, ws, !want_dx, s); break;
-    }
-    if (e != hipSuccess) return e;
-  }
-  // 5. dA, dB (zeros when there are no tokens).
-  {
-    const int64_t na = (int64_t)r * (K / 4);
-    const int64_t total = na + (int64_t)N * ((r + 3) / 4);
-    if (total > 0) {
-      hipLaunchKernelGGL(red_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64), 0, s, p.S, r,
-                         pad_rank(a.r), K, N, reinterpret_cast<const float*>(ws + p.off_pa),
-                         reinterpret_cast<const float*>(ws + p.off_pb),
-                         static_cast<uint16_t*>(a.dA), a.ldda, static_cast<uint16_t*>(a.dB),
-                         a.lddb, na);
-      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    }
-  }
-  return hipSuccess;
+  if (e != hipSuccess) return e;
+  return launch_red(a, p, ws, s);
 }
 
 }  // namespace lora

@@ -63,8 +63,8 @@ struct BwdArgs {
 
 // Workspace layout of the backward (byte offsets from a 256-B aligned base):
 // W^T [K, ldwt], A^T [K, ldat], B^T [r, ldbt], T^T and G^T [r, ldp], all
-// bf16, and the fp32 partial sums of dA [S][RP][K] and of dB [S][N][RP] over
-// S token ranges of tps tokens.
+// bf16, the fp32 partial sums of dA [S][RP][K] and of dB [S][N][RP] over S
+// token ranges of tps tokens.
 struct BwdPlan {
   int S;
   int64_t tps, ldwt, ldat, ldbt, ldp;
