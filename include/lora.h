@@ -9,7 +9,12 @@
  *             out = X W^T + ((X A^T) B^T) * scale, scale = alpha / r, and the
  *             fused kernel keeps the [tokens, r] intermediate X A^T on chip;
  *             section "BWD kernel speedup": its backward produces dA, dB and
- *             dX, and dA is parallelised over the sequence.
+ *             dX, and dA is parallelised over the sequence; section "Block
+ *             size tuning": candidate tile configurations are pruned by the
+ *             device's per-block thread, register and shared-memory limits
+ *             and a minimum occupancy, the survivors benchmarked, and the
+ *             winner cached per shape (nearest shape on a miss, else a
+ *             default).
  *   [unsloth] unsloth commit log for scripts/benchmarks/qwen3_flex_inference.py,
  *             the entry that replaces copy+merge_adapter by one
  *             addmm(pristine, B, A, alpha=scaling, out=W_inf) per layer: the
@@ -47,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 4
+#define LORA_ABI_VERSION 5
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -241,6 +246,71 @@ int lora_bwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r,
 /* Workspace bytes lora_bwd needs for these sizes (0 is possible), or -1 when
  * dtype or the sizes are not supported.  Depends on the sizes only. */
 int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int64_t r);
+
+/*
+ * Tile configurations of the bf16 tiled forward, for a tuner   [fastaf],
+ * "Block size tuning".  lora_fwd's own choice (AUTO) is the built-in default;
+ * lora_fwd_tile runs one configuration by id.  An id is instantiated only
+ * for the padded ranks whose LDS footprint fits the 160 KiB of a CU.
+ *
+ *   id  tile       waves  T shared over   ranks
+ *   0   64 x 32      4    1 N tile        r <= 32
+ *   1   128 x 128    8    1               r <= 256
+ *   2   128 x 128    8    2 N tiles       r <= 128
+ *   3   128 x 128    8    4 N tiles       r <= 128
+ *   4   256 x 256    8    1               r <= 64
+ *   5   256 x 256    8    2 N tiles       r <= 32
+ * ("T shared over g N tiles": a workgroup computes g consecutive output
+ * tiles of one row block and the down-projection T only once.)
+ */
+#define LORA_TILE_COUNT 6
+
+typedef struct lora_tile_info {
+    int32_t tile;        /* id */
+    int32_t bm, bn;      /* output tile rows (tokens) x columns */
+    int32_t waves;       /* 64-lane waves per workgroup */
+    int32_t stages;      /* depth of the LDS stage ring */
+    int32_t bk;          /* K per stage */
+    int32_t group;       /* N tiles per workgroup sharing T */
+    int32_t rank_pad;    /* rank the instantiation is padded to */
+    int32_t lds_bytes;   /* dynamic LDS per workgroup */
+} lora_tile_info;
+
+typedef struct lora_tile_usage {
+    int32_t vgprs;            /* vector registers per lane (numRegs) */
+    int32_t scratch_bytes;    /* per-lane spill memory; > 0 means spills */
+    int32_t blocks_per_cu;    /* resident workgroups per CU at lds_bytes */
+} lora_tile_usage;
+
+typedef struct lora_device_limits {
+    int32_t compute_units;
+    int32_t lds_per_block;         /* bytes */
+    int32_t lds_per_cu;            /* bytes */
+    int32_t regs_per_block;
+    int32_t max_threads_per_block;
+    int32_t wave_size;
+} lora_device_limits;
+
+/* Static description of tile `tile` at rank r (no HIP call).
+ * LORA_ERR_UNSUPPORTED: no such id, or not instantiated for this rank;
+ * LORA_ERR_SHAPE: r < 1; LORA_ERR_NULL: out is NULL. */
+int lora_tile_get_info(int tile, int64_t r, lora_tile_info *out);
+
+/* Register, spill and occupancy figures of tile `tile` at rank r on the
+ * current device (hipFuncGetAttributes, hipOccupancyMaxActiveBlocksPerMultiprocessor).
+ * Errors as lora_tile_get_info, plus LORA_ERR_HIP. */
+int lora_tile_get_usage(int tile, int64_t r, lora_tile_usage *out);
+
+/* Limits of the current device (hipGetDeviceProperties). */
+int lora_get_device_limits(lora_device_limits *out);
+
+/* lora_fwd with tile configuration `tile` (bf16 only; same arguments,
+ * layouts and errors as lora_fwd; LORA_ERR_UNSUPPORTED for f32, an unknown
+ * id or one not instantiated for this rank). */
+int lora_fwd_tile(int tile, int dtype, int64_t M, int64_t N, int64_t K, int64_t r,
+                  const void *X, int64_t ldx, const void *W, int64_t ldw,
+                  const void *A, int64_t lda, const void *B, int64_t ldb,
+                  float scale, void *Y, int64_t ldy, void *stream);
 
 /* Static, NUL-terminated description of a lora_status value. */
 const char *lora_status_str(int status);

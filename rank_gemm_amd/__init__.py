@@ -10,6 +10,8 @@ loaded, the first call raises.
     merge_batch([(W0, B, A, scale, W_inf), ...])   # many targets, few launches
     merge_inplace(W, B, A, scale)       # W += scale * B A in place (not bit-reversible)
     dX, dA, dB = bwd(X, W, A, B, dY, scale)   # gradients with W frozen (bf16)
+    Y = fwd(X, W, A, B, scale, tile=4)   # one tile configuration (see tune.py)
+    Y = fwd_tuned(X, W, A, B, scale)     # the configuration cached for this shape
 
 Tensors are torch tensors on the current HIP device, all bfloat16 or all
 float32, 2-D with unit inner stride (rows may be padded: the leading
@@ -42,9 +44,12 @@ VARIANTS = {"auto": 0, "tiled": 1, "decode": 2}
 MAX_RANK = 256
 DECODE_MAX_M = 64
 
+TILE_COUNT = 6
+
 EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch",
            "lora_merge_inplace", "lora_status_str", "lora_abi_version", "lora_fwd_pick",
-           "lora_bwd", "lora_bwd_workspace_size")
+           "lora_bwd", "lora_bwd_workspace_size", "lora_tile_get_info", "lora_tile_get_usage",
+           "lora_get_device_limits", "lora_fwd_tile")
 
 
 class MergeDesc(ctypes.Structure):
@@ -55,6 +60,26 @@ class MergeDesc(ctypes.Structure):
                 ("A", ctypes.c_void_p), ("lda", ctypes.c_int64),
                 ("scale", ctypes.c_float),
                 ("W_inf", ctypes.c_void_p), ("ldwi", ctypes.c_int64)]
+
+
+
+class TileInfo(ctypes.Structure):
+    """lora_tile_info of include/lora.h."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("tile", "bm", "bn", "waves", "stages", "bk",
+                                              "group", "rank_pad", "lds_bytes")]
+
+
+class TileUsage(ctypes.Structure):
+    """lora_tile_usage of include/lora.h."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("vgprs", "scratch_bytes", "blocks_per_cu")]
+
+
+class DeviceLimits(ctypes.Structure):
+    """lora_device_limits of include/lora.h."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("compute_units", "lds_per_block", "lds_per_cu",
+                                              "regs_per_block", "max_threads_per_block",
+                                              "wave_size")]
+
 
 _lib = None
 
@@ -96,6 +121,14 @@ def lib() -> ctypes.CDLL:
     L.lora_bwd.restype = i32
     L.lora_bwd_workspace_size.argtypes = [i32, i64, i64, i64, i64]
     L.lora_bwd_workspace_size.restype = i64
+    L.lora_tile_get_info.argtypes = [i32, i64, ctypes.POINTER(TileInfo)]
+    L.lora_tile_get_info.restype = i32
+    L.lora_tile_get_usage.argtypes = [i32, i64, ctypes.POINTER(TileUsage)]
+    L.lora_tile_get_usage.restype = i32
+    L.lora_get_device_limits.argtypes = [ctypes.POINTER(DeviceLimits)]
+    L.lora_get_device_limits.restype = i32
+    L.lora_fwd_tile.argtypes = [i32] + L.lora_fwd.argtypes
+    L.lora_fwd_tile.restype = i32
     _lib = L
     return L
 
@@ -148,6 +181,39 @@ def merge_batch_raw(dtype: int, descs, stream: int = 0) -> int:
     return int(lib().lora_merge_batch(dtype, len(descs), descs, stream or None))
 
 
+def tile_info(tile: int, r: int) -> Optional[TileInfo]:
+    """Static description of tile configuration `tile` at rank r, or None when
+    it is not instantiated for that rank (lora_tile_get_info; no HIP call)."""
+    out = TileInfo()
+    st = int(lib().lora_tile_get_info(tile, r, ctypes.byref(out)))
+    if st == LORA_ERR_UNSUPPORTED:
+        return None
+    _check(st, "lora_tile_get_info")
+    return out
+
+
+def tile_usage(tile: int, r: int) -> TileUsage:
+    """Registers, spill bytes and resident workgroups per CU on the current
+    device (lora_tile_get_usage)."""
+    out = TileUsage()
+    _check(int(lib().lora_tile_get_usage(tile, r, ctypes.byref(out))), "lora_tile_get_usage")
+    return out
+
+
+def device_limits() -> DeviceLimits:
+    out = DeviceLimits()
+    _check(int(lib().lora_get_device_limits(ctypes.byref(out))), "lora_get_device_limits")
+    return out
+
+
+def fwd_tile_raw(tile: int, dtype: int, M: int, N: int, K: int, r: int, X: int, ldx: int, W: int,
+                 ldw: int, A: int, lda: int, B: int, ldb: int, scale: float, Y: int, ldy: int,
+                 stream: int = 0) -> int:
+    """lora_fwd_tile with integer addresses; returns the lora_status."""
+    return int(lib().lora_fwd_tile(tile, dtype, M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, scale,
+                                   Y, ldy, stream or None))
+
+
 def bwd_workspace_size(dtype: int, M: int, N: int, K: int, r: int) -> int:
     """lora_bwd_workspace_size: bytes, or -1 when not supported."""
     return int(lib().lora_bwd_workspace_size(dtype, M, N, K, r))
@@ -190,10 +256,12 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def fwd(X, W, A, B, scale: float, out=None, variant: str = "auto"):
+def fwd(X, W, A, B, scale: float, out=None, variant: str = "auto", tile: Optional[int] = None):
     """Fused LoRA forward ``Y = X W^T + scale * (X A^T) B^T`` on the GPU.
 
     X[M,K], W[N,K], A[r,K], B[N,r]; returns Y[M,N] (``out`` if given).
+    ``tile``: run that tiled configuration (lora_fwd_tile, bf16) instead of
+    the library's choice; ``variant`` forces tiled/decode otherwise.
     """
     import torch
     M, K = X.shape
@@ -215,10 +283,38 @@ def fwd(X, W, A, B, scale: float, out=None, variant: str = "auto"):
     pa, lda = _mat(A, "A")
     pb, ldb = _mat(B, "B")
     py, ldy = _mat(out, "out")
+    if tile is not None:
+        st = fwd_tile_raw(int(tile), dt, M, N, K, r, px, ldx, pw, ldw, pa, lda, pb, ldb,
+                          float(scale), py, ldy, _stream(X.device))
+        _check(st, "lora_fwd_tile")
+        return out
     st = fwd_raw(VARIANTS[variant], dt, M, N, K, r, px, ldx, pw, ldw, pa, lda, pb, ldb,
                  float(scale), py, ldy, _stream(X.device))
     _check(st, "lora_fwd")
     return out
+
+
+_tile_cache = None
+
+
+def fwd_tuned(X, W, A, B, scale: float, out=None, cache=None):
+    """``fwd`` with the tile configuration a tuner cached for this shape (or
+    the nearest cached shape), else the library's own choice.  ``cache``: a
+    ``tune.TileCache``; by default the file ``tune.default_cache_path()``,
+    loaded once."""
+    from . import tune
+    global _tile_cache
+    if cache is None:
+        if _tile_cache is None:
+            _tile_cache = tune.TileCache.load()
+        cache = _tile_cache
+    dt = "bf16" if _dtype_code(X) == LORA_BF16 else "f32"
+    choice = cache.lookup(dt, X.shape[0], W.shape[0], X.shape[1], A.shape[0])
+    if choice is None:
+        return fwd(X, W, A, B, scale, out=out)
+    if choice == tune.DECODE:
+        return fwd(X, W, A, B, scale, out=out, variant="decode")
+    return fwd(X, W, A, B, scale, out=out, tile=int(choice.split(":")[1]))
 
 
 def merge(W0, B, A, scale: float, out=None):

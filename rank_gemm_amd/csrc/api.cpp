@@ -308,4 +308,63 @@ int lora_bwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void* 
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+int lora_tile_get_info(int tile, int64_t r, lora_tile_info* out) {
+  if (out == nullptr) return LORA_ERR_NULL;
+  if (r < 1) return LORA_ERR_SHAPE;
+  if (r > LORA_MAX_RANK || tile < 0 || tile >= LORA_TILE_COUNT) return LORA_ERR_UNSUPPORTED;
+  lora::TileProps t{};
+  if (lora::fwd_tile_props(tile, r, &t) != hipSuccess) return LORA_ERR_UNSUPPORTED;
+  *out = lora_tile_info{tile, t.bm, t.bn, t.waves, t.stages, t.bk, t.group, t.rank_pad,
+                        t.lds_bytes};
+  return LORA_OK;
+}
+
+int lora_tile_get_usage(int tile, int64_t r, lora_tile_usage* out) {
+  if (out == nullptr) return LORA_ERR_NULL;
+  if (r < 1) return LORA_ERR_SHAPE;
+  if (r > LORA_MAX_RANK || tile < 0 || tile >= LORA_TILE_COUNT) return LORA_ERR_UNSUPPORTED;
+  lora::TileProps t{};
+  if (lora::fwd_tile_props(tile, r, &t) != hipSuccess) return LORA_ERR_UNSUPPORTED;
+  hipFuncAttributes attr{};
+  if (hipFuncGetAttributes(&attr, t.kernel) != hipSuccess) return LORA_ERR_HIP;
+  // Occupancy at the kernel's LDS needs the raised dynamic-LDS limit.
+  if (hipFuncSetAttribute(t.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, t.lds_bytes) !=
+      hipSuccess)
+    return LORA_ERR_HIP;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, t.kernel, t.waves * 64,
+                                                   t.lds_bytes) != hipSuccess)
+    return LORA_ERR_HIP;
+  *out = lora_tile_usage{attr.numRegs, (int32_t)attr.localSizeBytes, blocks};
+  return LORA_OK;
+}
+
+int lora_get_device_limits(lora_device_limits* out) {
+  if (out == nullptr) return LORA_ERR_NULL;
+  int dev = 0;
+  hipDeviceProp_t p{};
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess)
+    return LORA_ERR_HIP;
+  *out = lora_device_limits{p.multiProcessorCount, (int32_t)p.sharedMemPerBlock,
+                            (int32_t)p.maxSharedMemoryPerMultiProcessor, p.regsPerBlock,
+                            p.maxThreadsPerBlock, p.warpSize};
+  return LORA_OK;
+}
+
+int lora_fwd_tile(int tile, int dtype, int64_t M, int64_t N, int64_t K, int64_t r,
+                  const void* X, int64_t ldx, const void* W, int64_t ldw, const void* A,
+                  int64_t lda, const void* B, int64_t ldb, float scale, void* Y, int64_t ldy,
+                  void* stream) {
+  const int st = check_fwd(dtype, M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, Y, ldy);
+  if (st != LORA_OK) return st;
+  lora::TileProps t{};
+  if (dtype != LORA_BF16 || tile < 0 || tile >= LORA_TILE_COUNT ||
+      lora::fwd_tile_props(tile, r, &t) != hipSuccess)
+    return LORA_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return LORA_OK;
+  const lora::FwdArgs a{M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, scale, Y, ldy};
+  const hipError_t e = lora::launch_fwd_tile_bf16(tile, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 }  // extern "C"

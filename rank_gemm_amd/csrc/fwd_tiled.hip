@@ -578,26 +578,112 @@ using Tall = Cfg<64, 32, 4, 1, RP, 8, 64>;
 template <int RP>
 using Mid = Cfg<128, 128, 4, 2, RP, 2, 64>;
 
+// The built-in choice (lora_fwd's default), from the tile tuner's
+// measurements on the benchmark shapes:
+//  * rank <= 32 and fewer tokens than one 128-row tile, or a 128 x 128 grid
+//    that would leave more than half of the 256 CUs idle: the 64 x 32 tile
+//    (512 x 1024 x 512 r16: 8.8 vs 10.8 us);
+//  * 256 x 256 when there are >= 256 such tiles and the last round of them
+//    is at least 80 % full (q_proj, 512 tiles: 160 vs 202 us; the q_proj
+//    backward's dX product, 320 tiles: 211 us vs 191 us on 128 x 128);
+//  * rank 128 with >= 512 128 x 128 tiles: T shared over 2 N tiles (square
+//    16384 x 8192 x 8192: 3.27 ms; over 4 tiles 3.73 ms; unshared 3.87 ms);
+//  * else 128 x 128.
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
+  const int64_t mid_tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
   if constexpr (RP <= 32) {
-    if (a.M <= 64) return launch<Tall<RP>>(a, s);
+    if (a.M <= 64 || mid_tiles < 128) return launch<Tall<RP>>(a, s);
   }
-  const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   if constexpr (RP <= 64) {
-    if (big_tiles >= 256) return launch<Big<RP>>(a, s);
+    const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+    const int64_t rounds = (big_tiles + 255) / 256;
+    if (big_tiles >= 256 && big_tiles * 5 >= rounds * 256 * 4) return launch<Big<RP>>(a, s);
   }
   if constexpr (RP == 128) {
-    // Rank 128 on 128 x 128 tiles: compute T once per 4 N tiles, when that
-    // still leaves a few workgroups per CU.  (Rank 256 does not fit the LDS
-    // budget with T kept; rank <= 64 takes 256 x 256 tiles at this size.)
-    const int64_t mid_tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    if (a.N > 3 * 128 && mid_tiles >= 4 * 256) return launch<Mid<RP>, 4>(a, s);
+    if (a.N > 128 && mid_tiles >= 512) return launch<Mid<RP>, 2>(a, s);
   }
   return launch<Mid<RP>>(a, s);
 }
 
+// ---- selectable tile configurations (the tile tuner's search space).  The
+// ids are part of the C ABI (lora_fwd_tile); an id exists only for the ranks
+// whose instantiation fits the LDS and the register file.
+template <class C, int G>
+void tile_fill(TileProps* t) {
+  t->bm = C::BM;
+  t->bn = C::BN;
+  t->waves = C::NW;
+  t->stages = C::STAGES;
+  t->bk = C::BK;
+  t->group = G;
+  t->rank_pad = C::RP;
+  t->lds_bytes = G > 1 ? C::kLdsG : C::kLds;
+  t->kernel = reinterpret_cast<const void*>(fwd_tiled_bf16_kernel<C, G>);
+}
+
+// One dispatch for both uses: with props, describe tile `id`; else launch it.
+template <int RP>
+hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
+  switch (id) {
+    case kTileTall:
+      if constexpr (RP <= 32) {
+        if (props) return tile_fill<Tall<RP>, 1>(props), hipSuccess;
+        return launch<Tall<RP>>(*a, s);
+      }
+      break;
+    case kTileMid:
+      if (props) return tile_fill<Mid<RP>, 1>(props), hipSuccess;
+      return launch<Mid<RP>>(*a, s);
+    case kTileMidG2:
+      if constexpr (RP <= 128) {
+        if (props) return tile_fill<Mid<RP>, 2>(props), hipSuccess;
+        return launch<Mid<RP>, 2>(*a, s);
+      }
+      break;
+    case kTileMidG4:
+      if constexpr (RP <= 128) {
+        if (props) return tile_fill<Mid<RP>, 4>(props), hipSuccess;
+        return launch<Mid<RP>, 4>(*a, s);
+      }
+      break;
+    case kTileBig:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<Big<RP>, 1>(props), hipSuccess;
+        return launch<Big<RP>>(*a, s);
+      }
+      break;
+    case kTileBigG2:
+      if constexpr (RP <= 32) {
+        if (props) return tile_fill<Big<RP>, 2>(props), hipSuccess;
+        return launch<Big<RP>, 2>(*a, s);
+      }
+      break;
+    default:
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t tile_dispatch(int id, int64_t r, TileProps* props, const FwdArgs* a, hipStream_t s) {
+  switch (pad_rank(r)) {
+    case 16: return tile_rp<16>(id, props, a, s);
+    case 32: return tile_rp<32>(id, props, a, s);
+    case 64: return tile_rp<64>(id, props, a, s);
+    case 128: return tile_rp<128>(id, props, a, s);
+    default: return tile_rp<256>(id, props, a, s);
+  }
+}
+
 }  // namespace
+
+hipError_t fwd_tile_props(int id, int64_t r, TileProps* out) {
+  return tile_dispatch(id, r, out, nullptr, nullptr);
+}
+
+hipError_t launch_fwd_tile_bf16(int id, const FwdArgs& a, hipStream_t s) {
+  return tile_dispatch(id, a.r, nullptr, &a, s);
+}
 
 hipError_t launch_fwd_tiled_bf16(const FwdArgs& a, hipStream_t s) {
   switch (pad_rank(a.r)) {

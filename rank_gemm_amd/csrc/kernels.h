@@ -78,6 +78,17 @@ inline int pad_rank(int64_t r) {
 
 hipError_t launch_fwd_tiled_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_tiled_f32(const FwdArgs& a, hipStream_t s);
+
+// Selectable tiled configurations (ids of the C ABI's lora_fwd_tile).
+enum TileId { kTileTall = 0, kTileMid = 1, kTileMidG2 = 2, kTileMidG4 = 3, kTileBig = 4,
+              kTileBigG2 = 5, kTileCount = 6 };
+struct TileProps {
+  int bm, bn, waves, stages, bk, group, rank_pad, lds_bytes;
+  const void* kernel;
+};
+// hipErrorInvalidValue when tile `id` has no instantiation for rank r.
+hipError_t fwd_tile_props(int id, int64_t r, TileProps* out);
+hipError_t launch_fwd_tile_bf16(int id, const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge_bf16(const MergeArgs& a, hipStream_t s);
 hipError_t launch_merge_f32(const MergeArgs& a, hipStream_t s);

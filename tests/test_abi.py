@@ -33,7 +33,7 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 4
+    assert rg.abi_version() == 5
     for s in range(10):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
@@ -264,3 +264,23 @@ def test_bwd_workspace_size():
     # a workspace one byte short is refused
     assert _bwd(M=4096, N=1024, K=1024, ldx=1024, ldw=1024, lda=1024, lddy=1024, lddx=1024,
                 ldda=1024, ws_bytes=n - 1) == rg.LORA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(tile=6), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=-1), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=0, r=64, ldb=64), rg.LORA_ERR_UNSUPPORTED),     # 64 x 32 tile: r <= 32
+    (dict(tile=4, r=100, ldb=100), rg.LORA_ERR_UNSUPPORTED),   # 256 x 256 tile: r <= 64
+    (dict(dtype=rg.LORA_F32), rg.LORA_ERR_UNSUPPORTED),
+    (dict(X=0), rg.LORA_ERR_NULL),
+    (dict(ldx=56), rg.LORA_ERR_STRIDE),
+    (dict(Y=PX), rg.LORA_ERR_ALIAS),
+    (dict(M=0), rg.LORA_OK),
+])
+def test_fwd_tile_rejects_before_any_hip_call(kw, want):
+    a = dict(tile=1, dtype=rg.LORA_BF16, M=64, N=64, K=64, r=16, X=PX, ldx=64, W=PW, ldw=64,
+             A=PA, lda=64, B=PB, ldb=16, scale=2.0, Y=PY, ldy=64)
+    a.update(kw)
+    assert rg.fwd_tile_raw(a["tile"], a["dtype"], a["M"], a["N"], a["K"], a["r"], a["X"], a["ldx"],
+                           a["W"], a["ldw"], a["A"], a["lda"], a["B"], a["ldb"], a["scale"],
+                           a["Y"], a["ldy"]) == want
