@@ -260,10 +260,12 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *   3   128 x 128    8    4 N tiles       r <= 128
  *   4   256 x 256    8    1               r <= 64
  *   5   256 x 256    8    2 N tiles       r <= 32
+ *   6   128 x 128    8    1               r <= 128   (three stages)
  * ("T shared over g N tiles": a workgroup computes g consecutive output
- * tiles of one row block and the down-projection T only once.)
+ * tiles of one row block and the down-projection T only once.  Every id
+ * stages 64 k per stage; 0 keeps eight stages, 6 three, the others two.)
  */
-#define LORA_TILE_COUNT 6
+#define LORA_TILE_COUNT 7
 
 typedef struct lora_tile_info {
     int32_t tile;        /* id */

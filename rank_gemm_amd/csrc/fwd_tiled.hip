@@ -577,6 +577,13 @@ template <int RP>
 using Tall = Cfg<64, 32, 4, 1, RP, 8, 64>;
 template <int RP>
 using Mid = Cfg<128, 128, 4, 2, RP, 2, 64>;
+// The same tile with three stages: one workgroup per CU with two stages in
+// flight (2048 x 2048 x 2048 r16: 24.5 vs 27.1 us; slower on the projection
+// shapes).  Measured and dropped: 32-deep stages four deep (64-B rows; 10-25 %
+// slower: half-line loads and twice the barriers) and 4 waves of 64 x 64 with
+// four stages (10-30 % slower).
+template <int RP>
+using Mid3 = Cfg<128, 128, 4, 2, RP, 3, 64>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
 // measurements on the benchmark shapes:
@@ -588,6 +595,9 @@ using Mid = Cfg<128, 128, 4, 2, RP, 2, 64>;
 //    backward's dX product, 320 tiles: 211 us vs 191 us on 128 x 128);
 //  * rank 128 with >= 512 128 x 128 tiles: T shared over 2 N tiles (square
 //    16384 x 8192 x 8192: 3.27 ms; over 4 tiles 3.73 ms; unshared 3.87 ms);
+//  * at most 256 128 x 128 tiles (one per CU, so a second resident workgroup
+//    would have nothing to do): 128 x 128 with three stages (2048 cubed r16:
+//    24.5 vs 27.1 us);
 //  * else 128 x 128.
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
@@ -602,6 +612,9 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
   }
   if constexpr (RP == 128) {
     if (a.N > 128 && mid_tiles >= 512) return launch<Mid<RP>, 2>(a, s);
+  }
+  if constexpr (RP <= 128) {
+    if (mid_tiles <= 256) return launch<Mid3<RP>>(a, s);
   }
   return launch<Mid<RP>>(a, s);
 }
@@ -657,6 +670,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 32) {
         if (props) return tile_fill<Big<RP>, 2>(props), hipSuccess;
         return launch<Big<RP>, 2>(*a, s);
+      }
+      break;
+    case kTileMid3:
+      if constexpr (RP <= 128) {
+        if (props) return tile_fill<Mid3<RP>, 1>(props), hipSuccess;
+        return launch<Mid3<RP>>(*a, s);
       }
       break;
     default:

@@ -8,7 +8,7 @@ fastest is cached per shape in a JSON file.  A shape missing from the cache
 takes the choice of the nearest cached shape; with no usable entry the
 library's own choice (lora_fwd) is used.
 
-Candidates are the tiled configurations of lora_fwd_tile (ids 0-5, see
+Candidates are the tiled configurations of lora_fwd_tile (ids 0-6, see
 include/lora.h) and, for bf16 with M <= 64 and r <= 32, the weight-streaming
 decode kernel ("decode").  Pruning rules, in order:
   * threads per workgroup above the device's limit;
@@ -176,7 +176,7 @@ def valid_for(choice: str, dtype: str, M: int, r: int) -> bool:
 
 def _tile_ranks(tid: int, r: int) -> bool:
     # Same table as include/lora.h (checked against lora_tile_get_info by the tests).
-    limit = {0: 32, 1: 256, 2: 128, 3: 128, 4: 64, 5: 32}.get(tid)
+    limit = {0: 32, 1: 256, 2: 128, 3: 128, 4: 64, 5: 32, 6: 128}.get(tid)
     return limit is not None and pad_rank(r) <= limit
 
 
@@ -277,6 +277,7 @@ BENCH_SHAPES = [
     (16384, 8192, 8192, 128),    # square, r 128
     (1, 4096, 4096, 16), (8, 4096, 4096, 16), (64, 4096, 4096, 16),   # decode-shaped
     (8192, 2560, 4096, 32),      # the q_proj backward's dX product
+    (2048, 2048, 2048, 16),      # a square that fills 256 128 x 128 tiles
 ]
 
 

@@ -267,7 +267,8 @@ def test_bwd_workspace_size():
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(tile=6), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=7), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=6, r=200, ldb=200), rg.LORA_ERR_UNSUPPORTED),
     (dict(tile=-1), rg.LORA_ERR_UNSUPPORTED),
     (dict(tile=0, r=64, ldb=64), rg.LORA_ERR_UNSUPPORTED),     # 64 x 32 tile: r <= 32
     (dict(tile=4, r=100, ldb=100), rg.LORA_ERR_UNSUPPORTED),   # 256 x 256 tile: r <= 64
