@@ -11,12 +11,14 @@ the other shapes of the same path measured in the same run: transformer
 projections (8192 tokens, hidden 2560, r = 32), the 16384 x 8192 x 8192
 square at r in {8, 16, 64, 128}, decode-shaped forwards (M in {1, 8, 64},
 W[4096,4096], rotated over 16 operand sets so the 256 MB last-level cache
-cannot hold them), the merge of 36 layers x 7 targets at r = 32, and the
-backward (dX, dA, dB with W frozen) on the mid-size and q_proj shapes.
+cannot hold them), a decode step through 36 layers' q/k/v and gate/up
+projections (batched against one launch per projection), the merge of 36
+layers x 7 targets at r = 32, and the backward (dX, dA, dB with W frozen)
+on the mid-size and q_proj shapes.
 
 --only NAME runs just one kernel a few times (for rocprofv3); NAME is one of
-tiny, mid, q, v, sq8, sq16, sq64, sq128, dec1, dec8, dec64, merge, copy,
-bwd_mid, bwd_q.
+tiny, mid, q, v, sq8, sq16, sq64, sq128, dec1, dec8, dec64, decstep, merge,
+copy, bwd_mid, bwd_q.
 """
 from __future__ import annotations
 
@@ -203,6 +205,59 @@ def run_merge_pass(rg, steps, warmup, layers=36):
     }
 
 
+def run_decode_step(rg, steps, warmup, layers=36):
+    """One decode token (M = 1) through the projections of 36 layers that read
+    the same input: q, k, v (hidden 2560 -> 4096, 1024, 1024) and gate, up
+    (2560 -> 9728, 9728), rank 32.  Per layer: two lora_fwd_batch calls (one
+    per shared input) against five lora_fwd calls; both captured in HIP graphs
+    (one launch is shorter than the host's per-call cost).  The weights of 36
+    layers (4.7 GB) do not fit the last-level cache."""
+    import torch
+    import synth
+    groups = [("q", "k", "v"), ("gate", "up")]
+    shapes = {n: (o, i) for n, o, i in synth.MERGE_TARGET_SHAPES}
+    r, scale = 32, 2.0
+    layer_items, total_bytes = [], 0
+    for layer in range(layers):
+        items = []
+        for gi, grp in enumerate(groups):
+            K = shapes[grp[0]][1]
+            X = synth.device_normal(9, layer * 2 + gi, synth.TX, (1, K), 1.0, "bf16")
+            for t, name in enumerate(grp):
+                N = shapes[name][0]
+                case = layer * 7 + t + 3 * gi
+                W = synth.device_normal(9, case, synth.TW, (N, K), 1.0 / K, "bf16")
+                A = synth.device_normal(9, case, synth.TA, (r, K), 1.0 / K, "bf16")
+                B = synth.device_normal(9, case, synth.TB, (N, r), 0.02, "bf16")
+                Y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+                items.append((gi, (X, W, A, B, scale, Y)))
+                total_bytes += 2 * (K + N * K + r * K + N * r + N)
+        layer_items.append(items)
+
+    def batched(_):
+        for items in layer_items:
+            for gi in range(len(groups)):
+                rg.fwd_batch([it for g, it in items if g == gi])
+
+    def single(_):
+        for items in layer_items:
+            for _, (X, W, A, B, sc, Y) in items:
+                rg.fwd(X, W, A, B, sc, out=Y)
+
+    b_ms = graph_region(batched, 1, steps, warmup)
+    s_ms = graph_region(single, 1, steps, warmup)
+    return {
+        "workload": f"decode_step_{layers}_layers_qkv_gateup_m1_r32",
+        "timing": "hip graph of one decode step (all layers), replayed",
+        "step_us_batched": round(b_ms * 1e3, 2),
+        "step_us_one_launch_per_projection": round(s_ms * 1e3, 2),
+        "launches_per_layer": {"batched": len(groups), "one_per_projection": 5},
+        "gbs": round(total_bytes / (b_ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * total_bytes / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "bytes_per_step": int(total_bytes),
+    }
+
+
 def bwd_flops(c):
     """Algorithmic flops of one backward: dY W (2 M N K), G = dY B and
     dB = s dY^T T (2 M N r each), T = X A^T, s G A and dA = s G^T X
@@ -342,6 +397,7 @@ def main():
             work.append(run_fwd_case(rg, c, 10, 2))
         for c in synth.DECODE:
             work.append(run_fwd_case(rg, c, 256, 32, rotate=16, graph=True))
+        work.append(run_decode_step(rg, 10, 2))
         work.append(run_merge_pass(rg, 5, 1))
         for c in (synth.MID, synth.QPROJ):
             work.append(run_bwd_case(rg, c, 20, 3))
@@ -366,6 +422,8 @@ def only(rg, name, steps, warmup):
         res = run_fwd_case(rg, c, steps, warmup, rotate=16 if dec else 1, graph=dec)
     elif name == "merge":
         res = run_merge_pass(rg, steps, warmup)
+    elif name == "decstep":
+        res = run_decode_step(rg, steps, warmup)
     elif name in ("bwd_mid", "bwd_q"):
         res = run_bwd_case(rg, synth.MID if name == "bwd_mid" else synth.QPROJ, steps, warmup)
     elif name == "copy":

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 5
+#define LORA_ABI_VERSION 6
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -123,6 +123,45 @@ int lora_fwd_variant(int variant, int dtype, int64_t M, int64_t N, int64_t K, in
                      const void *X, int64_t ldx, const void *W, int64_t ldw,
                      const void *A, int64_t lda, const void *B, int64_t ldb,
                      float scale, void *Y, int64_t ldy, void *stream);
+
+/*
+ * lora_fwd_batch -- several independent forwards in few launches.
+ *   [fastaf], "FWD kernel speedup": on small workloads the launch overhead
+ *   outweighs the work; a decode step's projections that read the same
+ *   tokens (q, k, v; gate, up) are such workloads.
+ *
+ * Element t of descs describes one forward exactly as the arguments of
+ * lora_fwd do; each Y is bitwise what lora_fwd would write.  Consecutive
+ * forwards that lora_fwd would run on the decode kernel (bf16,
+ * M <= LORA_DECODE_AUTO_M, r <= 32) with the same M and rank class
+ * (r <= 16, or 16 < r <= 32) share launches, up to 24 per launch, their
+ * descriptors passed as kernel arguments (nothing is allocated); every other
+ * forward is launched as lora_fwd would launch it.  Forwards run
+ * concurrently, so every Y must also not overlap any other forward's X, W,
+ * A, B or Y (LORA_ERR_ALIAS); inputs may be shared.
+ *
+ *   dtype         LORA_F32 or LORA_BF16, for every forward.
+ *   count         number of descriptors, >= 0 (0: no-op).
+ *   descs         HOST array of count descriptors, read during the call only.
+ *   stream        hipStream_t as void*.
+ * Returns a lora_status; on any invalid descriptor nothing is launched.
+ */
+typedef struct lora_fwd_desc {
+    int64_t M, N, K, r;
+    const void *X;
+    int64_t ldx;
+    const void *W;
+    int64_t ldw;
+    const void *A;
+    int64_t lda;
+    const void *B;
+    int64_t ldb;
+    float scale;
+    void *Y;
+    int64_t ldy;
+} lora_fwd_desc;
+
+int lora_fwd_batch(int dtype, int count, const lora_fwd_desc *descs, void *stream);
 
 /*
  * lora_merge -- merge from pristine   [unsloth], addmm refresh entry.

@@ -8,6 +8,7 @@ loaded, the first call raises.
     Y = fwd(X, W, A, B, scale)          # X W^T + scale * (X A^T) B^T
     merge(W0, B, A, scale, out=W_inf)   # W_inf = W0 + scale * B A, W0 untouched
     merge_batch([(W0, B, A, scale, W_inf), ...])   # many targets, few launches
+    fwd_batch([(X, W, A, B, scale, Y), ...])       # independent forwards, few launches
     merge_inplace(W, B, A, scale)       # W += scale * B A in place (not bit-reversible)
     dX, dA, dB = bwd(X, W, A, B, dY, scale)   # gradients with W frozen (bf16)
     Y = fwd(X, W, A, B, scale, tile=4)   # one tile configuration (see tune.py)
@@ -49,7 +50,7 @@ TILE_COUNT = 7
 EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch",
            "lora_merge_inplace", "lora_status_str", "lora_abi_version", "lora_fwd_pick",
            "lora_bwd", "lora_bwd_workspace_size", "lora_tile_get_info", "lora_tile_get_usage",
-           "lora_get_device_limits", "lora_fwd_tile")
+           "lora_get_device_limits", "lora_fwd_tile", "lora_fwd_batch")
 
 
 class MergeDesc(ctypes.Structure):
@@ -61,6 +62,16 @@ class MergeDesc(ctypes.Structure):
                 ("scale", ctypes.c_float),
                 ("W_inf", ctypes.c_void_p), ("ldwi", ctypes.c_int64)]
 
+
+
+class FwdDesc(ctypes.Structure):
+    """lora_fwd_desc of include/lora.h."""
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("r", ctypes.c_int64), ("X", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+                ("W", ctypes.c_void_p), ("ldw", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("lda", ctypes.c_int64),
+                ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("Y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
 
 
 class TileInfo(ctypes.Structure):
@@ -129,6 +140,8 @@ def lib() -> ctypes.CDLL:
     L.lora_get_device_limits.restype = i32
     L.lora_fwd_tile.argtypes = [i32] + L.lora_fwd.argtypes
     L.lora_fwd_tile.restype = i32
+    L.lora_fwd_batch.argtypes = [i32, i32, ctypes.POINTER(FwdDesc), vp]
+    L.lora_fwd_batch.restype = i32
     _lib = L
     return L
 
@@ -172,6 +185,13 @@ def merge_inplace_raw(dtype: int, N: int, K: int, r: int, W: int, ldw: int, B: i
     """lora_merge_inplace with integer addresses; returns the lora_status."""
     return int(lib().lora_merge_inplace(dtype, N, K, r, W, ldw, B, ldb, A, lda, scale,
                                         stream or None))
+
+
+def fwd_batch_raw(dtype: int, descs, stream: int = 0) -> int:
+    """lora_fwd_batch over a sequence of FwdDesc (or an array of them)."""
+    if not isinstance(descs, ctypes.Array):
+        descs = (FwdDesc * len(descs))(*descs)
+    return int(lib().lora_fwd_batch(dtype, len(descs), descs, stream or None))
 
 
 def merge_batch_raw(dtype: int, descs, stream: int = 0) -> int:
@@ -292,6 +312,34 @@ def fwd(X, W, A, B, scale: float, out=None, variant: str = "auto", tile: Optiona
                  float(scale), py, ldy, _stream(X.device))
     _check(st, "lora_fwd")
     return out
+
+
+def fwd_batch(items):
+    """Several independent forwards in few launches: ``items`` is a sequence of
+    ``(X, W, A, B, scale, Y)``; each ``Y`` is written as ``fwd`` would write
+    it.  All tensors share one dtype and device."""
+    if not items:
+        return
+    dt = _dtype_code(items[0][0])
+    dev = items[0][0].device
+    descs = (FwdDesc * len(items))()
+    for i, (X, W, A, B, scale, Y) in enumerate(items):
+        M, K = X.shape
+        N, r = W.shape[0], A.shape[0]
+        if (W.shape[1] != K or A.shape[1] != K or tuple(B.shape) != (N, r)
+                or tuple(Y.shape) != (M, N)):
+            raise ValueError(f"forward {i}: shape mismatch X{tuple(X.shape)} W{tuple(W.shape)} "
+                             f"A{tuple(A.shape)} B{tuple(B.shape)} Y{tuple(Y.shape)}")
+        for t, nm in ((X, "X"), (W, "W"), (A, "A"), (B, "B"), (Y, "Y")):
+            if _dtype_code(t) != dt or t.device != dev:
+                raise ValueError(f"forward {i}: {nm} must match the first X in dtype and device")
+        px, ldx = _mat(X, "X")
+        pw, ldw = _mat(W, "W")
+        pa, lda = _mat(A, "A")
+        pb, ldb = _mat(B, "B")
+        py, ldy = _mat(Y, "Y")
+        descs[i] = FwdDesc(M, N, K, r, px, ldx, pw, ldw, pa, lda, pb, ldb, float(scale), py, ldy)
+    _check(fwd_batch_raw(dt, descs, _stream(dev)), "lora_fwd_batch")
 
 
 _tile_cache = None

@@ -367,4 +367,54 @@ int lora_fwd_tile(int tile, int dtype, int64_t M, int64_t N, int64_t K, int64_t 
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (count < 0) return LORA_ERR_SHAPE;
+  if (count == 0) return LORA_OK;
+  if (descs == nullptr) return LORA_ERR_NULL;
+  const int64_t e = esize(dtype);
+  std::vector<lora::FwdArgs> work;
+  work.reserve(count);
+  for (int i = 0; i < count; ++i) {
+    const lora_fwd_desc& d = descs[i];
+    const int st = check_fwd(dtype, d.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda, d.B,
+                             d.ldb, d.Y, d.ldy);
+    if (st != LORA_OK) return st;
+    if (d.M == 0 || d.N == 0) continue;
+    work.push_back({d.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda, d.B, d.ldb, d.scale,
+                    d.Y, d.ldy});
+  }
+  // Every output against every other forward's inputs and output.
+  for (size_t i = 0; i < work.size(); ++i) {
+    const lora::FwdArgs& a = work[i];
+    const Range y = span(a.Y, a.M, a.N, a.ldy, e);
+    for (size_t j = 0; j < work.size(); ++j) {
+      if (j == i) continue;
+      const lora::FwdArgs& b = work[j];
+      if (overlap(y, span(b.X, b.M, b.K, b.ldx, e)) || overlap(y, span(b.W, b.N, b.K, b.ldw, e)) ||
+          overlap(y, span(b.A, b.r, b.K, b.lda, e)) || overlap(y, span(b.B, b.N, b.r, b.ldb, e)) ||
+          overlap(y, span(b.Y, b.M, b.N, b.ldy, e)))
+        return LORA_ERR_ALIAS;
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  size_t i = 0;
+  while (i < work.size() && err == hipSuccess) {
+    const lora::FwdArgs& a = work[i];
+    if (pick(dtype, a.M, a.r) == LORA_VARIANT_DECODE) {
+      size_t j = i + 1;
+      while (j < work.size() && pick(dtype, work[j].M, work[j].r) == LORA_VARIANT_DECODE &&
+             work[j].M == a.M && (work[j].r <= 16) == (a.r <= 16))
+        ++j;
+      err = lora::launch_fwd_decode_bf16_batch(&work[i], (int)(j - i), s);
+      i = j;
+    } else {
+      err = dtype == LORA_F32 ? lora::launch_fwd_tiled_f32(a, s) : lora::launch_fwd_tiled_bf16(a, s);
+      ++i;
+    }
+  }
+  return err == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -56,19 +56,18 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// One workgroup's work: output columns [n0, n0 + 16) of one forward.
 template <int MB, int RB, int U, int NW, bool AL, bool XL>
-__global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
+__device__ __forceinline__ void dec_body(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
-    int64_t ldy, int b_vec) {
+    int64_t ldy, int b_vec, int n0, unsigned char* smem) {
   using C = Dec<MB, RB, U, NW, AL, XL>;
   constexpr int RP = C::RP;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16;
 
   // Lanes of rows past N (or M) read row N - 1 (M - 1) again: those MFMA
   // rows and columns are never stored, and the repeated addresses cost no
@@ -273,6 +272,83 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
   }
 }
 
+template <int MB, int RB, int U, int NW, bool AL, bool XL>
+__global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
+    int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
+    const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
+    const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
+    int64_t ldy, int b_vec) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  dec_body<MB, RB, U, NW, AL, XL>(M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, scale, Y, ldy, b_vec,
+                                  blockIdx.x * 16, smem);
+}
+
+// Batched decode: up to kDecBatch forwards with the same M and rank class per
+// launch, their descriptors in the kernel arguments (no device memory).
+// Workgroups [first[t], first[t + 1]) belong to forward t; a workgroup finds
+// its forward by a uniform binary search.
+constexpr int kDecBatch = 24;
+struct DecDesc {
+  const uint16_t* X;
+  const uint16_t* W;
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* Y;
+  int64_t ldx, ldw, lda, ldb, ldy;
+  int N, K, r, b_vec;
+  float scale;
+};
+struct DecBatch {
+  int count, M;
+  int first[kDecBatch + 1];
+  DecDesc d[kDecBatch];
+};
+
+template <int MB, int RB, int U, int NW, bool AL, bool XL>
+__global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_batch_kernel(const DecBatch args) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int b = blockIdx.x;
+  int lo = 0, hi = args.count - 1;  // last t with first[t] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (args.first[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  const DecDesc& d = args.d[lo];
+  dec_body<MB, RB, U, NW, AL, XL>(args.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda, d.B,
+                                  d.ldb, d.scale, d.Y, d.ldy, d.b_vec,
+                                  (b - args.first[lo]) * 16, smem);
+}
+
+inline int dec_b_vec(const FwdArgs& a) {
+  return ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0);
+}
+
+// The forwards a[i0, i1) (same M, same rank class) in one launch.
+template <int MB, int RB, int U, bool AL, bool XL>
+hipError_t launch_dec_batch(const FwdArgs* a, int i0, int i1, hipStream_t s) {
+  constexpr int NW = 8;
+  using C = Dec<MB, RB, U, NW, AL, XL>;
+  auto kern = fwd_decode_bf16_batch_kernel<MB, RB, U, NW, AL, XL>;
+  static std::atomic<uint64_t> attr_done{0};
+  if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
+  DecBatch bt{};
+  bt.count = i1 - i0;
+  bt.M = (int)a[i0].M;
+  int blocks = 0;
+  for (int t = 0; t < bt.count; ++t) {
+    const FwdArgs& f = a[i0 + t];
+    bt.first[t] = blocks;
+    bt.d[t] = DecDesc{static_cast<const uint16_t*>(f.X), static_cast<const uint16_t*>(f.W),
+                      static_cast<const uint16_t*>(f.A), static_cast<const uint16_t*>(f.B),
+                      static_cast<uint16_t*>(f.Y), f.ldx, f.ldw, f.lda, f.ldb, f.ldy,
+                      (int)f.N, (int)f.K, (int)f.r, dec_b_vec(f), f.scale};
+    blocks += (int)((f.N + 15) / 16);
+  }
+  bt.first[bt.count] = blocks;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), C::kLds, s, bt);
+  return hipGetLastError();
+}
+
 template <int MB, int RB, int U, bool AL = false, bool XL = false>
 hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = 8;
@@ -281,7 +357,7 @@ hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
   static std::atomic<uint64_t> attr_done{0};
   if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   const int blocks = (int)((a.N + 15) / 16);
-  const int b_vec = ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0);
+  const int b_vec = dec_b_vec(a);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), C::kLds, s, (int)a.M, (int)a.N, (int)a.K,
                      (int)a.r, static_cast<const uint16_t*>(a.X), a.ldx,
                      static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
@@ -292,24 +368,42 @@ hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
 
 // Blocks per round: the loads of a round (16 U (1 + RB + MB) VGPRs) stay
 // within about 200 registers.
+// (One template choice for a single forward and for a batch of forwards
+// with the same M and rank class: batch = nullptr launches a alone.)
 template <int RB>
-hipError_t launch_dec_rb(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_dec_rb(const FwdArgs& a, const FwdArgs* batch, int i0, int i1, hipStream_t s) {
+#define LORA_DEC(MB, U, AL, XL)                                                    \
+  return batch ? launch_dec_batch<MB, RB, U, AL, XL>(batch, i0, i1, s)             \
+               : launch_dec<MB, RB, U, AL, XL>(a, s)
   switch ((a.M + 15) / 16) {
     case 1:
       if constexpr (RB == 1) {
-        if (a.M == 1) return launch_dec<1, 1, 4, true, true>(a, s);
+        if (a.M == 1) LORA_DEC(1, 4, true, true);
       }
-      return launch_dec<1, RB, RB == 1 ? 4 : 2, true, false>(a, s);
-    case 2: return launch_dec<2, RB, 2>(a, s);
-    case 3: return launch_dec<3, RB, RB == 1 ? 2 : 1>(a, s);
-    default: return launch_dec<4, RB, RB == 1 ? 2 : 1>(a, s);
+      LORA_DEC(1, (RB == 1 ? 4 : 2), true, false);
+    case 2: LORA_DEC(2, 2, false, false);
+    case 3: LORA_DEC(3, (RB == 1 ? 2 : 1), false, false);
+    default: LORA_DEC(4, (RB == 1 ? 2 : 1), false, false);
   }
+#undef LORA_DEC
 }
 
 }  // namespace
 
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s) {
-  return a.r <= 16 ? launch_dec_rb<1>(a, s) : launch_dec_rb<2>(a, s);
+  return a.r <= 16 ? launch_dec_rb<1>(a, nullptr, 0, 0, s) : launch_dec_rb<2>(a, nullptr, 0, 0, s);
+}
+
+// Forwards a[0, count): same M (<= LORA_DECODE_MAX_M) and the same rank class
+// (r <= 16, or 16 < r <= 32); kDecBatch at a time.
+hipError_t launch_fwd_decode_bf16_batch(const FwdArgs* a, int count, hipStream_t s) {
+  for (int i = 0; i < count; i += kDecBatch) {
+    const int j = i + kDecBatch < count ? i + kDecBatch : count;
+    const hipError_t e = a[i].r <= 16 ? launch_dec_rb<1>(a[i], a, i, j, s)
+                                      : launch_dec_rb<2>(a[i], a, i, j, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace lora

@@ -33,7 +33,7 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 5
+    assert rg.abi_version() == 6
     for s in range(10):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
@@ -285,3 +285,39 @@ def test_fwd_tile_rejects_before_any_hip_call(kw, want):
     assert rg.fwd_tile_raw(a["tile"], a["dtype"], a["M"], a["N"], a["K"], a["r"], a["X"], a["ldx"],
                            a["W"], a["ldw"], a["A"], a["lda"], a["B"], a["ldb"], a["scale"],
                            a["Y"], a["ldy"]) == want
+
+
+def _fdesc(**kw):
+    a = dict(M=1, N=64, K=64, r=16, X=PX, ldx=64, W=PW, ldw=64, A=PA, lda=64, B=PB, ldb=16,
+             scale=2.0, Y=PY, ldy=64)
+    a.update(kw)
+    return rg.FwdDesc(a["M"], a["N"], a["K"], a["r"], a["X"], a["ldx"], a["W"], a["ldw"], a["A"],
+                      a["lda"], a["B"], a["ldb"], a["scale"], a["Y"], a["ldy"])
+
+
+# A second forward sharing X (as q and k do), with its own W, A, B, Y.
+SECOND_FWD = dict(W=PX + 0x100000, A=PX + 0x200000, B=PX + 0x300000, Y=PX + 0x400000)
+
+
+@pytest.mark.parametrize("descs,want", [
+    ([_fdesc(r=0)], rg.LORA_ERR_SHAPE),
+    ([_fdesc(), _fdesc(**SECOND_FWD, ldy=8)], rg.LORA_ERR_STRIDE),
+    ([_fdesc(), _fdesc(**{**SECOND_FWD, "W": PX + 0x100002})], rg.LORA_ERR_ALIGN),
+    ([_fdesc(Y=PX)], rg.LORA_ERR_ALIAS),                                   # own input
+    ([_fdesc(), _fdesc(**{**SECOND_FWD, "W": PY})], rg.LORA_ERR_ALIAS),    # Y of 0 is W of 1
+    ([_fdesc(), _fdesc(**{**SECOND_FWD, "Y": PY + 64})], rg.LORA_ERR_ALIAS),  # outputs overlap
+    ([_fdesc(), _fdesc(**{**SECOND_FWD, "X": PY})], rg.LORA_ERR_ALIAS),    # Y of 0 is X of 1
+])
+def test_fwd_batch_rejects_before_any_hip_call(descs, want):
+    assert rg.fwd_batch_raw(rg.LORA_BF16, descs) == want
+
+
+def test_fwd_batch_argument_checks():
+    assert rg.fwd_batch_raw(rg.LORA_BF16, []) == rg.LORA_OK
+    assert rg.fwd_batch_raw(9, [_fdesc()]) == rg.LORA_ERR_DTYPE
+    L = rg.lib()
+    assert L.lora_fwd_batch(rg.LORA_BF16, -1, None, None) == rg.LORA_ERR_SHAPE
+    assert L.lora_fwd_batch(rg.LORA_BF16, 3, None, None) == rg.LORA_ERR_NULL
+    # empty forwards are skipped, whatever their pointers
+    assert rg.fwd_batch_raw(rg.LORA_BF16, [_fdesc(M=0, X=0, Y=0), _fdesc(N=0, W=0, B=0)]) == \
+        rg.LORA_OK
