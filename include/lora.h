@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 6
+#define LORA_ABI_VERSION 7
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -140,9 +140,23 @@ int lora_fwd_variant(int variant, int dtype, int64_t M, int64_t N, int64_t K, in
  * concurrently, so every Y must also not overlap any other forward's X, W,
  * A, B or Y (LORA_ERR_ALIAS); inputs may be shared.
  *
+ * With a workspace, each launch of batched decode forwards is preceded by a
+ * small launch that computes T = X A^T once per forward (A is then read once
+ * instead of once per 16 output columns, and the weight stream keeps four
+ * 128-deep K blocks per wave in flight at any rank).  For r <= 16 the results
+ * are still bitwise lora_fwd's (same partition of K, same summation order);
+ * for 16 < r <= 32 the weight stream is partitioned differently and Y
+ * differs from lora_fwd's by fp32 rounding order only (deterministic all the
+ * same).
+ *
  *   dtype         LORA_F32 or LORA_BF16, for every forward.
  *   count         number of descriptors, >= 0 (0: no-op).
  *   descs         HOST array of count descriptors, read during the call only.
+ *   workspace     NULL, or device scratch of workspace_bytes >=
+ *                 lora_fwd_batch_workspace_size(count), 256-byte aligned,
+ *                 not overlapping any operand; content ignored on entry,
+ *                 unspecified on return; calls in flight at the same time
+ *                 need separate workspaces.
  *   stream        hipStream_t as void*.
  * Returns a lora_status; on any invalid descriptor nothing is launched.
  */
@@ -161,7 +175,12 @@ typedef struct lora_fwd_desc {
     int64_t ldy;
 } lora_fwd_desc;
 
-int lora_fwd_batch(int dtype, int count, const lora_fwd_desc *descs, void *stream);
+int lora_fwd_batch(int dtype, int count, const lora_fwd_desc *descs, void *workspace,
+                   int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes lora_fwd_batch can use for count forwards (16 KiB each),
+ * or -1 for count < 0. */
+int64_t lora_fwd_batch_workspace_size(int count);
 
 /*
  * lora_merge -- merge from pristine   [unsloth], addmm refresh entry.

@@ -367,11 +367,19 @@ int lora_fwd_tile(int tile, int dtype, int64_t M, int64_t N, int64_t K, int64_t 
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
-int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* stream) {
+int64_t lora_fwd_batch_workspace_size(int count) {
+  return count < 0 ? -1 : (int64_t)count * lora::kDecTpBytes;
+}
+
+int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
   if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
   if (count < 0) return LORA_ERR_SHAPE;
   if (count == 0) return LORA_OK;
   if (descs == nullptr) return LORA_ERR_NULL;
+  if (workspace != nullptr && (workspace_bytes < (int64_t)count * lora::kDecTpBytes ||
+                               (reinterpret_cast<uintptr_t>(workspace) & 255)))
+    return LORA_ERR_WORKSPACE;
   const int64_t e = esize(dtype);
   std::vector<lora::FwdArgs> work;
   work.reserve(count);
@@ -384,10 +392,18 @@ int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* strea
     work.push_back({d.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda, d.B, d.ldb, d.scale,
                     d.Y, d.ldy});
   }
-  // Every output against every other forward's inputs and output.
+  // Every output against every other forward's inputs and output, and the
+  // workspace against every operand.
+  const Range wsr{reinterpret_cast<uintptr_t>(workspace),
+                  reinterpret_cast<uintptr_t>(workspace) +
+                      (workspace ? (uintptr_t)count * lora::kDecTpBytes : 0)};
   for (size_t i = 0; i < work.size(); ++i) {
     const lora::FwdArgs& a = work[i];
     const Range y = span(a.Y, a.M, a.N, a.ldy, e);
+    if (overlap(wsr, y) || overlap(wsr, span(a.X, a.M, a.K, a.ldx, e)) ||
+        overlap(wsr, span(a.W, a.N, a.K, a.ldw, e)) || overlap(wsr, span(a.A, a.r, a.K, a.lda, e)) ||
+        overlap(wsr, span(a.B, a.N, a.r, a.ldb, e)))
+      return LORA_ERR_ALIAS;
     for (size_t j = 0; j < work.size(); ++j) {
       if (j == i) continue;
       const lora::FwdArgs& b = work[j];
@@ -407,7 +423,9 @@ int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* strea
       while (j < work.size() && pick(dtype, work[j].M, work[j].r) == LORA_VARIANT_DECODE &&
              work[j].M == a.M && (work[j].r <= 16) == (a.r <= 16))
         ++j;
-      err = lora::launch_fwd_decode_bf16_batch(&work[i], (int)(j - i), s);
+      unsigned char* tws =
+          workspace ? static_cast<unsigned char*>(workspace) + i * lora::kDecTpBytes : nullptr;
+      err = lora::launch_fwd_decode_bf16_batch(&work[i], (int)(j - i), tws, s);
       i = j;
     } else {
       err = dtype == LORA_F32 ? lora::launch_fwd_tiled_f32(a, s) : lora::launch_fwd_tiled_bf16(a, s);

@@ -34,12 +34,12 @@ constexpr uint32_t kDecOob = 0x80000000u;  // offset past any resource's range
 // wave stages the rows of its own K range with 16-B-per-lane DMA loads
 // (buffer_load ... lds), whole 128-B lines per instruction, instead of
 // 16-row x 64-B register loads; the MFMA fragments are then read from LDS.
-template <int MB, int RB, int U, int NW, bool AL, bool XL>
+template <int MB, int RB, int U, int NW, bool AL, bool XL, bool TP = false>
 struct Dec {
   static constexpr int RP = RB * 16;
   static constexpr int kRowB = U * 256;                   // bytes of a staged row per round
   static constexpr int kChunks = U * 16;                  // 16-B chunks per staged row
-  static constexpr int kAB = AL ? NW * RP * kRowB : 0;    // per-wave A regions
+  static constexpr int kAB = AL && !TP ? NW * RP * kRowB : 0;  // per-wave A regions
   static constexpr int kXB = XL ? NW * kRowB : 0;         // per-wave X row
   static constexpr int kSlots = MB * (1 + RB);            // f32x4 partials per lane
   static constexpr int kRedB = NW * kSlots * kWave * 16;  // LDS for the reduction
@@ -57,13 +57,16 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 // One workgroup's work: output columns [n0, n0 + 16) of one forward.
-template <int MB, int RB, int U, int NW, bool AL, bool XL>
+// TP: T = X A^T was computed beforehand (tp: the NW per-wave partial sums,
+// as dec_t_kernel writes them); A is neither loaded nor multiplied here.
+template <int MB, int RB, int U, int NW, bool AL, bool XL, bool TP = false>
 __device__ __forceinline__ void dec_body(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
-    int64_t ldy, int b_vec, int n0, unsigned char* smem) {
-  using C = Dec<MB, RB, U, NW, AL, XL>;
+    int64_t ldy, int b_vec, int n0, unsigned char* smem, const f32x4* __restrict__ tp = nullptr) {
+  static_assert(!TP || MB == 1, "precomputed T: one 16-row block of tokens");
+  using C = Dec<MB, RB, U, NW, AL, XL, TP>;
   constexpr int RP = C::RP;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,7 +140,7 @@ __device__ __forceinline__ void dec_body(
       // 1024 / kRowB rows, lane i writing slot i % kChunks.
       constexpr int kRowsPerDma = 1024 / C::kRowB;
 #pragma unroll
-      for (int d = 0; d < RP / kRowsPerDma; ++d) {
+      for (int d = 0; d < (TP ? 0 : RP / kRowsPerDma); ++d) {
         const int j = d * kRowsPerDma + lane / C::kChunks;
         const int c = (lane % C::kChunks) ^ (j & 15);
         const int k = kbw * 128 + c * 8;
@@ -167,8 +170,10 @@ __device__ __forceinline__ void dec_body(
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) x[u][mb][q] = bload(rx, xbase[mb] + off[u][q]);
+          if constexpr (!TP) {
 #pragma unroll
-          for (int jb = 0; jb < RB; ++jb) a[u][jb][q] = bload(ra, abase[jb] + off[u][q]);
+            for (int jb = 0; jb < RB; ++jb) a[u][jb][q] = bload(ra, abase[jb] + off[u][q]);
+          }
         }
     }
 #pragma unroll
@@ -189,22 +194,24 @@ __device__ __forceinline__ void dec_body(
         for (int q = 0; q < 4; ++q) {
           const int c = u * 16 + q * 4 + lg;
 #pragma unroll
-          for (int jb = 0; jb < RB; ++jb) {
+          for (int jb = 0; jb < (TP ? 0 : RB); ++jb) {
             const int j = jb * 16 + lrow;
             a[u][jb][q] = *reinterpret_cast<const u32x4*>(as + j * C::kRowB + ((c ^ lrow) << 4));
           }
           if constexpr (XL) x[u][0][q] = *reinterpret_cast<const u32x4*>(xs + (c << 4));
         }
     }
+    if constexpr (!TP) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int jb = 0; jb < RB; ++jb)
-            tacc[mb][jb] = mfma16x16x32(x[u][mb][q], a[u][jb][q], tacc[mb][jb]);
+            for (int jb = 0; jb < RB; ++jb)
+              tacc[mb][jb] = mfma16x16x32(x[u][mb][q], a[u][jb][q], tacc[mb][jb]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -235,7 +242,13 @@ __device__ __forceinline__ void dec_body(
     for (int w = 0; w < NW; ++w) {
       y += red[(w * C::kSlots + mb * (1 + RB)) * kWave + lane];
 #pragma unroll
-      for (int jb = 0; jb < RB; ++jb) t[jb] += red[(w * C::kSlots + mb * (1 + RB) + 1 + jb) * kWave + lane];
+      for (int jb = 0; jb < RB; ++jb) {
+        if constexpr (TP) {
+          t[jb] += tp[(w * RB + jb) * kWave + lane];  // the same order as below
+        } else {
+          t[jb] += red[(w * C::kSlots + mb * (1 + RB) + 1 + jb) * kWave + lane];
+        }
+      }
     }
     // T rows of this M block to LDS (accumulator layout: lane holds column
     // j = 16 jb + l % 16 of rows 4 (l / 16) + q).
@@ -294,6 +307,7 @@ struct DecDesc {
   const uint16_t* A;
   const uint16_t* B;
   uint16_t* Y;
+  f32x4* tp;  // with a workspace: this forward's T partial sums (kDecTpBytes)
   int64_t ldx, ldw, lda, ldb, ldy;
   int N, K, r, b_vec;
   float scale;
@@ -304,7 +318,56 @@ struct DecBatch {
   DecDesc d[kDecBatch];
 };
 
-template <int MB, int RB, int U, int NW, bool AL, bool XL>
+// T = X A^T of every forward of a batch, as the NW waves of dec_body with
+// the same U would accumulate it: workgroup (t, w) is one wave doing exactly
+// wave w's part (its 128-deep K blocks kbw = (round NW + w) U + u, the same
+// X and A operands, the same MFMA order) and stores its accumulators; the
+// batch kernel adds the NW partials in wave order, as its LDS reduction
+// does.  A is read once per forward instead of once per 16 rows of W.
+template <int RB, int U>
+__global__ __launch_bounds__(64) void dec_t_kernel(const DecBatch args) {
+  constexpr int NW = 8;
+  const int t = blockIdx.x / NW, w = blockIdx.x % NW;
+  const DecDesc& d = args.d[t];
+  const int lane = threadIdx.x, lrow = lane & 15, lg = lane >> 4;
+  const int M = args.M, K = d.K, r = d.r;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)d.X, 0, (int)(M * d.ldx * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)d.A, 0, (int)(r * d.lda * 2), 0x00020000);
+  const uint32_t lane_k = lg * 16;
+  const uint32_t xbase = min(lrow, M - 1) * (uint32_t)d.ldx * 2 + lane_k;
+  uint32_t abase[RB];
+#pragma unroll
+  for (int jb = 0; jb < RB; ++jb) abase[jb] = (jb * 16 + lrow) * (uint32_t)d.lda * 2 + lane_k;
+  f32x4 tacc[RB];
+#pragma unroll
+  for (int jb = 0; jb < RB; ++jb) tacc[jb] = zero4();
+  const int nkb = (K + 127) >> 7;
+  for (int kbw = w * U; kbw < nkb; kbw += NW * U) {
+    u32x4 x[U][4], a[U][RB][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kb = kbw + u, k = kb * 128 + q * 32 + lg * 8;
+        const uint32_t off = k < K ? (uint32_t)(kb * 256 + q * 64) : kDecOob;
+        x[u][q] = bload(rx, xbase + off);
+#pragma unroll
+        for (int jb = 0; jb < RB; ++jb) a[u][jb][q] = bload(ra, abase[jb] + off);
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int jb = 0; jb < RB; ++jb) tacc[jb] = mfma16x16x32(x[u][q], a[u][jb][q], tacc[jb]);
+  }
+#pragma unroll
+  for (int jb = 0; jb < RB; ++jb) d.tp[(w * RB + jb) * kWave + lane] = tacc[jb];
+}
+
+template <int MB, int RB, int U, int NW, bool AL, bool XL, bool TP>
 __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_batch_kernel(const DecBatch args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int b = blockIdx.x;
@@ -314,23 +377,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_batch_kernel(const De
     if (args.first[mid] <= b) lo = mid; else hi = mid - 1;
   }
   const DecDesc& d = args.d[lo];
-  dec_body<MB, RB, U, NW, AL, XL>(args.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda, d.B,
-                                  d.ldb, d.scale, d.Y, d.ldy, d.b_vec,
-                                  (b - args.first[lo]) * 16, smem);
+  dec_body<MB, RB, U, NW, AL, XL, TP>(args.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda,
+                                      d.B, d.ldb, d.scale, d.Y, d.ldy, d.b_vec,
+                                      (b - args.first[lo]) * 16, smem, d.tp);
 }
 
 inline int dec_b_vec(const FwdArgs& a) {
   return ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0);
 }
 
-// The forwards a[i0, i1) (same M, same rank class) in one launch.
+// The forwards a[i0, i1) (same M, same rank class) in one launch; with a
+// workspace (tws: kDecTpBytes per forward) T first, in a launch of its own.
 template <int MB, int RB, int U, bool AL, bool XL>
-hipError_t launch_dec_batch(const FwdArgs* a, int i0, int i1, hipStream_t s) {
+hipError_t launch_dec_batch(const FwdArgs* a, int i0, int i1, unsigned char* tws, hipStream_t s) {
   constexpr int NW = 8;
   using C = Dec<MB, RB, U, NW, AL, XL>;
-  auto kern = fwd_decode_bf16_batch_kernel<MB, RB, U, NW, AL, XL>;
-  static std::atomic<uint64_t> attr_done{0};
-  if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   DecBatch bt{};
   bt.count = i1 - i0;
   bt.M = (int)a[i0].M;
@@ -338,13 +399,35 @@ hipError_t launch_dec_batch(const FwdArgs* a, int i0, int i1, hipStream_t s) {
   for (int t = 0; t < bt.count; ++t) {
     const FwdArgs& f = a[i0 + t];
     bt.first[t] = blocks;
+    f32x4* tp = tws ? reinterpret_cast<f32x4*>(tws + (size_t)t * kDecTpBytes) : nullptr;
     bt.d[t] = DecDesc{static_cast<const uint16_t*>(f.X), static_cast<const uint16_t*>(f.W),
                       static_cast<const uint16_t*>(f.A), static_cast<const uint16_t*>(f.B),
-                      static_cast<uint16_t*>(f.Y), f.ldx, f.ldw, f.lda, f.ldb, f.ldy,
+                      static_cast<uint16_t*>(f.Y), tp, f.ldx, f.ldw, f.lda, f.ldb, f.ldy,
                       (int)f.N, (int)f.K, (int)f.r, dec_b_vec(f), f.scale};
     blocks += (int)((f.N + 15) / 16);
   }
   bt.first[bt.count] = blocks;
+  if constexpr (MB == 1) {
+    if (tws != nullptr) {
+      // Without A the W stream has the registers of rank 16 at any rank:
+      // four 128-deep blocks per wave per round, A-less LDS staging of X.
+      // (With rank 16 this is the single-forward kernel's own partition, so
+      // the outputs stay bitwise; above it Y differs from it by rounding.)
+      constexpr int UT = 4;
+      using CT = Dec<1, RB, UT, NW, true, XL, true>;
+      static_assert(NW * RB * kWave * 16 <= kDecTpBytes, "T partials fit the workspace slot");
+      hipLaunchKernelGGL((dec_t_kernel<RB, UT>), dim3(bt.count * NW), dim3(64), 0, s, bt);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      auto kern = fwd_decode_bf16_batch_kernel<1, RB, UT, NW, true, XL, true>;
+      static std::atomic<uint64_t> attr_done{0};
+      if (hipError_t e = ensure_lds(kern, CT::kLds, attr_done); e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), CT::kLds, s, bt);
+      return hipGetLastError();
+    }
+  }
+  auto kern = fwd_decode_bf16_batch_kernel<MB, RB, U, NW, AL, XL, false>;
+  static std::atomic<uint64_t> attr_done{0};
+  if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), C::kLds, s, bt);
   return hipGetLastError();
 }
@@ -371,9 +454,10 @@ hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
 // (One template choice for a single forward and for a batch of forwards
 // with the same M and rank class: batch = nullptr launches a alone.)
 template <int RB>
-hipError_t launch_dec_rb(const FwdArgs& a, const FwdArgs* batch, int i0, int i1, hipStream_t s) {
+hipError_t launch_dec_rb(const FwdArgs& a, const FwdArgs* batch, int i0, int i1,
+                         unsigned char* tws, hipStream_t s) {
 #define LORA_DEC(MB, U, AL, XL)                                                    \
-  return batch ? launch_dec_batch<MB, RB, U, AL, XL>(batch, i0, i1, s)             \
+  return batch ? launch_dec_batch<MB, RB, U, AL, XL>(batch, i0, i1, tws, s)        \
                : launch_dec<MB, RB, U, AL, XL>(a, s)
   switch ((a.M + 15) / 16) {
     case 1:
@@ -391,16 +475,19 @@ hipError_t launch_dec_rb(const FwdArgs& a, const FwdArgs* batch, int i0, int i1,
 }  // namespace
 
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s) {
-  return a.r <= 16 ? launch_dec_rb<1>(a, nullptr, 0, 0, s) : launch_dec_rb<2>(a, nullptr, 0, 0, s);
+  return a.r <= 16 ? launch_dec_rb<1>(a, nullptr, 0, 0, nullptr, s)
+                   : launch_dec_rb<2>(a, nullptr, 0, 0, nullptr, s);
 }
 
 // Forwards a[0, count): same M (<= LORA_DECODE_MAX_M) and the same rank class
 // (r <= 16, or 16 < r <= 32); kDecBatch at a time.
-hipError_t launch_fwd_decode_bf16_batch(const FwdArgs* a, int count, hipStream_t s) {
+hipError_t launch_fwd_decode_bf16_batch(const FwdArgs* a, int count, void* tws, hipStream_t s) {
+  unsigned char* w = static_cast<unsigned char*>(tws);
   for (int i = 0; i < count; i += kDecBatch) {
     const int j = i + kDecBatch < count ? i + kDecBatch : count;
-    const hipError_t e = a[i].r <= 16 ? launch_dec_rb<1>(a[i], a, i, j, s)
-                                      : launch_dec_rb<2>(a[i], a, i, j, s);
+    unsigned char* wi = w ? w + (size_t)i * kDecTpBytes : nullptr;
+    const hipError_t e = a[i].r <= 16 ? launch_dec_rb<1>(a[i], a, i, j, wi, s)
+                                      : launch_dec_rb<2>(a[i], a, i, j, wi, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -90,9 +90,13 @@ struct TileProps {
 hipError_t fwd_tile_props(int id, int64_t r, TileProps* out);
 hipError_t launch_fwd_tile_bf16(int id, const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s);
-// Decode forwards with the same M and rank class (r <= 16 or 16 < r <= 32),
-// several per launch; each result is bitwise launch_fwd_decode_bf16's.
-hipError_t launch_fwd_decode_bf16_batch(const FwdArgs* a, int count, hipStream_t s);
+// Decode forwards with the same M (<= 16) and rank class (r <= 16 or
+// 16 < r <= 32), several per launch; each result is bitwise
+// launch_fwd_decode_bf16's.  tws (may be null): kDecTpBytes of device memory
+// per forward, 16-B aligned; with it T = X A^T is computed once per forward
+// in a launch of its own instead of by every workgroup.
+constexpr int kDecTpBytes = 8 * 2 * 64 * 16;  // NW waves x rank blocks (<= 2) x 64 lanes x f32x4
+hipError_t launch_fwd_decode_bf16_batch(const FwdArgs* a, int count, void* tws, hipStream_t s);
 hipError_t launch_merge_bf16(const MergeArgs& a, hipStream_t s);
 hipError_t launch_merge_f32(const MergeArgs& a, hipStream_t s);
 hipError_t launch_merge_bf16_batch(const MergeArgs* a, int count, hipStream_t s);

@@ -33,7 +33,7 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 6
+    assert rg.abi_version() == 7
     for s in range(10):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
@@ -316,8 +316,15 @@ def test_fwd_batch_argument_checks():
     assert rg.fwd_batch_raw(rg.LORA_BF16, []) == rg.LORA_OK
     assert rg.fwd_batch_raw(9, [_fdesc()]) == rg.LORA_ERR_DTYPE
     L = rg.lib()
-    assert L.lora_fwd_batch(rg.LORA_BF16, -1, None, None) == rg.LORA_ERR_SHAPE
-    assert L.lora_fwd_batch(rg.LORA_BF16, 3, None, None) == rg.LORA_ERR_NULL
+    assert L.lora_fwd_batch(rg.LORA_BF16, -1, None, None, 0, None) == rg.LORA_ERR_SHAPE
+    assert L.lora_fwd_batch(rg.LORA_BF16, 3, None, None, 0, None) == rg.LORA_ERR_NULL
+    n = rg.fwd_batch_workspace_size(2)
+    assert n == 2 * rg.fwd_batch_workspace_size(1) > 0 and rg.fwd_batch_workspace_size(-1) == -1
+    two = [_fdesc(), _fdesc(**SECOND_FWD)]
+    WS = 0x70000000
+    assert rg.fwd_batch_raw(rg.LORA_BF16, two, 0, WS, n - 1) == rg.LORA_ERR_WORKSPACE
+    assert rg.fwd_batch_raw(rg.LORA_BF16, two, 0, WS + 16, n) == rg.LORA_ERR_WORKSPACE
+    assert rg.fwd_batch_raw(rg.LORA_BF16, two, 0, PW, n) == rg.LORA_ERR_ALIAS
     # empty forwards are skipped, whatever their pointers
     assert rg.fwd_batch_raw(rg.LORA_BF16, [_fdesc(M=0, X=0, Y=0), _fdesc(N=0, W=0, B=0)]) == \
         rg.LORA_OK

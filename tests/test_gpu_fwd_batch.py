@@ -1,6 +1,7 @@
 """lora_fwd_batch on the GPU: each output bitwise equal to lora_fwd's for the
 same forward (the batched decode launch runs the same kernel code per
-forward), over a mix that exercises the grouping: several decode-shaped
+forward; with a workspace and 16 < r <= 32, equal up to fp32 rounding order),
+over a mix that exercises the grouping: several decode-shaped
 forwards sharing X (different N and K), a change of rank class, a change of
 M, a tiled forward in between, and a ragged last column block; plus parity
 with the oracle and bitwise equal HIP graph replays."""
@@ -25,7 +26,8 @@ def _make(i, M, N, K, r):
     return c, c.make()
 
 
-def test_fwd_batch_equals_fwd(gpu_lib):
+@pytest.mark.parametrize("with_ws", [False, True], ids=["no_workspace", "workspace"])
+def test_fwd_batch_equals_fwd(gpu_lib, with_ws):
     import torch
     rg = gpu_lib
     cases, X = [], None
@@ -36,19 +38,30 @@ def test_fwd_batch_equals_fwd(gpu_lib):
             Xh = t["X"]
         cases.append((c, Xh, X, to_dev(t["W"]), to_dev(t["A"]), to_dev(t["B"]), t))
     outs = [torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda") for c, *_ in cases]
-    rg.fwd_batch([(X, W, A, B, c.scale, Y) for (c, _, X, W, A, B, _), Y in zip(cases, outs)])
+    ws = None
+    if with_ws:  # garbage content: the kernels must not depend on it
+        ws = torch.full((rg.fwd_batch_workspace_size(len(cases)),), 0xFF, dtype=torch.uint8,
+                        device="cuda")
+    rg.fwd_batch([(X, W, A, B, c.scale, Y) for (c, _, X, W, A, B, _), Y in zip(cases, outs)],
+                 workspace=ws)
     torch.cuda.synchronize()
     for (c, Xh, X, W, A, B, t), Y in zip(cases, outs):
         single = to_host(rg.fwd(X, W, A, B, c.scale))
         got = to_host(Y)
-        assert np.array_equal(got, single), c.name
+        if with_ws and c.M <= 16 and c.r > 16:
+            # the weight stream runs four K blocks per wave here (two in
+            # lora_fwd at this rank): same values up to fp32 rounding order
+            assert rel_fro(as_f64(got), as_f64(single)) <= 1e-3, c.name
+        else:
+            assert np.array_equal(got, single), c.name
         ref = oracle.fwd(Xh, t["W"], t["A"], t["B"], c.scale)
         err = rel_fro(as_f64(got), ref)
         print(f"{c.name} M{c.M} N{c.N} K{c.K} r{c.r}: rel_fro={err:.3e}")
         assert err <= TOL["bf16"]
 
 
-def test_fwd_batch_graph_replays(gpu_lib):
+@pytest.mark.parametrize("with_ws", [False, True], ids=["no_workspace", "workspace"])
+def test_fwd_batch_graph_replays(gpu_lib, with_ws):
     import torch
     rg = gpu_lib
     items, outs = [], []
@@ -57,7 +70,9 @@ def test_fwd_batch_graph_replays(gpu_lib):
         Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         items.append((to_dev(t["X"]), to_dev(t["W"]), to_dev(t["A"]), to_dev(t["B"]), c.scale, Y))
         outs.append(Y)
-    rg.fwd_batch(items)
+    ws = (torch.empty((rg.fwd_batch_workspace_size(len(items)),), dtype=torch.uint8, device="cuda")
+          if with_ws else None)
+    rg.fwd_batch(items, workspace=ws)
     torch.cuda.synchronize()
     eager = [to_host(Y) for Y in outs]
     g = torch.cuda.CUDAGraph()
@@ -65,7 +80,7 @@ def test_fwd_batch_graph_replays(gpu_lib):
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            rg.fwd_batch(items)
+            rg.fwd_batch(items, workspace=ws)
     torch.cuda.synchronize()
     for rep in range(3):
         for Y in outs:
