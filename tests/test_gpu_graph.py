@@ -73,3 +73,32 @@ def test_merge_batch_graph_replay(gpu_lib):
         gpu_lib.merge_batch([(w0, b, a, s, o) for (w0, b, a, s), o in zip(ins, outs)])
 
     _replays_match_eager(launch, outs)
+
+
+@pytest.mark.parametrize("want_dx", [True, False], ids=["with_dx", "no_dx"])
+def test_bwd_graph_replay(gpu_lib, want_dx):
+    """The backward's launches (transposes + projection, dX, token contraction,
+    reduce) replayed from a graph, the workspace reused across replays with
+    NaN written over it in between."""
+    import torch
+    rg = gpu_lib
+    M, N, K, r = 700, 264, 328, 24
+    c = synth.FwdCase("gbwd", 97, 900, M, N, K, r, 48.0, "bf16")
+    t = c.make("XWABD")
+    X, W, A, B, dY = (to_dev(t[k]) for k in ("X", "W", "A", "B", "dY"))
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((r, K), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((N, r), dtype=torch.bfloat16, device="cuda")
+    need = rg.bwd_workspace_size(rg.LORA_BF16, M, N, K, r)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    p = rg._mat
+
+    def launch():
+        ws.fill_(0xFF)  # a torch fill kernel, recorded too: garbage the kernels must not read
+        st = rg.bwd_raw(rg.LORA_BF16, M, N, K, r, *p(X, "X"), *p(W, "W"), *p(A, "A"),
+                        *p(B, "B"), *p(dY, "dY"), c.scale,
+                        *(p(dX, "dX") if want_dx else (0, K)), *p(dA, "dA"), *p(dB, "dB"),
+                        ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+        assert st == rg.LORA_OK
+
+    _replays_match_eager(launch, [dX, dA, dB] if want_dx else [dA, dB])
