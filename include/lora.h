@@ -274,7 +274,7 @@ int lora_merge_inplace(int dtype, int64_t N, int64_t K, int64_t r,
  *   M, N, K, r    tokens, d_out, d_in, rank; N and K multiples of 8.
  *                 M == 0: dA = 0 and dB = 0 are written.  1 <= r <= 256, and
  *                 (r padded to 16/32/64/128/256) * (M rounded up to 64)
- *                 <= 2^30.
+ *                 <= 2^30 - 64.
  *   X, ldx        [M,K] layer input (the forward's X).
  *   W, ldw        [N,K] base weight; only read for dX (may be NULL when dX is).
  *   A, lda        [r,K] lora_A.       B, ldb   [N,r] lora_B.

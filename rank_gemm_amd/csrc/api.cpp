@@ -95,9 +95,9 @@ int check_merge(int dtype, int64_t N, int64_t K, int64_t r, const void* W0, int6
 int64_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (M < 0 || N < 0 || K < 0 || r < 1 || r > LORA_MAX_RANK) return -1;
   if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return -1;
-  // T^T and G^T rows ([rank padded, M rounded to 64] bf16) are addressed with
-  // 32-bit byte offsets.
-  if ((int64_t)lora::pad_rank(r) * ((M + 63) / 64 * 64) > (int64_t(1) << 30)) return -1;
+  // T^T and G^T ([rank padded, M rounded to 64] bf16) are addressed with
+  // signed 32-bit byte ranges (r x ldp x 2 < 2^31).
+  if ((int64_t)lora::pad_rank(r) * ((M + 63) / 64 * 64) > (int64_t(1) << 30) - 64) return -1;
   return lora::bwd_plan(M, N, K, r).bytes;
 }
 
@@ -122,8 +122,9 @@ int check_bwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void*
   if ((tok && (ldx > LORA_MAX_LD || lddy > LORA_MAX_LD)) || lda > LORA_MAX_LD ||
       N > LORA_MAX_LD || (wantx && ldw > LORA_MAX_LD))
     return LORA_ERR_UNSUPPORTED;
-  if (K % 8 || N % 8 || (tok && (ldx % 8 || lddy % 8)) || lda % 8 || ldda % 8 ||
-      (wantx && ldw % 8))
+  // Leading-dimension alignment matters only for operands with elements.
+  if (K % 8 || N % 8 || (tok && K > 0 && ldx % 8) || (tok && N > 0 && lddy % 8) ||
+      (K > 0 && (lda % 8 || ldda % 8)) || (wantx && N > 0 && ldw % 8))
     return LORA_ERR_ALIGN;
   if ((K > 0 && (!aligned16(A) || !aligned16(dA) || (tok && !aligned16(X)))) ||
       (tok && N > 0 && !aligned16(dY)) || (wantx && N > 0 && !aligned16(W)) ||

@@ -490,9 +490,11 @@ hipError_t launch_rank(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, bo
                     a.scale, a.dX, a.lddx, Gt, p.ldp};
     if (hipError_t e = launch_fwd_tiled_bf16(f, s); e != hipSuccess) return e;
   } else {
-    // 1. B^T; 2. s T and s G.
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks(pre, 256)), dim3(256), 0, s, pre);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    // 1. B^T (nothing when N == 0); 2. s T and s G.
+    if (const int64_t blocks = prep_blocks(pre, 256); blocks > 0) {
+      hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, pre);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
     if (hipError_t e = launch_proj_nw<RP>(a, p, jt, jg, 2, nullptr, s); e != hipSuccess) return e;
   }
   // 3. Token contraction, reduction included.

@@ -223,6 +223,7 @@ def _bwd(**kw):
     (dict(r=0), rg.LORA_ERR_SHAPE),
     (dict(r=257, ldb=257, lddb=257), rg.LORA_ERR_UNSUPPORTED),
     (dict(M=1 << 24, r=128, ldb=128, lddb=128), rg.LORA_ERR_UNSUPPORTED),  # r * M past 2^30
+    (dict(M=1 << 23, r=128, ldb=128, lddb=128), rg.LORA_ERR_UNSUPPORTED),  # exactly 2^30
     (dict(X=0), rg.LORA_ERR_NULL),
     (dict(A=0), rg.LORA_ERR_NULL),
     (dict(B=0), rg.LORA_ERR_NULL),

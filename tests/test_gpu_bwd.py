@@ -165,3 +165,25 @@ def test_bwd_strided_operands(gpu_lib):
     _check("b_strided", got, ref)
     assert (dXb[:, K:].float() == 7).all() and (dAb[:, K:].float() == 7).all()
     assert (dBb[:, r:].float() == 7).all()
+
+
+@pytest.mark.parametrize("N,K,want_dx", [(0, 64, True), (0, 64, False), (48, 0, False),
+                                         (48, 0, True)],
+                         ids=["n0_dx", "n0_nodx", "k0_nodx", "k0_dx"])
+def test_bwd_empty_feature_dims(gpu_lib, N, K, want_dx):
+    """N = 0: G = 0, so dX = 0 and dA = 0 (dB is empty); K = 0: T = 0, so
+    dB = 0 (dX and dA are empty)."""
+    import torch
+    rg = gpu_lib
+    M, r = 130, 8
+    dev = "cuda"
+    X = torch.randn((M, K), device=dev).to(torch.bfloat16)
+    W = torch.randn((N, K), device=dev).to(torch.bfloat16)
+    A = torch.randn((r, K), device=dev).to(torch.bfloat16)
+    B = torch.randn((N, r), device=dev).to(torch.bfloat16)
+    dY = torch.randn((M, N), device=dev).to(torch.bfloat16)
+    dX, dA, dB = rg.bwd(X, W, A, B, dY, 2.0, want_dx=want_dx)
+    torch.cuda.synchronize()
+    for g in (dX, dA, dB):
+        if g is not None and g.numel():
+            assert (g.float() == 0).all()
