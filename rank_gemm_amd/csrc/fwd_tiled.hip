@@ -81,6 +81,15 @@ struct Cfg {
   static constexpr int kTOffG = STAGES * kStageB;
   static constexpr int kLdsG = kTOffG + BM * kTS * 2;
   static_assert(BN * kTS * 2 <= kTOffG && kYB <= kTOffG, "group epilogue fits in the ring");
+  // B tile elements per thread, fetched into registers at kernel start when
+  // few enough (the epilogue's gather would otherwise put a memory round trip
+  // after the K loop).  Not for 256 x 256 tiles: their main loop already
+  // holds nearly every register, and the early loads slowed it down; nor for
+  // 64 x 32 tiles past rank 16, where the live values push the kernel past
+  // 64 VGPRs and cost a wave of occupancy per SIMD.
+  static constexpr int kBPre = BN * RP / NT;
+  static constexpr bool kBEarly = BN * RP % NT == 0 && kBPre <= 8 && BM * BN <= 128 * 128 &&
+                                  (BM * BN > 64 * 32 || RP <= 16);
   static constexpr int kTSlots = (TM * RB + WN - 1) / WN;  // T accumulators per wave
   static constexpr int kGroup = 4;         // M tiles per group (XCD-contiguous ids)
   static constexpr int kGroupShared = 8;   // M tiles swept together by all XCDs (measured best)
@@ -292,6 +301,19 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
   for (int s = 0; s < C::kTSlots; ++s) tacc[s] = zero4();
 
+  // G == 1: the B tile's elements of this thread, loaded before the K loop.
+  constexpr bool kBEarly = C::kBEarly && G == 1;
+  uint16_t bpre[kBEarly ? C::kBPre : 1];
+  if constexpr (kBEarly) {
+    const int n0 = ng0 * BN;
+#pragma unroll
+    for (int i = 0; i < C::kBPre; ++i) {
+      const int e = tid + i * C::NT;
+      const int n = e / RP, j = e % RP;
+      bpre[i] = (j < r && n0 + n < N) ? B[(int64_t)(n0 + n) * ldb + j] : uint16_t(0);
+    }
+  }
+
   for (int g = 0; g < G; ++g) {
   const int n0 = (ng0 + g) * BN;
   if (n0 >= N) break;  // uniform: the group's last tiles may lie past N
@@ -448,11 +470,19 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     }
   }
   }
-  for (int e = tid; e < BN * RP; e += C::NT) {
-    const int n = e / RP, j = e % RP;
-    uint16_t v = 0;
-    if (j < r && n0 + n < N) v = B[(int64_t)(n0 + n) * ldb + j];
-    bs[n * C::kTS + j] = v;
+  if constexpr (kBEarly) {
+#pragma unroll
+    for (int i = 0; i < C::kBPre; ++i) {
+      const int e = tid + i * C::NT;
+      bs[(e / RP) * C::kTS + e % RP] = bpre[i];
+    }
+  } else {
+    for (int e = tid; e < BN * RP; e += C::NT) {
+      const int n = e / RP, j = e % RP;
+      uint16_t v = 0;
+      if (j < r && n0 + n < N) v = B[(int64_t)(n0 + n) * ldb + j];
+      bs[n * C::kTS + j] = v;
+    }
   }
   __syncthreads();
 
