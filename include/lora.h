@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 7
+#define LORA_ABI_VERSION 8
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -319,11 +319,16 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *   4   256 x 256    8    1               r <= 64
  *   5   256 x 256    8    2 N tiles       r <= 32
  *   6   128 x 128    8    1               r <= 128   (three stages)
+ *   7   128 x 128    8    1               r <= 64    (three stages, k split)
  * ("T shared over g N tiles": a workgroup computes g consecutive output
  * tiles of one row block and the down-projection T only once.  Every id
- * stages 64 k per stage; 0 keeps eight stages, 6 three, the others two.)
+ * stages 64 k per stage; 0 keeps eight stages, 6 and 7 three, the others
+ * two.  "k split": two groups of four waves compute the same tile, each
+ * from one 32-wide half of every stage, and their sums are added before the
+ * up-projection; its results differ from the other ids' in rounding, which
+ * all agree bit for bit with each other.)
  */
-#define LORA_TILE_COUNT 7
+#define LORA_TILE_COUNT 8
 
 typedef struct lora_tile_info {
     int32_t tile;        /* id */
@@ -334,6 +339,7 @@ typedef struct lora_tile_info {
     int32_t group;       /* N tiles per workgroup sharing T */
     int32_t rank_pad;    /* rank the instantiation is padded to */
     int32_t lds_bytes;   /* dynamic LDS per workgroup */
+    int32_t k_split;     /* wave groups sharing each stage's k range (1 or 2) */
 } lora_tile_info;
 
 typedef struct lora_tile_usage {

@@ -45,7 +45,7 @@ VARIANTS = {"auto": 0, "tiled": 1, "decode": 2}
 MAX_RANK = 256
 DECODE_MAX_M = 64
 
-TILE_COUNT = 7
+TILE_COUNT = 8
 
 EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch",
            "lora_merge_inplace", "lora_status_str", "lora_abi_version", "lora_fwd_pick",
@@ -78,7 +78,7 @@ class FwdDesc(ctypes.Structure):
 class TileInfo(ctypes.Structure):
     """lora_tile_info of include/lora.h."""
     _fields_ = [(n, ctypes.c_int32) for n in ("tile", "bm", "bn", "waves", "stages", "bk",
-                                              "group", "rank_pad", "lds_bytes")]
+                                              "group", "rank_pad", "lds_bytes", "k_split")]
 
 
 class TileUsage(ctypes.Structure):

@@ -316,7 +316,7 @@ int lora_tile_get_info(int tile, int64_t r, lora_tile_info* out) {
   lora::TileProps t{};
   if (lora::fwd_tile_props(tile, r, &t) != hipSuccess) return LORA_ERR_UNSUPPORTED;
   *out = lora_tile_info{tile, t.bm, t.bn, t.waves, t.stages, t.bk, t.group, t.rank_pad,
-                        t.lds_bytes};
+                        t.lds_bytes, t.k_split};
   return LORA_OK;
 }
 

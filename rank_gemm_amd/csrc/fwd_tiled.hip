@@ -50,13 +50,20 @@ __device__ __forceinline__ int stage_off(int row, int chunk) {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_>
+// KS = 2 splits every stage's k range between two groups of WM x WN waves
+// that compute the same BM x BN tile: group g multiplies k32 half g of each
+// stage, and the epilogue adds the two partial sums through LDS.  Each wave
+// then holds a tile KS times taller for the same LDS reads per k32, which
+// cuts the LDS bytes read per MFMA (the K loop of the 128 x 128 tile is
+// bound by LDS bandwidth), while keeping two waves per SIMD.
+template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_, BK = BK_;
+  static constexpr int KS = KS_;
   static constexpr int kRowB = BK * 2;                // bytes per staged row
   static constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one 1-KiB wave load covers
   static constexpr int kChunks = BK / 8;              // 16-B chunks per row
-  static constexpr int NW = WM * WN;
+  static constexpr int NW = WM * WN * KS;
   static constexpr int NT = NW * kWave;
   static constexpr int TM = BM / WM / 16;
   static constexpr int TN = BN / WN / 16;
@@ -75,7 +82,12 @@ struct Cfg {
   static constexpr int kEpiB = (BM + BN) * kTS * 2;
   static constexpr int kYS = BN + 8;                // output staging row stride (elements)
   static constexpr int kYB = BM * kYS * 2;
-  static constexpr int kLds = cmax(STAGES * kStageB, cmax(kEpiB, kYB));
+  // K split: after the loop each wave sends the half of its accumulators that
+  // its partner in the other group keeps (1 KiB per fragment), and group 1
+  // sends its partial T; the area starts after the epilogue's T and B tiles.
+  static constexpr int kXOff = kEpiB;
+  static constexpr int kXchB = KS == 2 ? WM * WN * (TM * TN + (TM * RB + WN - 1) / WN) * 1024 : 0;
+  static constexpr int kLds = cmax(cmax(STAGES * kStageB, kXOff + kXchB), cmax(kEpiB, kYB));
   // With T kept across the N tiles of a group: T after the ring, the B tile
   // and the output staging inside it.
   static constexpr int kTOffG = STAGES * kStageB;
@@ -106,6 +118,7 @@ struct Cfg {
                 "X/W loads split evenly over waves");
   static_assert(kLds <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2, "ring: one stage being read, at least one in flight");
+  static_assert(KS == 1 || (KS == 2 && BK == 64 && TM % 2 == 0), "k split: one k32 half per group");
   static_assert(BK == 32 || BK == 64, "one or two k32 substeps per stage");
 };
 
@@ -236,8 +249,11 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int wm = wave / WN;
-  const int wn = wave % WN;
+  static_assert(C::KS == 1 || G == 1, "k split: one tile per workgroup");
+  const int wgi = C::KS == 1 ? wave : wave % (C::WM * WN);  // wave within its k group
+  const int kg = C::KS == 1 ? 0 : wave / (C::WM * WN);     // k group (KS = 2: its k32 half)
+  const int wm = wgi / WN;
+  const int wn = wgi % WN;
   const int lrow = lane & 15;
   const int lk = lane >> 4;
 
@@ -348,6 +364,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int xrow0 = wm * TM * 16 + lrow;  // + 16 * ring_row_block(k) for ring slot k
   const int wrow0 = wn * TN * 16 + lrow;
   Frags<C> cur;
+  const int lk0 = C::KS == 2 ? kg * 4 + lk : lk;  // logical chunk of this wave's first k32
   wait_stages<C, STAGES - 1, WT>(wave);
   __builtin_amdgcn_s_barrier();
   {
@@ -357,14 +374,14 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       cur.a[i] = *reinterpret_cast<const u32x4*>(
-          xs + stage_off<BK>(xrow0 + ring_row_block<C>(i, rot) * 16, lk));
+          xs + stage_off<BK>(xrow0 + ring_row_block<C>(i, rot) * 16, lk0));
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      cur.b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, lk));
+      cur.b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(wrow0 + j * 16, lk0));
     if constexpr (WT) {
 #pragma unroll
       for (int u = 0; u < C::kTF; ++u)
-        cur.t[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk));
+        cur.t[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk0));
     }
   }
 
@@ -389,7 +406,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     const unsigned char* xs = smem + (sync ? nslot : rslot) * C::kStageB;
     const unsigned char* ws = xs + BM * kRowB;
     const unsigned char* as = ws + BN * kRowB;
-    const int cc = (sync ? 0 : (u + 1) * 4) + lk;  // logical 16-B chunk of the next substep
+    // logical 16-B chunk of the next substep
+    const int cc = (sync ? (C::KS == 2 ? kg * 4 : 0) : (u + 1) * 4) + lk;
     // After the final substep the reads fetch a zero stage (never used).
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -435,6 +453,20 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 
   u32x4 b2[TN], t2[C::kTF];
   int rslot = 0;  // ring slot of stage kt
+  if constexpr (C::KS == 2) {
+    // One substep per stage (this group's k32 half), ending in the stage's
+    // barrier; two stages per iteration so the register sets alternate.
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      int nslot = rslot + 1 == STAGES ? 0 : rslot + 1;
+      substep(true, rslot, nslot, kt, 0, cur.b, cur.t, b2, t2);
+      rslot = nslot;
+      nslot = rslot + 1 == STAGES ? 0 : rslot + 1;
+      substep(true, rslot, nslot, kt + 1, 0, b2, t2, cur.b, cur.t);
+      rslot = nslot;
+    }
+    if (kt < nk) substep(true, rslot, rslot + 1 == STAGES ? 0 : rslot + 1, kt, 0, cur.b, cur.t, b2, t2);
+  } else {
   for (int kt = 0; kt < nk; ++kt) {
     const int nslot = rslot + 1 == STAGES ? 0 : rslot + 1;  // slot of stage kt+1
     if constexpr (NSUB == 2) {
@@ -449,16 +481,65 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     }
     rslot = nslot;
   }
+  }
   };  // kloop
   if (g == 0) kloop(std::true_type{});
   else kloop(std::false_type{});
   __syncthreads();
 
+  // ---- k split: add the two groups' partial sums.  Group g keeps ring slots
+  // [g TM/2, (g+1) TM/2) of its accumulators and receives the partner's
+  // values for them; group 0 receives group 1's partial T.  Addition is
+  // commutative, so every kept value is (group 0's sum) + (group 1's sum).
+  constexpr int TH = TM / C::KS;  // ring slots a wave keeps
+  if constexpr (C::KS == 2) {
+    float* xch = reinterpret_cast<float*>(smem + C::kXOff);
+    constexpr int kTOff = C::WM * WN * TM * TN;  // fragment index of the T area
+    auto frag = [&](int f) { return reinterpret_cast<f32x4*>(xch + (f * kWave + lane) * 4); };
+    auto put = [&](auto s0c) {
+      constexpr int S0 = decltype(s0c)::value;
+#pragma unroll
+      for (int i = 0; i < TH; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) *frag(((wgi * 2 + kg) * TH + i) * TN + j) = acc[S0 + i][j];
+    };
+    auto take = [&](auto s0c) {
+      constexpr int S0 = decltype(s0c)::value;
+#pragma unroll
+      for (int i = 0; i < TH; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const f32x4 v = *frag(((wgi * 2 + 1 - kg) * TH + i) * TN + j);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[S0 + i][j][q] += v[q];
+        }
+    };
+    if (kg == 0) {
+      put(std::integral_constant<int, TH>{});
+    } else {
+      put(std::integral_constant<int, 0>{});
+#pragma unroll
+      for (int sl = 0; sl < C::kTSlots; ++sl) *frag(kTOff + wgi * C::kTSlots + sl) = tacc[sl];
+    }
+    __syncthreads();
+    if (kg == 0) {
+      take(std::integral_constant<int, 0>{});
+#pragma unroll
+      for (int sl = 0; sl < C::kTSlots; ++sl) {
+        const f32x4 v = *frag(kTOff + wgi * C::kTSlots + sl);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tacc[sl][q] += v[q];
+      }
+    } else {
+      take(std::integral_constant<int, TH>{});
+    }
+  }
+
   // ---- epilogue 1: scaled T (bf16) and the B tile into LDS.  With G > 1,
   // T lives past the stage ring and is written by the first tile only.
   uint16_t* ts = reinterpret_cast<uint16_t*>(smem + (G > 1 ? C::kTOffG : 0));
   uint16_t* bs = G > 1 ? reinterpret_cast<uint16_t*>(smem) : ts + BM * C::kTS;
-  if (g == 0) {
+  if (g == 0 && kg == 0) {
 #pragma unroll
   for (int sl = 0; sl < C::kTSlots; ++sl) {
     const int i = ring_row_block<C>(t_ring_slot<C>(sl), rot);
@@ -497,6 +578,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     }
   }
 
+  uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
+  if constexpr (C::KS == 1) {
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank.
   if constexpr (RP >= 32) {
 #pragma unroll
@@ -532,7 +615,6 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   __syncthreads();
 
   // ---- epilogue 3: round once to bf16, stage, store coalesced.
-  uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -543,6 +625,65 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
         ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
       }
   __syncthreads();
+  } else {
+  // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank, for
+  // the ring slots [S0, S0 + TH) this wave keeps.
+  auto epi2 = [&](auto s0c) {
+    constexpr int S0 = decltype(s0c)::value;
+    if constexpr (RP >= 32) {
+#pragma unroll
+      for (int kk = 0; kk < RP / 32; ++kk) {
+        u32x4 a[TH], b[TN];
+#pragma unroll
+        for (int i = 0; i < TH; ++i)
+          a[i] = *reinterpret_cast<const u32x4*>(
+              ts + (wm * TM * 16 + ring_row_block<C>(S0 + i, rot) * 16 + lrow) * C::kTS + kk * 32 +
+              lk * 8);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS +
+                                                 kk * 32 + lk * 8);
+#pragma unroll
+        for (int i = 0; i < TH; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[S0 + i][j] = mfma16x16x32(a[i], b[j], acc[S0 + i][j]);
+      }
+    } else {
+      u32x2 a[TH], b[TN];
+#pragma unroll
+      for (int i = 0; i < TH; ++i)
+        a[i] = *reinterpret_cast<const u32x2*>(
+            ts + (wm * TM * 16 + ring_row_block<C>(S0 + i, rot) * 16 + lrow) * C::kTS + lk * 4);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = *reinterpret_cast<const u32x2*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS + lk * 4);
+#pragma unroll
+      for (int i = 0; i < TH; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[S0 + i][j] = mfma16x16x16(a[i], b[j], acc[S0 + i][j]);
+    }
+  };
+  if (kg == 0) epi2(std::integral_constant<int, 0>{});
+  else epi2(std::integral_constant<int, TH>{});
+  __syncthreads();
+
+  // ---- epilogue 3: round once to bf16, stage, store coalesced.
+  auto epi3 = [&](auto s0c) {
+    constexpr int S0 = decltype(s0c)::value;
+#pragma unroll
+    for (int i = S0; i < S0 + TH; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lk * 4 + q;
+          ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
+        }
+  };
+  if (kg == 0) epi3(std::integral_constant<int, 0>{});
+  else epi3(std::integral_constant<int, TH>{});
+  __syncthreads();
+  }
   constexpr int kCPR = BN / 8;  // 16-B chunks per output row
   for (int e = tid; e < BM * kCPR; e += C::NT) {
     const int row = e / kCPR, c = e % kCPR;
@@ -614,6 +755,10 @@ using Mid = Cfg<128, 128, 4, 2, RP, 2, 64>;
 // four stages (10-30 % slower).
 template <int RP>
 using Mid3 = Cfg<128, 128, 4, 2, RP, 3, 64>;
+// 128 x 128 with the k split: 4 x 2 waves of 32 x 64 per k group, two
+// groups (16 waves, four per SIMD), three stages.
+template <int RP>
+using MidK2 = Cfg<128, 128, 4, 2, RP, 3, 64, 2>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
 // measurements on the benchmark shapes:
@@ -662,6 +807,7 @@ void tile_fill(TileProps* t) {
   t->group = G;
   t->rank_pad = C::RP;
   t->lds_bytes = G > 1 ? C::kLdsG : C::kLds;
+  t->k_split = C::KS;
   t->kernel = reinterpret_cast<const void*>(fwd_tiled_bf16_kernel<C, G>);
 }
 
@@ -706,6 +852,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 128) {
         if (props) return tile_fill<Mid3<RP>, 1>(props), hipSuccess;
         return launch<Mid3<RP>>(*a, s);
+      }
+      break;
+    case kTileMidK2:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<MidK2<RP>, 1>(props), hipSuccess;
+        return launch<MidK2<RP>>(*a, s);
       }
       break;
     default:

@@ -33,7 +33,7 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 7
+    assert rg.abi_version() == 8
     for s in range(10):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
@@ -268,7 +268,8 @@ def test_bwd_workspace_size():
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(tile=7), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=8), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=7, r=100, ldb=100), rg.LORA_ERR_UNSUPPORTED),   # k-split tile: r <= 64
     (dict(tile=6, r=200, ldb=200), rg.LORA_ERR_UNSUPPORTED),
     (dict(tile=-1), rg.LORA_ERR_UNSUPPORTED),
     (dict(tile=0, r=64, ldb=64), rg.LORA_ERR_UNSUPPORTED),     # 64 x 32 tile: r <= 32

@@ -82,6 +82,7 @@ def test_tile_table_matches_library():
                 assert info.tile == tid and info.rank_pad == tune.pad_rank(r)
                 assert info.lds_bytes <= 160 * 1024
                 assert info.waves * 64 <= 1024
+                assert info.k_split == (2 if tid == 7 else 1)
     assert rg.tile_info(rg.TILE_COUNT, 16) is None
     assert rg.tile_info(-1, 16) is None
     assert int(rg.lib().lora_tile_get_info(0, 0, None)) in (rg.LORA_ERR_NULL, rg.LORA_ERR_SHAPE)
