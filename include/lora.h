@@ -319,16 +319,18 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *   4   256 x 256    8    1               r <= 64
  *   5   256 x 256    8    2 N tiles       r <= 32
  *   6   128 x 128    8    1               r <= 128   (three stages)
- *   7   128 x 128    8    1               r <= 64    (three stages, k split)
+ *   7   128 x 128   16    1               r <= 64    (three stages, k split)
+ *   8   128 x 128   12    1               r <= 128   (three stages, 4 loaders)
  * ("T shared over g N tiles": a workgroup computes g consecutive output
  * tiles of one row block and the down-projection T only once.  Every id
- * stages 64 k per stage; 0 keeps eight stages, 6 and 7 three, the others
- * two.  "k split": two groups of four waves compute the same tile, each
- * from one 32-wide half of every stage, and their sums are added before the
- * up-projection; its results differ from the other ids' in rounding, which
- * all agree bit for bit with each other.)
+ * stages 64 k per stage; 0 keeps eight stages, 6, 7 and 8 three, the
+ * others two.  "k split": two groups of eight waves compute the same tile,
+ * each from one 32-wide half of every stage, and their sums are added before
+ * the up-projection; its results differ from the other ids' in rounding,
+ * which all agree bit for bit with each other.  "4 loaders": four of the
+ * waves only issue the stage loads, the other eight only multiply.)
  */
-#define LORA_TILE_COUNT 8
+#define LORA_TILE_COUNT 9
 
 typedef struct lora_tile_info {
     int32_t tile;        /* id */

@@ -56,14 +56,22 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // then holds a tile KS times taller for the same LDS reads per k32, which
 // cuts the LDS bytes read per MFMA (the K loop of the 128 x 128 tile is
 // bound by LDS bandwidth), while keeping two waves per SIMD.
-template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1>
+//
+// PW > 0 adds PW loader waves that issue every stage's loads while the
+// WM x WN x KS multiplying waves only read LDS and run MFMAs.  A wave stalls
+// at a load issue when the memory pipeline is backed up, and a multiplying
+// wave stalled there cannot issue its MFMAs either: with separate loaders the
+// loads and the MFMAs overlap.
+template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1, int PW_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_, BK = BK_;
-  static constexpr int KS = KS_;
+  static constexpr int KS = KS_, PW = PW_;
   static constexpr int kRowB = BK * 2;                // bytes per staged row
   static constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one 1-KiB wave load covers
   static constexpr int kChunks = BK / 8;              // 16-B chunks per row
-  static constexpr int NW = WM * WN * KS;
+  static constexpr int NWC = WM * WN * KS;          // multiplying waves
+  static constexpr int NW = NWC + PW;               // all waves
+  static constexpr int LW = PW > 0 ? PW : NWC;      // waves that issue the stage loads
   static constexpr int NT = NW * kWave;
   static constexpr int TM = BM / WM / 16;
   static constexpr int TN = BN / WN / 16;
@@ -71,13 +79,13 @@ struct Cfg {
   static constexpr int ROWS = BM + BN + RP;         // staged rows per stage
   static constexpr int kStageB = ROWS * kRowB;
   static_assert(BK == 32 || BK == 64, "stage depth");
-  static constexpr int kXL = BM / kRowsPerLoad / NW;  // X loads (1 KiB each) per wave per stage
-  static constexpr int kWL = BN / kRowsPerLoad / NW;  // W loads per wave per stage
+  static constexpr int kXL = BM / kRowsPerLoad / LW;  // X loads (1 KiB each) per loader per stage
+  static constexpr int kWL = BN / kRowsPerLoad / LW;  // W loads per loader per stage
   static constexpr int kAN = (RP + kRowsPerLoad - 1) / kRowsPerLoad;  // A loads per stage
-  static constexpr int kAL = (kAN + NW - 1) / NW;     // A load slots per wave per stage
-  // Loads per stage: waves below kAN % NW issue one A load more than the rest.
-  static constexpr int kLoadsLo = kXL + kWL + kAN / NW;
-  static constexpr int kLoadsHi = kLoadsLo + (kAN % NW != 0 ? 1 : 0);
+  static constexpr int kAL = (kAN + LW - 1) / LW;     // A load slots per loader per stage
+  // Loads per stage: loaders below kAN % LW issue one A load more than the rest.
+  static constexpr int kLoadsLo = kXL + kWL + kAN / LW;
+  static constexpr int kLoadsHi = kLoadsLo + (kAN % LW != 0 ? 1 : 0);
   static constexpr int kTS = RP + 8;                // epilogue T / B row stride (elements)
   static constexpr int kEpiB = (BM + BN) * kTS * 2;
   static constexpr int kYS = BN + 8;                // output staging row stride (elements)
@@ -99,9 +107,10 @@ struct Cfg {
   // holds nearly every register, and the early loads slowed it down; nor for
   // 64 x 32 tiles past rank 16, where the live values push the kernel past
   // 64 VGPRs and cost a wave of occupancy per SIMD.
-  static constexpr int kBPre = BN * RP / NT;
-  static constexpr bool kBEarly = BN * RP % NT == 0 && kBPre <= 8 && BM * BN <= 128 * 128 &&
-                                  (BM * BN > 64 * 32 || RP <= 16);
+  // (held by the multiplying waves' threads)
+  static constexpr int kBPre = BN * RP / (NWC * kWave);
+  static constexpr bool kBEarly = BN * RP % (NWC * kWave) == 0 && kBPre <= 8 &&
+                                  BM * BN <= 128 * 128 && (BM * BN > 64 * 32 || RP <= 16);
   static constexpr int kTSlots = (TM * RB + WN - 1) / WN;  // T accumulators per wave
   static constexpr int kGroup = 4;         // M tiles per group (XCD-contiguous ids)
   static constexpr int kGroupShared = 8;   // M tiles swept together by all XCDs (measured best)
@@ -114,8 +123,8 @@ struct Cfg {
   static_assert((TM & (TM - 1)) == 0, "ring rotation needs a power-of-two row-block count");
   static constexpr int kTF = kTByRank ? RB / WN : 1;       // A fragments per wave
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiling");
-  static_assert(BM % (kRowsPerLoad * NW) == 0 && BN % (kRowsPerLoad * NW) == 0,
-                "X/W loads split evenly over waves");
+  static_assert(BM % (kRowsPerLoad * LW) == 0 && BN % (kRowsPerLoad * LW) == 0,
+                "X/W loads split evenly over the loaders");
   static_assert(kLds <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2, "ring: one stage being read, at least one in flight");
   static_assert(KS == 1 || (KS == 2 && BK == 64 && TM % 2 == 0), "k split: one k32 half per group");
@@ -189,7 +198,7 @@ __device__ __forceinline__ void wait_stages(int wave) {
     return;
   }
   if constexpr (C::kLoadsHi != C::kLoadsLo) {
-    if (wave < C::kAN % C::NW) {
+    if (wave < C::kAN % C::LW) {
       wait_vmcnt<Newer * C::kLoadsHi>();
       return;
     }
@@ -213,19 +222,19 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
   constexpr int kRowB = C::kRowB;
 #pragma unroll
   for (int s = 0; s < C::kXL; ++s)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(base + (wave + s * C::NW) * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(base + (wave + s * C::LW) * 1024), 16,
                                              off_or_oob(kin, vx + sgpr(s * sx + kb)), 0, 0, 0);
 #pragma unroll
   for (int s = 0; s < C::kWL; ++s)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rw, (lds_void*)(base + C::BM * kRowB + (wave + s * C::NW) * 1024), 16,
+        rw, (lds_void*)(base + C::BM * kRowB + (wave + s * C::LW) * 1024), 16,
         off_or_oob(kin, vw + sgpr(s * sw + kb)), 0, 0, 0);
   if constexpr (!WT) return;  // T already known: no A rows
 #pragma unroll
   for (int s = 0; s < C::kAL; ++s)
-    if (wave + s * C::NW < C::kAN)
+    if (wave + s * C::LW < C::kAN)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void*)(base + (C::BM + C::BN) * kRowB + (wave + s * C::NW) * 1024), 16,
+          ra, (lds_void*)(base + (C::BM + C::BN) * kRowB + (wave + s * C::LW) * 1024), 16,
           off_or_oob(kin, va + sgpr(s * sa + kb)), 0, 0, 0);
 }
 
@@ -250,8 +259,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   static_assert(C::KS == 1 || G == 1, "k split: one tile per workgroup");
-  const int wgi = C::KS == 1 ? wave : wave % (C::WM * WN);  // wave within its k group
-  const int kg = C::KS == 1 ? 0 : wave / (C::WM * WN);     // k group (KS = 2: its k32 half)
+  // With loader waves: waves [0, NWC) multiply, waves [NWC, NW) load.
+  const bool mul = C::PW == 0 || wave < C::NWC;
+  const int lw = C::PW == 0 ? wave : wave - C::NWC;  // loader index (loaders only)
+  const int cw = C::PW == 0 ? wave : (mul ? wave : 0);
+  const int wgi = C::KS == 1 ? cw : cw % (C::WM * WN);  // wave within its k group
+  const int kg = C::KS == 1 ? 0 : cw / (C::WM * WN);     // k group (KS = 2: its k32 half)
   const int wm = wgi / WN;
   const int wn = wgi % WN;
   const int lrow = lane & 15;
@@ -304,12 +317,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   constexpr int BK = C::BK, kRowB = C::kRowB, kRPL = C::kRowsPerLoad;
   const int lrow_in_load = lane / C::kChunks;
   const int lchunk = (lane % C::kChunks) ^ swz<BK>(lrow_in_load);
-  const uint32_t vx = (uint32_t)((wave * kRPL + lrow_in_load) * ldx * 2 + lchunk * 16);
-  const uint32_t vw = (uint32_t)((wave * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
-  const uint32_t va = (uint32_t)((wave * kRPL + lrow_in_load) * lda * 2 + lchunk * 16);
-  const uint32_t sx = (uint32_t)(NW * kRPL * ldx * 2);  // byte stride between a wave's slots
-  const uint32_t sw = (uint32_t)(NW * kRPL * ldw * 2);
-  const uint32_t sa = (uint32_t)(NW * kRPL * lda * 2);
+  const uint32_t vx = (uint32_t)((lw * kRPL + lrow_in_load) * ldx * 2 + lchunk * 16);
+  const uint32_t vw = (uint32_t)((lw * kRPL + lrow_in_load) * ldw * 2 + lchunk * 16);
+  const uint32_t va = (uint32_t)((lw * kRPL + lrow_in_load) * lda * 2 + lchunk * 16);
+  const uint32_t sx = (uint32_t)(C::LW * kRPL * ldx * 2);  // byte stride between a loader's slots
+  const uint32_t sw = (uint32_t)(C::LW * kRPL * ldw * 2);
+  const uint32_t sa = (uint32_t)(C::LW * kRPL * lda * 2);
 
   const int rot = ring_rot<C>(wn);
   f32x4 acc[TM][TN];
@@ -324,7 +337,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     const int n0 = ng0 * BN;
 #pragma unroll
     for (int i = 0; i < C::kBPre; ++i) {
-      const int e = tid + i * C::NT;
+      const int e = tid + i * C::NWC * kWave;
       const int n = e / RP, j = e % RP;
       bpre[i] = (j < r && n0 + n < N) ? B[(int64_t)(n0 + n) * ldb + j] : uint16_t(0);
     }
@@ -357,15 +370,38 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // streams.
   constexpr int NSUB = BK / 32;
   const int nk = (K + BK - 1) / BK;
+  if constexpr (C::PW > 0) {
+    if (!mul) {
+      // Loader: the same barriers as the multiplying waves (one after stage
+      // 0 has landed, one per stage), each preceded by the wait for the
+      // stage the multipliers read next; after the barrier of stage kt every
+      // read of stage kt is done and its slot is refilled.
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    issue_stage<C, WT>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+      for (int s = 0; s < STAGES; ++s)
+        issue_stage<C, WT>(smem, s, s * BK, K, lw, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+      wait_stages<C, STAGES - 1, WT>(lw);
+      __builtin_amdgcn_s_barrier();
+      int slot = 0;
+      for (int kt = 0; kt < nk; ++kt) {
+        wait_stages<C, STAGES - 2, WT>(lw);
+        __builtin_amdgcn_s_barrier();
+        issue_stage<C, WT>(smem, slot, (kt + STAGES) * BK, K, lw, lchunk, rx, rw, ra, vx, vw, va,
+                           sx, sw, sa);
+        slot = slot + 1 == STAGES ? 0 : slot + 1;
+      }
+      return;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      issue_stage<C, WT>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+  }
 
   const int xrow0 = wm * TM * 16 + lrow;  // + 16 * ring_row_block(k) for ring slot k
   const int wrow0 = wn * TN * 16 + lrow;
   Frags<C> cur;
   const int lk0 = C::KS == 2 ? kg * 4 + lk : lk;  // logical chunk of this wave's first k32
-  wait_stages<C, STAGES - 1, WT>(wave);
+  if constexpr (C::PW == 0) wait_stages<C, STAGES - 1, WT>(wave);
   __builtin_amdgcn_s_barrier();
   {
     const unsigned char* xs = smem;
@@ -397,11 +433,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       // flight; this wave's reads of stage kt are complete.  After the
       // barrier every wave is past both.  A bare s_barrier: a fence would
       // drain every stage in flight.
-      wait_stages<C, STAGES - 2, WT>(wave);
+      if constexpr (C::PW == 0) wait_stages<C, STAGES - 2, WT>(wave);
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      issue_stage<C, WT>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx,
-                     sw, sa);
+      if constexpr (C::PW == 0)
+        issue_stage<C, WT>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va,
+                           sx, sw, sa);
     }
     const unsigned char* xs = smem + (sync ? nslot : rslot) * C::kStageB;
     const unsigned char* ws = xs + BM * kRowB;
@@ -425,7 +462,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
           xs + stage_off<BK>(xrow0 + ring_row_block<C>(i, rot) * 16, cc));
     }
     // Interleave DMA issues and LDS reads between the MFMAs.
-    constexpr int kDma = C::kXL + C::kWL;
+    constexpr int kDma = C::PW > 0 ? 0 : C::kXL + C::kWL;
     constexpr int kReads = TN + (WT ? C::kTF : 0) + TM;
     constexpr int kMfma = TM * TN;
     if (sync) {
@@ -514,24 +551,28 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
           for (int q = 0; q < 4; ++q) acc[S0 + i][j][q] += v[q];
         }
     };
-    if (kg == 0) {
-      put(std::integral_constant<int, TH>{});
-    } else {
-      put(std::integral_constant<int, 0>{});
+    if (mul) {
+      if (kg == 0) {
+        put(std::integral_constant<int, TH>{});
+      } else {
+        put(std::integral_constant<int, 0>{});
 #pragma unroll
-      for (int sl = 0; sl < C::kTSlots; ++sl) *frag(kTOff + wgi * C::kTSlots + sl) = tacc[sl];
+        for (int sl = 0; sl < C::kTSlots; ++sl) *frag(kTOff + wgi * C::kTSlots + sl) = tacc[sl];
+      }
     }
     __syncthreads();
-    if (kg == 0) {
-      take(std::integral_constant<int, 0>{});
+    if (mul) {
+      if (kg == 0) {
+        take(std::integral_constant<int, 0>{});
 #pragma unroll
-      for (int sl = 0; sl < C::kTSlots; ++sl) {
-        const f32x4 v = *frag(kTOff + wgi * C::kTSlots + sl);
+        for (int sl = 0; sl < C::kTSlots; ++sl) {
+          const f32x4 v = *frag(kTOff + wgi * C::kTSlots + sl);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) tacc[sl][q] += v[q];
+          for (int q = 0; q < 4; ++q) tacc[sl][q] += v[q];
+        }
+      } else {
+        take(std::integral_constant<int, TH>{});
       }
-    } else {
-      take(std::integral_constant<int, TH>{});
     }
   }
 
@@ -539,7 +580,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // T lives past the stage ring and is written by the first tile only.
   uint16_t* ts = reinterpret_cast<uint16_t*>(smem + (G > 1 ? C::kTOffG : 0));
   uint16_t* bs = G > 1 ? reinterpret_cast<uint16_t*>(smem) : ts + BM * C::kTS;
-  if (g == 0 && kg == 0) {
+  if (g == 0 && kg == 0 && mul) {
 #pragma unroll
   for (int sl = 0; sl < C::kTSlots; ++sl) {
     const int i = ring_row_block<C>(t_ring_slot<C>(sl), rot);
@@ -552,10 +593,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
   }
   if constexpr (kBEarly) {
+    if (mul) {
 #pragma unroll
-    for (int i = 0; i < C::kBPre; ++i) {
-      const int e = tid + i * C::NT;
-      bs[(e / RP) * C::kTS + e % RP] = bpre[i];
+      for (int i = 0; i < C::kBPre; ++i) {
+        const int e = tid + i * C::NWC * kWave;
+        bs[(e / RP) * C::kTS + e % RP] = bpre[i];
+      }
     }
   } else {
     for (int e = tid; e < BN * RP; e += C::NT) {
@@ -581,7 +624,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
   if constexpr (C::KS == 1) {
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank.
-  if constexpr (RP >= 32) {
+  if (!mul) {
+  } else if constexpr (RP >= 32) {
 #pragma unroll
     for (int kk = 0; kk < RP / 32; ++kk) {
       u32x4 a[TM], b[TN];
@@ -615,6 +659,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   __syncthreads();
 
   // ---- epilogue 3: round once to bf16, stage, store coalesced.
+  if (mul) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -624,6 +669,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
         const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lk * 4 + q;
         ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
       }
+  }
   __syncthreads();
   } else {
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank, for
@@ -663,8 +709,10 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
         for (int j = 0; j < TN; ++j) acc[S0 + i][j] = mfma16x16x16(a[i], b[j], acc[S0 + i][j]);
     }
   };
-  if (kg == 0) epi2(std::integral_constant<int, 0>{});
-  else epi2(std::integral_constant<int, TH>{});
+  if (mul) {
+    if (kg == 0) epi2(std::integral_constant<int, 0>{});
+    else epi2(std::integral_constant<int, TH>{});
+  }
   __syncthreads();
 
   // ---- epilogue 3: round once to bf16, stage, store coalesced.
@@ -680,8 +728,10 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
           ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
         }
   };
-  if (kg == 0) epi3(std::integral_constant<int, 0>{});
-  else epi3(std::integral_constant<int, TH>{});
+  if (mul) {
+    if (kg == 0) epi3(std::integral_constant<int, 0>{});
+    else epi3(std::integral_constant<int, TH>{});
+  }
   __syncthreads();
   }
   constexpr int kCPR = BN / 8;  // 16-B chunks per output row
@@ -759,26 +809,34 @@ using Mid3 = Cfg<128, 128, 4, 2, RP, 3, 64>;
 // groups (16 waves, four per SIMD), three stages.
 template <int RP>
 using MidK2 = Cfg<128, 128, 4, 2, RP, 3, 64, 2>;
+// The three-stage 128 x 128 tile with four loader waves (12 waves).
+// Measured on X[4096,1024] W[1024,1024] r16: 13.0 us against 14.6 us for
+// the same tile without loaders; two loaders 13.2 us, eight 12.9 us but
+// slower elsewhere; with two stages 13.1 us but slower at larger K.
+template <int RP>
+using Mid3L = Cfg<128, 128, 4, 2, RP, 3, 64, 1, 4>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
 // measurements on the benchmark shapes:
-//  * rank <= 32 and fewer tokens than one 128-row tile, or a 128 x 128 grid
-//    that would leave more than half of the 256 CUs idle: the 64 x 32 tile
-//    (512 x 1024 x 512 r16: 8.8 vs 10.8 us);
+//  * rank <= 32 and at most 64 tokens, or fewer than 64 tiles of 128 x 128
+//    (three quarters of the 256 CUs idle): the 64 x 32 tile (512 x 1024 x
+//    1024 r32: 7.9 vs 11.1 us with loaders; at 64 tiles the loader tile
+//    wins, 1024 x 1024 x 2048 r16: 16.5 vs 20.6 us);
 //  * 256 x 256 when there are >= 256 such tiles and the last round of them
 //    is at least 80 % full (q_proj, 512 tiles: 160 vs 202 us; the q_proj
 //    backward's dX product, 320 tiles: 211 us vs 191 us on 128 x 128);
 //  * rank 128 with >= 512 128 x 128 tiles: T shared over 2 N tiles (square
 //    16384 x 8192 x 8192: 3.27 ms; over 4 tiles 3.73 ms; unshared 3.87 ms);
 //  * at most 256 128 x 128 tiles (one per CU, so a second resident workgroup
-//    would have nothing to do): 128 x 128 with three stages (2048 cubed r16:
-//    24.5 vs 27.1 us);
+//    would have nothing to do): 128 x 128 with three stages and four loader
+//    waves (4096 x 1024 x 1024 r16: 13.0 us; without loaders 14.6, two
+//    stages 15.1; 2048 cubed r16: 22.4 vs 23.6 and 25.9 us);
 //  * else 128 x 128.
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
   const int64_t mid_tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
   if constexpr (RP <= 32) {
-    if (a.M <= 64 || mid_tiles < 128) return launch<Tall<RP>>(a, s);
+    if (a.M <= 64 || mid_tiles < 64) return launch<Tall<RP>>(a, s);
   }
   if constexpr (RP <= 64) {
     const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
@@ -789,7 +847,7 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
     if (a.N > 128 && mid_tiles >= 512) return launch<Mid<RP>, 2>(a, s);
   }
   if constexpr (RP <= 128) {
-    if (mid_tiles <= 256) return launch<Mid3<RP>>(a, s);
+    if (mid_tiles <= 256) return launch<Mid3L<RP>>(a, s);
   }
   return launch<Mid<RP>>(a, s);
 }
@@ -858,6 +916,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 64) {
         if (props) return tile_fill<MidK2<RP>, 1>(props), hipSuccess;
         return launch<MidK2<RP>>(*a, s);
+      }
+      break;
+    case kTileMid3L:
+      if constexpr (RP <= 128) {
+        if (props) return tile_fill<Mid3L<RP>, 1>(props), hipSuccess;
+        return launch<Mid3L<RP>>(*a, s);
       }
       break;
     default:
