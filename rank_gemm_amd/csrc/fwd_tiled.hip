@@ -815,6 +815,11 @@ using MidK2 = Cfg<128, 128, 4, 2, RP, 3, 64, 2>;
 // slower elsewhere; with two stages 13.1 us but slower at larger K.
 template <int RP>
 using Mid3L = Cfg<128, 128, 4, 2, RP, 3, 64, 1, 4>;
+// 128 x 256 with wave tiles of 64 x 64 (fewer LDS bytes per MFMA than 32 x
+// 64) and four loaders, three stages: 8192 x 1024 x 2560 r32 44.4 us against
+// 50.5 on 128 x 128 (two workgroups per CU); 256 x 128 measured slower.
+template <int RP>
+using WideL = Cfg<128, 256, 2, 4, RP, 3, 64, 1, 4>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
 // measurements on the benchmark shapes:
@@ -831,7 +836,9 @@ using Mid3L = Cfg<128, 128, 4, 2, RP, 3, 64, 1, 4>;
 //    would have nothing to do): 128 x 128 with three stages and four loader
 //    waves (4096 x 1024 x 1024 r16: 13.0 us; without loaders 14.6, two
 //    stages 15.1; 2048 cubed r16: 22.4 vs 23.6 and 25.9 us);
-//  * else 128 x 128.
+//  * rank <= 32 past that: 128 x 256 with loaders (8192 x 1024 x 2560 r32:
+//    44.4 vs 50.5 us; the q_proj backward's dX product 176 vs 188 us);
+//  * else 128 x 128, two stages (two workgroups per CU).
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
   const int64_t mid_tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
@@ -849,7 +856,8 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
   if constexpr (RP <= 128) {
     if (mid_tiles <= 256) return launch<Mid3L<RP>>(a, s);
   }
-  return launch<Mid<RP>>(a, s);
+  if constexpr (RP <= 32) return launch<WideL<RP>>(a, s);
+  else return launch<Mid<RP>>(a, s);
 }
 
 // ---- selectable tile configurations (the tile tuner's search space).  The
@@ -922,6 +930,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 128) {
         if (props) return tile_fill<Mid3L<RP>, 1>(props), hipSuccess;
         return launch<Mid3L<RP>>(*a, s);
+      }
+      break;
+    case kTileWideL:
+      if constexpr (RP <= 32) {
+        if (props) return tile_fill<WideL<RP>, 1>(props), hipSuccess;
+        return launch<WideL<RP>>(*a, s);
       }
       break;
     default:
