@@ -322,16 +322,19 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *   7   128 x 128   16    1               r <= 64    (three stages, k split)
  *   8   128 x 128   12    1               r <= 128   (three stages, 4 loaders)
  *   9   128 x 256   12    1               r <= 32    (three stages, 4 loaders)
+ *  10   64 x 64      8    1               r <= 64    (four stages, 4 loaders)
+ *  11   64 x 32      8    1               r <= 64    (four stages, 4 loaders)
+ *  12   32 x 32      6    1               r <= 64    (four stages, 4 loaders)
  * ("T shared over g N tiles": a workgroup computes g consecutive output
  * tiles of one row block and the down-projection T only once.  Every id
- * stages 64 k per stage; 0 keeps eight stages, 6 to 9 three, the others
- * two.  "k split": two groups of eight waves compute the same tile,
+ * stages 64 k per stage; the stage counts not given are two.  0 keeps
+ * eight stages.  "k split": two groups of eight waves compute the same tile,
  * each from one 32-wide half of every stage, and their sums are added before
  * the up-projection; its results differ from the other ids' in rounding,
  * which all agree bit for bit with each other.  "4 loaders": four of the
  * waves only issue the stage loads, the other eight only multiply.)
  */
-#define LORA_TILE_COUNT 10
+#define LORA_TILE_COUNT 13
 
 typedef struct lora_tile_info {
     int32_t tile;        /* id */

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     int64_t ldt) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int BM = C::BM, BN = C::BN, RP = C::RP, TM = C::TM, TN = C::TN;
-  constexpr int WN = C::WN, NW = C::NW, STAGES = C::STAGES;
+  constexpr int WN = C::WN, STAGES = C::STAGES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -613,11 +613,15 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // Optional side output: the scaled down-projection s T of this M tile, as
   // the epilogue rounded it, stored transposed ([r, ldt], tokens contiguous)
   // by the workgroup of the first N tile.  Rows past M hold zeros (X rows
-  // past M read as zeros).  The backward takes s dY B from here.
+  // past M read as zeros); the last M tile also writes the zero rows from its
+  // end up to ldt, which can lie past it when BM is smaller than ldt's
+  // padding.  The backward takes s dY B from here.
   if (tout != nullptr && ng0 == 0 && g == 0) {
-    for (int e = tid; e < BM * r; e += C::NT) {
-      const int row = e % BM, j = e / BM;
-      if (m0 + row < ldt) tout[(int64_t)j * ldt + m0 + row] = ts[row * C::kTS + j];
+    const int rend = m0 + BM >= M ? (int)ldt : min(m0 + BM, (int)ldt);  // rows [m0, rend)
+    const int nrow = rend - m0;
+    for (int e = tid; e < nrow * r; e += C::NT) {
+      const int row = e % nrow, j = e / nrow;
+      tout[(int64_t)j * ldt + m0 + row] = row < BM ? ts[row * C::kTS + j] : uint16_t(0);
     }
   }
 
@@ -820,33 +824,41 @@ using Mid3L = Cfg<128, 128, 4, 2, RP, 3, 64, 1, 4>;
 // 50.5 on 128 x 128 (two workgroups per CU); 256 x 128 measured slower.
 template <int RP>
 using WideL = Cfg<128, 256, 2, 4, RP, 3, 64, 1, 4>;
+// Small tiles with four loaders and four stages, for grids that the 128 x
+// 128 tile would leave under-filled: the smaller the tile, the more
+// workgroups share the streaming of W (tall-skinny and decode-like shapes).
+// Measured with W streamed from HBM (16 rotating operand sets):
+// 1024 x 1024 x 2048 r16 on 64 x 64: 10.3 us (128 x 128: 16.4); 512 x 1024 x
+// 1024 r32 on 64 x 32: 6.7 us (64 x 32 without loaders, eight stages: 8.8);
+// 64 x 4096 x 4096 r16 on 32 x 32: 18.0 us (19.9).
+template <int RP>
+using SqL = Cfg<64, 64, 4, 1, RP, 4, 64, 1, 4>;
+template <int RP>
+using TallL = Cfg<64, 32, 4, 1, RP, 4, 64, 1, 4>;
+template <int RP>
+using SmallL = Cfg<32, 32, 2, 1, RP, 4, 64, 1, 4>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
-// measurements on the benchmark shapes:
-//  * rank <= 32 and at most 64 tokens, or fewer than 64 tiles of 128 x 128
-//    (three quarters of the 256 CUs idle): the 64 x 32 tile (512 x 1024 x
-//    1024 r32: 7.9 vs 11.1 us with loaders; at 64 tiles the loader tile
-//    wins, 1024 x 1024 x 2048 r16: 16.5 vs 20.6 us);
-//  * 256 x 256 when there are >= 256 such tiles and the last round of them
-//    is at least 80 % full (q_proj, 512 tiles: 160 vs 202 us; the q_proj
-//    backward's dX product, 320 tiles: 211 us vs 191 us on 128 x 128);
+// measurements on the benchmark shapes and on rotating operand sets:
+//  * 256 x 256 (r <= 64) when there are >= 256 such tiles and the last round
+//    of them is at least 80 % full (q_proj, 512 tiles: 160 vs 202 us; the
+//    q_proj backward's dX product, 320 tiles: 211 us vs 191 us on 128 x 128);
 //  * rank 128 with >= 512 128 x 128 tiles: T shared over 2 N tiles (square
 //    16384 x 8192 x 8192: 3.27 ms; over 4 tiles 3.73 ms; unshared 3.87 ms);
-//  * at most 256 128 x 128 tiles (one per CU, so a second resident workgroup
-//    would have nothing to do): 128 x 128 with three stages and four loader
-//    waves (4096 x 1024 x 1024 r16: 13.0 us; without loaders 14.6, two
-//    stages 15.1; 2048 cubed r16: 22.4 vs 23.6 and 25.9 us);
+//  * at most 256 tiles of 128 x 128: the largest loader tile (128 x 128,
+//    64 x 64, 64 x 32, 32 x 32) whose grid has at least 160 workgroups, else
+//    32 x 32.  128 x 128 keeps the work at 192 tiles (3072 x 1024 x 1024:
+//    12.6 vs 16.7 us on 64 x 64) and gives it up at 128 (2048 x 1024 x 4096:
+//    40.1 vs 38.4 us);
 //  * rank <= 32 past that: 128 x 256 with loaders (8192 x 1024 x 2560 r32:
 //    44.4 vs 50.5 us; the q_proj backward's dX product 176 vs 188 us);
 //  * else 128 x 128, two stages (two workgroups per CU).
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
-  const int64_t mid_tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if constexpr (RP <= 32) {
-    if (a.M <= 64 || mid_tiles < 64) return launch<Tall<RP>>(a, s);
-  }
+  auto grid = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  const int64_t mid_tiles = grid(128, 128);
   if constexpr (RP <= 64) {
-    const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+    const int64_t big_tiles = grid(256, 256);
     const int64_t rounds = (big_tiles + 255) / 256;
     if (big_tiles >= 256 && big_tiles * 5 >= rounds * 256 * 4) return launch<Big<RP>>(a, s);
   }
@@ -854,7 +866,16 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
     if (a.N > 128 && mid_tiles >= 512) return launch<Mid<RP>, 2>(a, s);
   }
   if constexpr (RP <= 128) {
-    if (mid_tiles <= 256) return launch<Mid3L<RP>>(a, s);
+    if (mid_tiles <= 256) {
+      constexpr int64_t kFill = 160;
+      if (mid_tiles >= kFill) return launch<Mid3L<RP>>(a, s);
+      if constexpr (RP <= 64) {
+        if (grid(64, 64) >= kFill) return launch<SqL<RP>>(a, s);
+        if (grid(64, 32) >= kFill) return launch<TallL<RP>>(a, s);
+        return launch<SmallL<RP>>(a, s);
+      }
+      return launch<Mid3L<RP>>(a, s);
+    }
   }
   if constexpr (RP <= 32) return launch<WideL<RP>>(a, s);
   else return launch<Mid<RP>>(a, s);
@@ -936,6 +957,24 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 32) {
         if (props) return tile_fill<WideL<RP>, 1>(props), hipSuccess;
         return launch<WideL<RP>>(*a, s);
+      }
+      break;
+    case kTileSqL:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<SqL<RP>, 1>(props), hipSuccess;
+        return launch<SqL<RP>>(*a, s);
+      }
+      break;
+    case kTileTallL:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<TallL<RP>, 1>(props), hipSuccess;
+        return launch<TallL<RP>>(*a, s);
+      }
+      break;
+    case kTileSmallL:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<SmallL<RP>, 1>(props), hipSuccess;
+        return launch<SmallL<RP>>(*a, s);
       }
       break;
     default:
