@@ -279,6 +279,8 @@ BENCH_SHAPES = [
     (1, 4096, 4096, 16), (8, 4096, 4096, 16), (64, 4096, 4096, 16),   # decode-shaped
     (8192, 2560, 4096, 32),      # the q_proj backward's dX product
     (2048, 2048, 2048, 16),      # a square that fills 256 128 x 128 tiles
+    (1024, 1024, 2048, 16),      # 64 128 x 128 tiles: a smaller tile fills the CUs
+    (256, 4096, 4096, 16),       # few tokens, W streamed by many workgroups
 ]
 
 
