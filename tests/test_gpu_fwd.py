@@ -108,6 +108,27 @@ def test_large_rank_groups_sampled_rows(gpu_lib, M, N, K, r):
     assert np.isfinite(as_f64(got)).all()
 
 
+@pytest.mark.parametrize("M,N,K,r", [(256, 4096, 4096, 16), (1000, 1024, 2056, 40),
+                                     (512, 1032, 1024, 32), (64, 4096, 4096, 64),
+                                     (40, 2048, 2048, 24)])
+def test_small_grid_loader_tiles_sampled_rows(gpu_lib, M, N, K, r):
+    """Grids with few 128 x 128 tiles run on the 64 x 64, 64 x 32 and 32 x 32
+    tiles with loader waves (W streamed by many workgroups): full size,
+    ragged N and K, ranks below the padded rank, sampled rows against the
+    oracle, and the same result on a second call."""
+    c = synth.FwdCase(f"small{M}x{N}x{K}r{r}", 95, r, M, N, K, r, 2.0 * r, "bf16")
+    t = c.make()
+    got = _run(gpu_lib, t, c.scale)
+    again = _run(gpu_lib, t, c.scale)
+    rows = sample_rows(M, 32, seed=r)
+    ref = _oracle_rows(t, c.scale, rows)
+    err = rel_fro(as_f64(got[rows]), ref)
+    print(f"{c.name}: rows={len(rows)} rel_fro={err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.isfinite(as_f64(got)).all()
+    assert np.array_equal(got, again)
+
+
 # ------------------------------------------------------ shapes and edges
 
 def _rand_case(seed, M, N, K, r, dtype, var_b=0.02):
