@@ -8,11 +8,13 @@
 // workgroup per output tile, and the [tokens, r] intermediate never leaves the
 // chip (accumulator registers, then LDS for the operand re-layout).
 //
-// Per workgroup (BM x BN output tile, WM x WN waves, each wave a grid of
-// 16 x 16 MFMA blocks):
+// Per workgroup (BM x BN output tile; WM x WN multiplying waves, each a grid
+// of 16 x 16 MFMA blocks, twice that with the k split; PW loader waves or
+// none, see Cfg):
 //   K loop, BK (32 or 64) per stage, STAGES-deep ring of LDS stages:
 //     X[BM x BK], W[BN x BK] and A[RP x BK] go straight from global memory to
-//     LDS (buffer_load ... lds, 16 B per lane, no register staging).  Each
+//     LDS (buffer_load ... lds, 16 B per lane, no register staging), issued
+//     by the loader waves, or by the multiplying waves when there are none.  Each
 //     buffer resource starts at the tile's first row and ends at the last
 //     valid row, so rows past M, N or r and the K tail read as zeros.
 //     16-B chunks are XOR-swizzled per row so that MFMA operand reads
