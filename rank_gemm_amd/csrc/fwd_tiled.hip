@@ -54,10 +54,10 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // KS = 2 splits every stage's k range between two groups of WM x WN waves
 // that compute the same BM x BN tile: group g multiplies k32 half g of each
-// stage, and the epilogue adds the two partial sums through LDS.  Each wave
-// then holds a tile KS times taller for the same LDS reads per k32, which
-// cuts the LDS bytes read per MFMA (the K loop of the 128 x 128 tile is
-// bound by LDS bandwidth), while keeping two waves per SIMD.
+// stage, and the epilogue adds the two partial sums through LDS.  It doubles
+// the waves per tile (more latency hiding) without more LDS reads per stage,
+// or, with half as many waves per group, gives each wave a tile twice as
+// large for the same number of waves.
 //
 // PW > 0 adds PW loader waves that issue every stage's loads while the
 // WM x WN x KS multiplying waves only read LDS and run MFMAs.  A wave stalls
@@ -190,9 +190,10 @@ __device__ __forceinline__ void t_update_ab(const u32x4 (&a)[C::TM], const u32x4
     tacc[sl] = mfma16x16x32(a[t_ring_slot<C>(sl)], t[t_frag<C>(sl)], tacc[sl]);
 }
 
-// Wait until this wave's loads of all but its `Newer` most recent stages have
-// landed.  Loads complete in issue order, so the count must be this wave's
-// own per-stage load count: waves that also load an A row issue one more.
+// Wait until the loads of loader `wave` (its index among the waves that issue
+// stage loads) of all but its `Newer` most recent stages have landed.  Loads
+// complete in issue order, so the count must be this loader's own per-stage
+// load count: loaders that also load an A row issue one more.
 template <class C, int Newer, bool WT = true>
 __device__ __forceinline__ void wait_stages(int wave) {
   if constexpr (!WT) {
@@ -208,10 +209,10 @@ __device__ __forceinline__ void wait_stages(int wave) {
   wait_vmcnt<Newer * C::kLoadsLo>();
 }
 
-// Issue one stage of direct-to-LDS loads for this wave: its X slots, its W
-// slots and (waves below kAN) its A slot.  Slot s of a matrix is the wave's
-// slot 0 plus s * NW 1-KiB loads, i.e. a wave-uniform byte stride.  Lanes
-// whose 16-B chunk lies past K read zeros.
+// Issue one stage of direct-to-LDS loads for loader `wave`: its X slots, its
+// W slots and (loaders below kAN) its A slot.  Slot s of a matrix is the
+// loader's slot 0 plus s * LW 1-KiB loads, i.e. a wave-uniform byte stride.
+// Lanes whose 16-B chunk lies past K read zeros.
 template <class C, bool WT = true>
 __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0, int K, int wave,
                                             int lchunk, __amdgpu_buffer_rsrc_t rx,
@@ -314,8 +315,10 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       (void*)A, 0, (int)(r * lda * 2), 0x00020000);
 
   // Lane i of a 1-KiB load writes staged row (q * rows_per_load + i / chunks),
-  // physical chunk i % chunks, so it fetches logical chunk (i % chunks) ^ swz(row).  Wave w issues X loads
-  // q = w, w + NW, ..., the same for W, and A load q = w when w < RP / 16.
+  // physical chunk i % chunks, so it fetches logical chunk (i % chunks) ^
+  // swz(row).  Loader w (a loader wave, or every wave of a tile without
+  // loaders) issues X loads q = w, w + LW, ..., the same for W, and A load
+  // q = w when w < kAN.
   constexpr int BK = C::BK, kRowB = C::kRowB, kRPL = C::kRowsPerLoad;
   const int lrow_in_load = lane / C::kChunks;
   const int lchunk = (lane % C::kChunks) ^ swz<BK>(lrow_in_load);
