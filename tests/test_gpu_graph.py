@@ -34,7 +34,9 @@ def _replays_match_eager(launch, outs, replays=3):
             assert to_host(o).tobytes() == e.tobytes(), f"replay {k}"
 
 
-@pytest.mark.parametrize("M", [1, 64, 300])
+# M = 1: decode kernel; 64: 32 x 32 loader tile; 300: 64 x 32 loader tile;
+# 4096: 128 x 128 loader tile; 8192: 128 x 256 loader tile.
+@pytest.mark.parametrize("M", [1, 64, 300, 4096, 8192])
 def test_fwd_graph_replay(gpu_lib, M):
     import torch
     c = synth.FwdCase(f"g{M}", 97, M, M, 1024, 768, 16, 32.0, "bf16")
