@@ -21,7 +21,7 @@
 //      intermediate is s dY B = s G, which it also stores as (s G)^T
 //   3. tc_kernel     dA and dB partial sums per token range, fp32
 //   4. red_kernel    dA, dB = round(ordered sum of the partials)
-// Without dX: prep_kernel (B^T), proj_kernel (s T and s G), tc_kernel,
+// Without dX: prep_kernel (B^T), proj_kernel (s G and s T), tc_kernel,
 // red_kernel.  With no tokens, red_kernel alone writes dA = 0 and dB = 0.
 // (Folding the reduction into the token contraction, the last workgroup of
 // a column tile adding the others' partials, needs an agent-scope release
@@ -121,12 +121,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------- projection
-// P^T[j, m] = round(scale * sum_c Z[m, c] U[j, c]) for a tile of BT tokens,
-// both operands contraction-contiguous.  Job 0: Z = X, U = A (s T); job 1:
-// Z = dY, U = B^T (s G, when the input gradient is not computed; otherwise the
-// dX kernel provides it).  Each wave owns 16 tokens and runs the contraction in
-// order, 32 at a time, with the operands in the same MFMA roles as the tiled
-// forward kernel's down-projection: both produce bitwise the same s G.
+// P^T[j, m] = round(scale * sum_c Z[m, c] U[j, c]) for a tile of 16 tokens,
+// both operands contraction-contiguous: s T (Z = X, U = A), and s G (Z = dY,
+// U = B^T) when dX is not computed (otherwise the dX kernel provides it).
+// The contraction is split over the KW waves of a workgroup: wave w takes the
+// 64-wide stages w, w + KW, ... through a ring of its own (no barriers inside
+// the loop), and wave 0 adds the KW partial sums in wave order.  One wave
+// walking the whole contraction of its 16 tokens keeps too few loads in
+// flight and runs at latency, not bandwidth.  s G summed this way is rounded
+// differently from the dX kernel's, so dA with and without dX agree to
+// rounding, not bitwise; each is deterministic.
 struct ProjJob {
   const uint16_t* Z;
   int64_t ldz;
@@ -136,23 +140,19 @@ struct ProjJob {
   uint16_t* Pt;
 };
 
-// NW_ waves per workgroup, BT = 16 NW_ tokens: fewer waves per workgroup for
-// fewer tokens, so that the grid still spreads over the CUs.
-template <int RP, int NW_>
-struct Prj {
-  static constexpr int NW = NW_, BT = 16 * NW, NT = NW * kWave, RB = RP / 16;
-  static constexpr int kRows = BT + RP;          // staged rows per stage: tokens, then ranks
-  static constexpr int kStageB = kRows * 128;    // 64 contraction values per row
-  static constexpr int kZL = BT / 8;             // Z loads per stage (two per wave), first
-  static constexpr int kLoads = kRows / 8;       // 1-KiB loads per stage
-  static constexpr int kUL = (RP / 8 + NW - 1) / NW;  // U load slots per wave
-  static constexpr int kLo = kLoads / NW, kHi = kLo + (kLoads % NW != 0 ? 1 : 0);
-  // Ring depth: up to 64 KiB, and the vmcnt of STAGES - 2 stages in flight
-  // within its 6-bit field.
-  static constexpr int STAGES = cmini(clampi(64 * 1024 / kStageB, 2, 6), 2 + 63 / kHi);
-  static constexpr int kLds = STAGES * kStageB;
-  static_assert(kZL == 2 * NW, "two Z loads per wave");
-  static_assert((STAGES - 2) * kHi <= 63, "vmcnt range");
+template <int RP, int KW_>
+struct PrjK {
+  static constexpr int KW = KW_, NT = KW * kWave, RB = RP / 16;
+  static constexpr int kStageB = (16 + RP) * 128;  // 16 token rows, then RP rank rows
+  static constexpr int kLoads = (16 + RP) / 8;     // 1-KiB loads per stage, all one wave's
+  // Ring depth per wave: up to 4 stages within the LDS and the vmcnt of
+  // STAGES - 2 stages in flight within its 6-bit field; at least 2.
+  static constexpr int STAGES = cmini(cmini(4, 160 * 1024 / (KW * kStageB)), 2 + 63 / kLoads);
+  static constexpr int kRing = STAGES * kStageB;
+  static constexpr int kRed = KW * RB * kWave * 16;  // partial sums, after the loop
+  static constexpr int kLds = cmaxi(cmaxi(KW * kRing, kRed), kPrepTileB);
+  static_assert(STAGES >= 2, "LDS budget");
+  static_assert((STAGES - 2) * kLoads <= 63, "vmcnt range");
   static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
@@ -169,100 +169,115 @@ __device__ __forceinline__ void wait_own(int wave) {
   wait_vmcnt<Newer * Lo>();
 }
 
-// Blocks x >= prep_from run the preparation work instead (one launch for
-// both when the projection does not need B^T); their LDS is the ring's.
-template <int RP, int NW>
-__global__ __launch_bounds__(NW * kWave) void proj_kernel(int M, int r, float scale,
-                                                               ProjJob j0, ProjJob j1,
-                                                               int64_t ldp, PrepArgs pa,
-                                                               int prep_from) {
-  using P = Prj<RP, NW>;
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  if ((int)blockIdx.x >= prep_from) {
-    prep_block(pa, blockIdx.x - prep_from, threadIdx.x, P::NT, *reinterpret_cast<PrepTile*>(smem));
-    return;
-  }
-  const ProjJob jb = blockIdx.y == 0 ? j0 : j1;
+template <int RP, int KW>
+__device__ __forceinline__ void proj_split(int M, int r, float scale, const ProjJob& jb,
+                                           int64_t ldp, int tile, unsigned char* smem) {
+  using P = PrjK<RP, KW>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, lk = lane >> 4;
-  const int m0 = blockIdx.x * P::BT;
+  const int m0 = tile * 16;
   const int C = jb.C;
 
   // Z rows of the tile (rows past M read zeros); U rows past r read zeros.
-  const int zrows = max(0, min(P::BT, M - m0));
+  const int zrows = max(0, min(16, M - m0));
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(jb.Z + (int64_t)m0 * jb.ldz), 0, (int)(zrows * jb.ldz * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t ru =
       __builtin_amdgcn_make_buffer_rsrc((void*)jb.U, 0, (int)(r * jb.ldu * 2), 0x00020000);
-  // Lane i of a 1-KiB load writes row 8q + i / 8, physical chunk i % 8.
-  // Wave w issues Z loads q = w and w + NW and U loads kZL + w + NW s.
+  // Lane i of 1-KiB load q writes row 8 q + i / 8, physical chunk i % 8:
+  // loads 0-1 the 16 token rows, loads 2.. the rank rows.
   const int lrl = lane >> 3;
   const int lch = (lane & 7) ^ lrl;
-  const uint32_t vz = (uint32_t)((8 * wave + lrl) * jb.ldz * 2 + lch * 16);
-  const uint32_t sz = (uint32_t)(8 * P::NW * jb.ldz * 2);
-  const uint32_t vu = (uint32_t)((8 * wave + lrl) * jb.ldu * 2 + lch * 16);
-  const uint32_t su = (uint32_t)(8 * P::NW * jb.ldu * 2);
+  const uint32_t vz = (uint32_t)(lrl * jb.ldz * 2 + lch * 16);
+  const uint32_t vu = (uint32_t)(lrl * jb.ldu * 2 + lch * 16);
+  unsigned char* ring = smem + wave * P::kRing;
 
-  auto issue = [&](int st) {
-    unsigned char* base = smem + (st % P::STAGES) * P::kStageB;
+  auto issue = [&](int st, int slot) {
+    unsigned char* base = ring + slot * P::kStageB;
     const int c0 = st * 64;
     const bool kin = c0 + lch * 8 < C;
     const uint32_t cb = (uint32_t)c0 * 2;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(base + (wave + s * P::NW) * 1024),
-                                               16, off_or_oob(kin, vz + sgpr(s * sz + cb)), 0, 0,
-                                               0);
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rz, (lds_void*)(base + q * 1024), 16,
+          off_or_oob(kin, vz + sgpr((uint32_t)(8 * q * jb.ldz * 2) + cb)), 0, 0, 0);
 #pragma unroll
-    for (int s = 0; s < P::kUL; ++s) {
-      const int p = wave + s * P::NW;  // U load index (stage load kZL + p)
-      if (p < RP / 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ru, (lds_void*)(base + (P::kZL + p) * 1024), 16,
-            off_or_oob(kin, vu + sgpr(s * su + cb)), 0, 0, 0);
-    }
+    for (int q = 0; q < RP / 8; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ru, (lds_void*)(base + (2 + q) * 1024), 16,
+          off_or_oob(kin, vu + sgpr((uint32_t)(8 * q * jb.ldu * 2) + cb)), 0, 0, 0);
   };
 
   f32x4 acc[P::RB];
 #pragma unroll
   for (int i = 0; i < P::RB; ++i) acc[i] = zero4();
 
+  // This wave's stages: wave + KW i for i < mine; the prefetches past them
+  // read zeros.
   const int nk = (C + 63) / 64;
+  const int mine = nk > wave ? (nk - wave + KW - 1) / KW : 0;
 #pragma unroll
-  for (int s = 0; s < P::STAGES - 1; ++s) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_own<P::kLo, P::kHi, P::kLoads, P::NW, P::STAGES - 2>(wave);
+  for (int i = 0; i < P::STAGES - 1; ++i) issue(wave + KW * i, i);
+  int slot = 0;
+  for (int i = 0; i < mine; ++i) {
+    wait_vmcnt<(P::STAGES - 2) * P::kLoads>();
     wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    issue(kt + P::STAGES - 1);
-    const unsigned char* sb = smem + (kt % P::STAGES) * P::kStageB;
+    issue(wave + KW * (i + P::STAGES - 1), slot == 0 ? P::STAGES - 1 : slot - 1);
+    const unsigned char* sb = ring + slot * P::kStageB;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const u32x4 z = *reinterpret_cast<const u32x4*>(sb + row_off(16 * wave + lrow, 4 * u + lk));
+      const u32x4 z = *reinterpret_cast<const u32x4*>(sb + row_off(lrow, 4 * u + lk));
 #pragma unroll
-      for (int i = 0; i < P::RB; ++i) {
+      for (int j = 0; j < P::RB; ++j) {
         const u32x4 w =
-            *reinterpret_cast<const u32x4*>(sb + row_off(P::BT + 16 * i + lrow, 4 * u + lk));
-        acc[i] = mfma16x16x32(z, w, acc[i]);
+            *reinterpret_cast<const u32x4*>(sb + row_off(16 + 16 * j + lrow, 4 * u + lk));
+        acc[j] = mfma16x16x32(z, w, acc[j]);
       }
     }
+    slot = slot + 1 == P::STAGES ? 0 : slot + 1;
   }
   // Loads of the stages past the end (zeros) may still be landing in the ring.
   wait_vmcnt<0>();
-
-  // acc[i] lane: rank 16 i + lrow, tokens m0 + 16 w + 4 lk + 0..3 (< ldp: the
-  // grid covers ldp / BT tiles).
-  const int64_t m = m0 + 16 * wave + 4 * lk;
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
-  for (int i = 0; i < P::RB; ++i) {
-    const int j = 16 * i + lrow;
-    if (j < r) {
-      uint32_t* o = reinterpret_cast<uint32_t*>(jb.Pt + (int64_t)j * ldp + m);
-      o[0] = pack_bf2(scale * acc[i][0], scale * acc[i][1]);
-      o[1] = pack_bf2(scale * acc[i][2], scale * acc[i][3]);
+  for (int j = 0; j < P::RB; ++j) red[(wave * P::RB + j) * kWave + lane] = acc[j];
+  __syncthreads();
+  if (wave != 0) return;
+
+  // acc[j] lane: rank 16 j + lrow, tokens m0 + 4 lk + 0..3 (< ldp: the grid
+  // covers ldp / 16 tiles).
+  const int64_t m = m0 + 4 * lk;
+#pragma unroll
+  for (int j = 0; j < P::RB; ++j) {
+    f32x4 sum = red[j * kWave + lane];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) sum += red[(w * P::RB + j) * kWave + lane];
+    const int jr = 16 * j + lrow;
+    if (jr < r) {
+      uint32_t* o = reinterpret_cast<uint32_t*>(jb.Pt + (int64_t)jr * ldp + m);
+      o[0] = pack_bf2(scale * sum[0], scale * sum[1]);
+      o[1] = pack_bf2(scale * sum[2], scale * sum[3]);
     }
   }
+}
+
+// Blocks [0, gtiles): s G (without dX); [gtiles, gtiles + tiles): s T; the
+// rest: the preparation (with dX), in the rings' LDS.
+template <int RP, int KW>
+__global__ __launch_bounds__(KW * kWave) void proj_kernel(int M, int r, float scale, ProjJob jt,
+                                                          ProjJob jg, int64_t ldp, PrepArgs pa,
+                                                          int gtiles, int tiles) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int b = blockIdx.x;
+  if (b < gtiles)
+    proj_split<RP, KW>(M, r, scale, jg, ldp, b, smem);
+  else if (b < gtiles + tiles)
+    proj_split<RP, KW>(M, r, scale, jt, ldp, b - gtiles, smem);
+  else
+    prep_block(pa, b - gtiles - tiles, threadIdx.x, KW * kWave, *reinterpret_cast<PrepTile*>(smem));
 }
 
 // Sum of S float4 partials p[0], p[stride], ... added in index order; the
@@ -441,33 +456,35 @@ __global__ __launch_bounds__(64) void red_kernel(int S, int r, int RP, int K, in
     if (j + q < r) out[q] = f2bf(s4[q]);
 }
 
-// The projection (jobs 1: s T; 2: s T and s G), optionally followed in the
-// same grid by the preparation blocks (only with one job: blocks of a second
-// job row would repeat them).
-template <int RP, int NW>
+// The projection: s T, and either s G (want_g) or the preparation blocks.
+template <int RP, int KW>
 hipError_t launch_proj(const BwdArgs& a, const BwdPlan& p, const ProjJob& jt, const ProjJob& jg,
-                       int jobs, const PrepArgs* pre, hipStream_t s) {
-  using P = Prj<RP, NW>;
-  auto kern = proj_kernel<RP, NW>;
-  const int lds = cmaxi(P::kLds, kPrepTileB);
+                       bool want_g, const PrepArgs* pre, hipStream_t s) {
+  auto kern = proj_kernel<RP, KW>;
+  constexpr int lds = PrjK<RP, KW>::kLds;
   static std::atomic<uint64_t> done{0};
   if (hipError_t e = ensure_lds(kern, lds, done); e != hipSuccess) return e;
-  const int tiles = (int)(p.ldp / P::BT);
-  const int64_t extra = (pre != nullptr && jobs == 1) ? prep_blocks(*pre, P::NT) : 0;
+  const int tiles = (int)(p.ldp / 16);
+  const int gtiles = want_g ? tiles : 0;
+  const int64_t extra = pre != nullptr ? prep_blocks(*pre, KW * kWave) : 0;
   const PrepArgs none{};
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles + extra), jobs), dim3(P::NT), lds, s, (int)a.M,
-                     (int)a.r, a.scale, jt, jg, p.ldp, extra > 0 ? *pre : none, tiles);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gtiles + tiles + extra)), dim3(KW * kWave), lds, s,
+                     (int)a.M, (int)a.r, a.scale, jt, jg, p.ldp, extra > 0 ? *pre : none, gtiles,
+                     tiles);
   return hipGetLastError();
 }
 
+// Waves per workgroup (KW): about 1024 waves over the 16-token tiles, at
+// most 4 (2 for the 256 ranks, whose rings take the LDS).  The choice
+// depends on the tokens alone, so s T, hence dB, is bitwise the same with
+// and without dX.
 template <int RP>
-hipError_t launch_proj_nw(const BwdArgs& a, const BwdPlan& p, const ProjJob& jt,
-                          const ProjJob& jg, int jobs, const PrepArgs* pre, hipStream_t s) {
-  // The most waves per workgroup that still gives 256 projection workgroups.
-  const int64_t tiles16 = p.ldp / 16 * jobs;
-  if (tiles16 >= 4 * 256) return launch_proj<RP, 4>(a, p, jt, jg, jobs, pre, s);
-  if (tiles16 >= 2 * 256) return launch_proj<RP, 2>(a, p, jt, jg, jobs, pre, s);
-  return launch_proj<RP, 1>(a, p, jt, jg, jobs, pre, s);
+hipError_t launch_proj_kw(const BwdArgs& a, const BwdPlan& p, const ProjJob& jt,
+                          const ProjJob& jg, bool want_g, const PrepArgs* pre, hipStream_t s) {
+  const int64_t tiles = p.ldp / 16;
+  if (tiles <= 256) return launch_proj<RP, RP < 256 ? 4 : 2>(a, p, jt, jg, want_g, pre, s);
+  if (tiles <= 512) return launch_proj<RP, 2>(a, p, jt, jg, want_g, pre, s);
+  return launch_proj<RP, 1>(a, p, jt, jg, want_g, pre, s);
 }
 
 // Launches 1-3 for M > 0 (see the top of the file).
@@ -483,7 +500,7 @@ hipError_t launch_rank(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, bo
   const ProjJob jg{static_cast<const uint16_t*>(a.dY), a.lddy, N, Bt, p.ldbt, Gt};
   if (want_dx) {
     // 1. s T with the transposes; 2. dX, whose rank intermediate is s G.
-    if (hipError_t e = launch_proj_nw<RP>(a, p, jt, jg, 1, &pre, s); e != hipSuccess) return e;
+    if (hipError_t e = launch_proj_kw<RP>(a, p, jt, jg, false, &pre, s); e != hipSuccess) return e;
     const uint16_t* Wt = reinterpret_cast<const uint16_t*>(ws + p.off_wt);
     const uint16_t* At = reinterpret_cast<const uint16_t*>(ws + p.off_at);
     const FwdArgs f{a.M, a.K, a.N, a.r, a.dY, a.lddy, Wt, p.ldwt, Bt, p.ldbt, At, p.ldat,
@@ -495,7 +512,7 @@ hipError_t launch_rank(const BwdArgs& a, const BwdPlan& p, unsigned char* ws, bo
       hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, pre);
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
-    if (hipError_t e = launch_proj_nw<RP>(a, p, jt, jg, 2, nullptr, s); e != hipSuccess) return e;
+    if (hipError_t e = launch_proj_kw<RP>(a, p, jt, jg, true, nullptr, s); e != hipSuccess) return e;
   }
   // 3. Token contraction, reduction included.
   const int tiles0 = (K + 63) / 64, tiles1 = (N + 63) / 64;
