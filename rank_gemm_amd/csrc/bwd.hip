@@ -56,11 +56,9 @@ __device__ __forceinline__ int tr_off(int row, int col) {
 }
 
 // ---------------------------------------------------------------- transposes
-// Preparation work, in blocks of nt threads: blocks [0, wtiles) each write
-// a 64 x 64 tile of W^T (16-B loads of W rows into LDS, 16-B stores of W^T
-// rows; N and K are multiples of 8, so a chunk is either wholly inside or
-// wholly outside); the following blocks write B^T and A^T, one element per
-// thread.
+// Preparation work, in blocks of nt threads (nt / 64 waves): the first
+// blocks write W^T, one 64 x 64 tile per wave; the following blocks write B^T
+// and A^T, one element per thread.
 struct PrepArgs {
   int N, K, r, wtiles_k, wtiles;
   const uint16_t* W; int64_t ldw; uint16_t* Wt; int64_t ldwt;
@@ -68,40 +66,47 @@ struct PrepArgs {
   const uint16_t* A; int64_t lda; uint16_t* At; int64_t ldat;
 };
 
-typedef uint16_t PrepTile[64][72];  // 144-B rows
-constexpr int kPrepTileB = 64 * 72 * 2;
-
 // Blocks the preparation needs with nt threads per block.
 inline int64_t prep_blocks(const PrepArgs& a, int nt) {
+  const int wpb = nt / kWave;
   const int64_t small = (int64_t)a.r * a.N + (int64_t)a.K * a.r;
-  return a.wtiles + (small + nt - 1) / nt;
+  return (a.wtiles + wpb - 1) / wpb + (small + nt - 1) / nt;
 }
 
-__device__ __forceinline__ void prep_block(const PrepArgs& a, int b, int tid, int nt,
-                                           PrepTile& tile) {
-  if (b < a.wtiles) {
-    const int n0 = (b / a.wtiles_k) * 64, k0 = (b % a.wtiles_k) * 64;
-    for (int c = tid; c < 512; c += nt) {
-      const int row = c >> 3, ch = c & 7;
-      const int n = n0 + row, k = k0 + ch * 8;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (n < a.N && k < a.K) v = *reinterpret_cast<const u32x4*>(a.W + (int64_t)n * a.ldw + k);
-      *reinterpret_cast<u32x4*>(&tile[row][ch * 8]) = v;
-    }
-    __syncthreads();
-    for (int c = tid; c < 512; c += nt) {
-      const int row = c >> 3, ch = c & 7;  // row: k offset, ch: chunk of 8 n
-      const int k = k0 + row, n = n0 + ch * 8;
-      if (k >= a.K || n >= a.N) continue;
-      uint32_t w[4];
+// W^T tile t through registers: lane l owns the 8 x 8 block at W rows
+// n0 + 8 (l / 8) + 0..7 and columns k0 + 8 (l % 8) + 0..7, read as eight
+// 16-B row loads and written as eight 16-B rows of W^T; each instruction
+// moves whole 128-B segments (8 lanes per row), with no LDS and no barrier.
+// N and K are multiples of 8, so a block is wholly inside or outside.
+__device__ __forceinline__ void prep_wt_tile(const PrepArgs& a, int t, int lane) {
+  const int n = (t / a.wtiles_k) * 64 + 8 * (lane >> 3);
+  const int k = (t % a.wtiles_k) * 64 + 8 * (lane & 7);
+  if (n >= a.N || k >= a.K) return;
+  u32x4 v[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        w[q] = uint32_t(tile[ch * 8 + 2 * q][row]) | (uint32_t(tile[ch * 8 + 2 * q + 1][row]) << 16);
-      *reinterpret_cast<u32x4*>(a.Wt + (int64_t)k * a.ldwt + n) = u32x4{w[0], w[1], w[2], w[3]};
+  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const u32x4*>(a.W + (int64_t)(n + i) * a.ldw + k);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // W^T row k + j: element j of each of the eight W rows, two per word.
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x0 = v[2 * q][j >> 1], x1 = v[2 * q + 1][j >> 1];
+      w[q] = (j & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
     }
+    *reinterpret_cast<u32x4*>(a.Wt + (int64_t)(k + j) * a.ldwt + n) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+__device__ __forceinline__ void prep_block(const PrepArgs& a, int b, int tid, int nt) {
+  const int wpb = nt / kWave;
+  const int wblocks = (a.wtiles + wpb - 1) / wpb;
+  if (b < wblocks) {
+    const int t = b * wpb + (tid >> 6);
+    if (t < a.wtiles) prep_wt_tile(a, t, tid & 63);
     return;
   }
-  int64_t e = (int64_t)(b - a.wtiles) * nt + tid;
+  int64_t e = (int64_t)(b - wblocks) * nt + tid;
   const int64_t nb = (int64_t)a.r * a.N;
   if (e < nb) {
     const int j = (int)(e / a.N), n = (int)(e % a.N);
@@ -116,8 +121,7 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int b, int tid, in
 }
 
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-  __shared__ __attribute__((aligned(16))) PrepTile tile;
-  prep_block(a, blockIdx.x, threadIdx.x, 256, tile);
+  prep_block(a, blockIdx.x, threadIdx.x, 256);
 }
 
 // ---------------------------------------------------------------- projection
@@ -150,7 +154,7 @@ struct PrjK {
   static constexpr int STAGES = cmini(cmini(4, 160 * 1024 / (KW * kStageB)), 2 + 63 / kLoads);
   static constexpr int kRing = STAGES * kStageB;
   static constexpr int kRed = KW * RB * kWave * 16;  // partial sums, after the loop
-  static constexpr int kLds = cmaxi(cmaxi(KW * kRing, kRed), kPrepTileB);
+  static constexpr int kLds = cmaxi(KW * kRing, kRed);
   static_assert(STAGES >= 2, "LDS budget");
   static_assert((STAGES - 2) * kLoads <= 63, "vmcnt range");
   static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -265,7 +269,7 @@ __device__ __forceinline__ void proj_split(int M, int r, float scale, const Proj
 }
 
 // Blocks [0, gtiles): s G (without dX); [gtiles, gtiles + tiles): s T; the
-// rest: the preparation (with dX), in the rings' LDS.
+// rest: the preparation (with dX).
 template <int RP, int KW>
 __global__ __launch_bounds__(KW * kWave) void proj_kernel(int M, int r, float scale, ProjJob jt,
                                                           ProjJob jg, int64_t ldp, PrepArgs pa,
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(KW * kWave) void proj_kernel(int M, int r, float sc
   else if (b < gtiles + tiles)
     proj_split<RP, KW>(M, r, scale, jt, ldp, b - gtiles, smem);
   else
-    prep_block(pa, b - gtiles - tiles, threadIdx.x, KW * kWave, *reinterpret_cast<PrepTile*>(smem));
+    prep_block(pa, b - gtiles - tiles, threadIdx.x, KW * kWave);
 }
 
 // Sum of S float4 partials p[0], p[stride], ... added in index order; the
