@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 8
+#define LORA_ABI_VERSION 9
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -325,6 +325,7 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *  10   64 x 64      8    1               r <= 64    (four stages, 4 loaders)
  *  11   64 x 32      8    1               r <= 64    (four stages, 4 loaders)
  *  12   32 x 32      6    1               r <= 64    (four stages, 4 loaders)
+ *  13   256 x 160   12    1               r <= 32    (two stages, 4 loaders)
  * ("T shared over g N tiles": a workgroup computes g consecutive output
  * tiles of one row block and the down-projection T only once.  Every id
  * stages 64 k per stage; the stage counts not given are two.  0 keeps
@@ -334,7 +335,7 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  * which all agree bit for bit with each other.  "4 loaders": four of the
  * waves only issue the stage loads, the other eight only multiply.)
  */
-#define LORA_TILE_COUNT 13
+#define LORA_TILE_COUNT 14
 
 typedef struct lora_tile_info {
     int32_t tile;        /* id */

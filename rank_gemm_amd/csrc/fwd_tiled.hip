@@ -829,6 +829,13 @@ using Mid3L = Cfg<128, 128, 4, 2, RP, 3, 64, 1, 4>;
 // 50.5 on 128 x 128 (two workgroups per CU); 256 x 128 measured slower.
 template <int RP>
 using WideL = Cfg<128, 256, 2, 4, RP, 3, 64, 1, 4>;
+// 256 x 160 with four loaders, two stages (8 waves of 64 x 80: 0.45 LDS
+// fragment reads per MFMA), for grids whose 128 x 256 tiles leave the last
+// round of 256 CUs part-empty: 8192 x 2560 outputs, K 4096, r32 (the q_proj
+// backward's dX product) take 512 such tiles, two full rounds, 162 us
+// against 183.5 us on 640 tiles of 128 x 256 (2.5 rounds).
+template <int RP>
+using BigNL = Cfg<256, 160, 4, 2, RP, 2, 64, 1, 4>;
 // Small tiles with four loaders and four stages, for grids that the 128 x
 // 128 tile would leave under-filled: the smaller the tile, the more
 // workgroups share the streaming of W (tall-skinny and decode-like shapes).
@@ -856,7 +863,9 @@ using SmallL = Cfg<32, 32, 2, 1, RP, 4, 64, 1, 4>;
 //    12.6 vs 16.7 us on 64 x 64) and gives it up at 128 (2048 x 1024 x 4096:
 //    40.1 vs 38.4 us);
 //  * rank <= 32 past that: 128 x 256 with loaders (8192 x 1024 x 2560 r32:
-//    44.4 vs 50.5 us; the q_proj backward's dX product 176 vs 188 us);
+//    44.4 vs 50.5 us), or 256 x 160 with loaders when its grid fills the
+//    rounds of 256 workgroups at least 10 % better (the q_proj backward's dX
+//    product: 162 us, against 183.5 on 128 x 256 and 188 on 128 x 128);
 //  * else 128 x 128, two stages (two workgroups per CU).
 template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
@@ -882,8 +891,18 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
       return launch<Mid3L<RP>>(a, s);
     }
   }
-  if constexpr (RP <= 32) return launch<WideL<RP>>(a, s);
-  else return launch<Mid<RP>>(a, s);
+  if constexpr (RP <= 32) {
+    // Output elements per workgroup slot of the grid rounded up to whole
+    // rounds of 256: 256 x 160 when it fills the rounds clearly better.
+    auto fill = [&](int bm, int bn) {
+      const int64_t t = grid(bm, bn);
+      return (double)a.M * (double)a.N / ((double)((t + 255) / 256) * 256.0 * bm * bn);
+    };
+    if (fill(256, 160) >= 1.1 * fill(128, 256)) return launch<BigNL<RP>>(a, s);
+    return launch<WideL<RP>>(a, s);
+  } else {
+    return launch<Mid<RP>>(a, s);
+  }
 }
 
 // ---- selectable tile configurations (the tile tuner's search space).  The
@@ -962,6 +981,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 32) {
         if (props) return tile_fill<WideL<RP>, 1>(props), hipSuccess;
         return launch<WideL<RP>>(*a, s);
+      }
+      break;
+    case kTileBigNL:
+      if constexpr (RP <= 32) {
+        if (props) return tile_fill<BigNL<RP>, 1>(props), hipSuccess;
+        return launch<BigNL<RP>>(*a, s);
       }
       break;
     case kTileSqL:

@@ -83,7 +83,8 @@ hipError_t launch_fwd_tiled_f32(const FwdArgs& a, hipStream_t s);
 enum TileId { kTileTall = 0, kTileMid = 1, kTileMidG2 = 2, kTileMidG4 = 3, kTileBig = 4,
               kTileBigG2 = 5, kTileMid3 = 6, kTileMidK2 = 7,
               kTileMid3L = 8, kTileWideL = 9,
-              kTileSqL = 10, kTileTallL = 11, kTileSmallL = 12, kTileCount = 13 };
+              kTileSqL = 10, kTileTallL = 11, kTileSmallL = 12, kTileBigNL = 13,
+              kTileCount = 14 };
 struct TileProps {
   int bm, bn, waves, stages, bk, group, rank_pad, lds_bytes, k_split;
   const void* kernel;

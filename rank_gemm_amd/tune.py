@@ -177,7 +177,7 @@ def valid_for(choice: str, dtype: str, M: int, r: int) -> bool:
 def _tile_ranks(tid: int, r: int) -> bool:
     # Same table as include/lora.h (checked against lora_tile_get_info by the tests).
     limit = {0: 32, 1: 256, 2: 128, 3: 128, 4: 64, 5: 32, 6: 128, 7: 64, 8: 128, 9: 32,
-             10: 64, 11: 64, 12: 64}.get(tid)
+             10: 64, 11: 64, 12: 64, 13: 32}.get(tid)
     return limit is not None and pad_rank(r) <= limit
 
 

@@ -33,7 +33,7 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 8
+    assert rg.abi_version() == 9
     for s in range(10):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
@@ -268,9 +268,10 @@ def test_bwd_workspace_size():
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(tile=13), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=14), rg.LORA_ERR_UNSUPPORTED),
     (dict(tile=10, r=100, ldb=100), rg.LORA_ERR_UNSUPPORTED),  # 64 x 64 loader tile: r <= 64
     (dict(tile=9, r=40, ldb=40), rg.LORA_ERR_UNSUPPORTED),     # 128 x 256 loader tile: r <= 32
+    (dict(tile=13, r=40, ldb=40), rg.LORA_ERR_UNSUPPORTED),    # 256 x 160 loader tile: r <= 32
     (dict(tile=8, r=200, ldb=200), rg.LORA_ERR_UNSUPPORTED),   # loader tile: r <= 128
     (dict(tile=7, r=100, ldb=100), rg.LORA_ERR_UNSUPPORTED),   # k-split tile: r <= 64
     (dict(tile=6, r=200, ldb=200), rg.LORA_ERR_UNSUPPORTED),

@@ -30,6 +30,8 @@ SHAPES = [
     (3000, 900, 2056, 128),  # 128 x 128 loader tile, rank 128
     (64, 520, 1000, 128),    # 128 x 128 loader tile, rank 128, one row tile
     (4100, 1032, 264, 24),   # 128 x 256 loader tile
+    (4000, 2504, 264, 24),   # 256 x 160 loader tile (ragged M and N)
+    (8192, 2560, 136, 32),   # 256 x 160 loader tile (512 tiles, two full rounds)
     (4100, 1032, 264, 100),  # 128 x 128, two stages, rank 128
     (5000, 3000, 136, 200),  # 128 x 128, two stages, rank 256
     (4000, 4096, 96, 20),    # 256 x 256 (256 tiles, ragged M)
