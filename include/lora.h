@@ -78,9 +78,9 @@ typedef enum lora_dtype {
 } lora_dtype;
 
 /* Forward variants.  AUTO picks DECODE for bf16 with M <= LORA_DECODE_AUTO_M
- * and r <= 32, TILED otherwise (for 16 < M <= 64 the tiled kernel runs a
- * 64 x 32 tile streaming W with a deep stage ring, faster there than the
- * decode kernel).  Forcing one is for tests and measurement. */
+ * and r <= 32, TILED otherwise (for 16 < M <= 64 the tiled kernel's small
+ * tiles with loader waves stream W from many workgroups, faster there than
+ * the decode kernel).  Forcing one is for tests and measurement. */
 typedef enum lora_variant {
     LORA_VARIANT_AUTO = 0,
     LORA_VARIANT_TILED = 1,   /* MFMA-tiled fused forward, any M */
@@ -317,7 +317,8 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *   2   128 x 128    8    2 N tiles       r <= 128
  *   3   128 x 128    8    4 N tiles       r <= 128
  *   4   256 x 256    8    1               r <= 64
- *   5   256 x 256    8    2 N tiles       r <= 32
+ *   5   (retired: 256 x 256 with T shared over 2 N tiles spilled at every
+ *       rank; never instantiated, lora_tile_get_info returns UNSUPPORTED)
  *   6   128 x 128    8    1               r <= 128   (three stages)
  *   7   128 x 128   16    1               r <= 64    (three stages, k split)
  *   8   128 x 128   12    1               r <= 128   (three stages, 4 loaders)

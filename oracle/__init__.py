@@ -55,6 +55,8 @@ def _load():
     lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_bf16_n.argtypes = [vp, vp, i64]
+    lib.oracle_round_bf16_n.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_get_threads.restype = ctypes.c_int
     _lib = lib
@@ -194,7 +196,12 @@ def bwd(X: np.ndarray, W: np.ndarray, A: np.ndarray, B: np.ndarray, dY: np.ndarr
 def round_bf16(x) -> np.ndarray:
     """Correctly rounded (nearest, ties to even) fp64 -> bf16, as uint16 bits."""
     lib = _load()
-    flat = np.asarray(x, dtype=np.float64).ravel()
-    out = np.fromiter((lib.oracle_round_bf16(float(v)) for v in flat), dtype=np.uint16,
-                      count=flat.size)
+    flat = np.ascontiguousarray(np.asarray(x, dtype=np.float64).ravel())
+    out = np.empty(flat.size, dtype=np.uint16)
+    lib.oracle_round_bf16_n(flat.ctypes.data, out.ctypes.data, flat.size)
     return out.reshape(np.shape(x))
+
+
+def round_bf16_scalar(x: float) -> int:
+    """oracle_round_bf16 on one value (the array form calls it per element)."""
+    return int(_load().oracle_round_bf16(float(x)))

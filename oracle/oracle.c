@@ -200,6 +200,13 @@ uint16_t oracle_round_bf16(double x)
     return b;
 }
 
+/* oracle_round_bf16 applied to n values, x[i] -> out[i]. */
+void oracle_round_bf16_n(const double *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_round_bf16(x[i]);
+}
+
 /*
  * Merge from pristine, rows [n0, n1) of the [N, K] result:
  *   Wref[n,k] = W0[n,k] + scale * sum_j B[n,j] A[j,k]

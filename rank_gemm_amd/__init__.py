@@ -109,6 +109,14 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         _build.build()
+    # One HIP runtime per process: torch ships its own libamdhip64 (the same
+    # soname liblora.so needs).  Loaded first, it satisfies liblora.so's
+    # dependency; loaded after liblora.so, the system runtime would already
+    # be in the process and torch would add a second one beside it.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     L.lora_fwd.argtypes = [i32, i64, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, f32, vp,
@@ -167,6 +175,15 @@ def _check(status: int, what: str) -> None:
 
 
 # ---------------------------------------------------------------- raw ABI
+
+def fwd_auto_raw(dtype: int, M: int, N: int, K: int, r: int, X: int, ldx: int, W: int, ldw: int,
+                 A: int, lda: int, B: int, ldb: int, scale: float, Y: int, ldy: int,
+                 stream: int = 0) -> int:
+    """lora_fwd (the library's own kernel choice) with integer addresses;
+    returns the lora_status."""
+    return int(lib().lora_fwd(dtype, M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, scale, Y, ldy,
+                              stream or None))
+
 
 def fwd_raw(variant: int, dtype: int, M: int, N: int, K: int, r: int, X: int, ldx: int, W: int,
             ldw: int, A: int, lda: int, B: int, ldb: int, scale: float, Y: int, ldy: int,
@@ -269,10 +286,17 @@ def _dtype_code(t) -> int:
 
 
 def _mat(t, name: str):
+    """(address, leading dimension) of a row-major 2-D tensor.  Rows must
+    not overlap: a row stride shorter than the row (an expand()ed or
+    overlapping view) is rejected, since the kernels would read or write
+    rows' worth of memory the tensor does not hold."""
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit inner stride")
+    if t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} has row stride {t.stride(0)} < row length {t.shape[1]}: "
+                         f"overlapping rows are not supported")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a HIP device")
     return t.data_ptr(), max(t.stride(0), t.shape[1], 1)
@@ -315,9 +339,14 @@ def fwd(X, W, A, B, scale: float, out=None, variant: str = "auto", tile: Optiona
                           float(scale), py, ldy, _stream(X.device))
         _check(st, "lora_fwd_tile")
         return out
+    if variant == "auto":
+        st = fwd_auto_raw(dt, M, N, K, r, px, ldx, pw, ldw, pa, lda, pb, ldb, float(scale), py,
+                          ldy, _stream(X.device))
+        _check(st, "lora_fwd")
+        return out
     st = fwd_raw(VARIANTS[variant], dt, M, N, K, r, px, ldx, pw, ldw, pa, lda, pb, ldb,
                  float(scale), py, ldy, _stream(X.device))
-    _check(st, "lora_fwd")
+    _check(st, "lora_fwd_variant")
     return out
 
 

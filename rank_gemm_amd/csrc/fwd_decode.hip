@@ -95,8 +95,9 @@ __device__ __forceinline__ void dec_body(
   // The epilogue's B row (lane: row n0 + l % 16), loaded now by the waves
   // that run the epilogue, so its latency hides behind the W stream; masking
   // past r waits for the epilogue, so nothing here waits on these loads.
-  // Positions past r load a valid chunk of the row.  Rows that are not
-  // 16-B aligned (ldb % 8 != 0) are read in the epilogue instead.
+  // b_vec holds only when r % 8 == 0 (and rows are 16-B aligned), so every
+  // chunk min(8 c, r - 8) lies inside the row's r elements; otherwise the
+  // epilogue reads B element by element.
   u32x4 bv[RP / 8];
   const int64_t brow = min(n0 + lrow, N - 1);
   if (b_vec && wave < MB) {
@@ -382,8 +383,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_batch_kernel(const De
                                       (b - args.first[lo]) * 16, smem, d.tp);
 }
 
+// 16-B loads of B rows: aligned rows whose rank is a multiple of 8 (no chunk
+// reaches past a row's last element).
 inline int dec_b_vec(const FwdArgs& a) {
-  return ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0);
+  return ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0) && (a.r % 8 == 0);
 }
 
 // The forwards a[i0, i1) (same M, same rank class) in one launch; with a

@@ -800,6 +800,11 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 // whole 128-B lines per row.
 template <int RP>
 using Big = Cfg<256, 256, 2, 4, RP, 2, 64>;
+// 256 x 256 with 4 waves (2 x 2) of 128 x 128, one per SIMD, accumulators in
+// the AGPRs: a third fewer LDS fragment bytes per MFMA than 8 waves of
+// 128 x 64 (each wave reads (128 + 128) rows per k for 128 x 128 outputs).
+template <int RP>
+using Big4 = Cfg<256, 256, 2, 2, RP, 2, 64>;
 // Tall: 64 x 32, 4 waves (4 x 1), eight 64-deep stages in flight, for few
 // tokens (M <= 64): the cost is streaming W and re-reading X from L2, so the
 // tile is narrow and the ring deep.
@@ -954,10 +959,8 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       }
       break;
     case kTileBigG2:
-      if constexpr (RP <= 32) {
-        if (props) return tile_fill<Big<RP>, 2>(props), hipSuccess;
-        return launch<Big<RP>, 2>(*a, s);
-      }
+      // Retired: 256 x 256 with T shared over 2 N tiles spilled registers
+      // at every rank; the id stays reserved and is never instantiated.
       break;
     case kTileMid3:
       if constexpr (RP <= 128) {
@@ -981,6 +984,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 32) {
         if (props) return tile_fill<WideL<RP>, 1>(props), hipSuccess;
         return launch<WideL<RP>>(*a, s);
+      }
+      break;
+    case kTileBig4:
+      if constexpr (RP <= 16) {  // rank 32 spills (27 registers)
+        if (props) return tile_fill<Big4<RP>, 1>(props), hipSuccess;
+        return launch<Big4<RP>>(*a, s);
       }
       break;
     case kTileBigNL:

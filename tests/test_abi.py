@@ -102,11 +102,24 @@ def _merge(**kw):
 ])
 def test_fwd_rejects_before_any_hip_call(kw, want):
     assert _fwd(**kw) == want
+    if kw.get("variant", 0) == 0:
+        # the same arguments through the lora_fwd symbol itself
+        assert _fwd_auto(**kw) == want
+
+
+def _fwd_auto(**kw):
+    a = dict(dtype=rg.LORA_BF16, M=64, N=64, K=64, r=16, X=PX, ldx=64, W=PW, ldw=64, A=PA,
+             lda=64, B=PB, ldb=16, scale=2.0, Y=PY, ldy=64)
+    a.update({k: v for k, v in kw.items() if k != "variant"})
+    return rg.fwd_auto_raw(a["dtype"], a["M"], a["N"], a["K"], a["r"], a["X"], a["ldx"], a["W"],
+                           a["ldw"], a["A"], a["lda"], a["B"], a["ldb"], a["scale"], a["Y"],
+                           a["ldy"])
 
 
 @pytest.mark.parametrize("kw", [dict(M=0), dict(N=0), dict(M=0, X=0, Y=0), dict(N=0, W=0, B=0)])
 def test_fwd_empty_is_noop(kw):
     assert _fwd(**kw) == rg.LORA_OK
+    assert _fwd_auto(**kw) == rg.LORA_OK
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -334,3 +347,39 @@ def test_fwd_batch_argument_checks():
     # empty forwards are skipped, whatever their pointers
     assert rg.fwd_batch_raw(rg.LORA_BF16, [_fdesc(M=0, X=0, Y=0), _fdesc(N=0, W=0, B=0)]) == \
         rg.LORA_OK
+
+
+def test_torch_wrapper_rejects_overlapping_rows():
+    """A row stride shorter than the row (expand()ed or overlapping views)
+    is refused before anything reaches the library: the kernels would
+    otherwise read or write rows the tensor does not hold."""
+    torch = pytest.importorskip("torch")
+    row = torch.zeros(1, 64, dtype=torch.bfloat16)
+    X = row.expand(32, 64)                                  # stride (0, 1)
+    assert X.stride(0) == 0
+    with pytest.raises(ValueError, match="row stride"):
+        rg._mat(X, "X")
+    flat = torch.zeros(200, dtype=torch.bfloat16)
+    Y = flat.as_strided((10, 64), (8, 1))                   # rows overlap
+    with pytest.raises(ValueError, match="row stride"):
+        rg._mat(Y, "out")
+    # one row, or rows padded past their length, are fine (then the device check)
+    with pytest.raises(ValueError, match="HIP device"):
+        rg._mat(row, "X")
+    with pytest.raises(ValueError, match="HIP device"):
+        rg._mat(flat.as_strided((2, 64), (72, 1)), "X")
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library before torch must not put a second HIP runtime in
+    the process (torch ships its own libamdhip64 with the same soname): with
+    two, the first GPU calls fail and later ones crash.  Checked in a fresh
+    interpreter that loads the library first and torch afterwards."""
+    import subprocess
+    import sys
+    code = ("import re, sys; sys.path.insert(0, %r); import rank_gemm_amd as rg; rg.lib(); "
+            "import torch; maps = open('/proc/self/maps').read(); "
+            "print(len(set(re.findall(r'/\\S*libamdhip64\\S*', maps))))" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1", out.stdout

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import TOL, as_f64, rel_fro, to_dev, to_host
+from helpers import TOL, as_f64, check_fwd_elements, rel_fro, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +56,8 @@ def test_fwd_batch_equals_fwd(gpu_lib, with_ws):
             assert np.array_equal(got, single), c.name
         ref = oracle.fwd(Xh, t["W"], t["A"], t["B"], c.scale)
         err = rel_fro(as_f64(got), ref)
-        print(f"{c.name} M{c.M} N{c.N} K{c.K} r{c.r}: rel_fro={err:.3e}")
+        ratio = check_fwd_elements(got, ref, Xh, t["W"], t["A"], t["B"], c.scale, "bf16", c.name)
+        print(f"{c.name} M{c.M} N{c.N} K{c.K} r{c.r}: rel_fro={err:.3e} worst/bound={ratio:.3f}")
         assert err <= TOL["bf16"]
 
 

@@ -3,16 +3,16 @@ that every default configuration (decode kernel; 32 x 32, 64 x 32, 64 x 64,
 128 x 128 and 128 x 256 tiles with loader waves; 128 x 128 two-stage; 256 x
 256) runs with ragged M, N and K tails and ranks below their padded rank.
 
-Bar: relative Frobenius error <= 1e-2 (bf16) against the fp64 oracle on
-sampled rows (row m of Y depends on row m of X only), finite everywhere,
-and the same bits on a second call.
+Bar: relative Frobenius error <= 1e-2 (bf16) against the fp64 oracle and
+every element within the per-element bound of the kernels' arithmetic
+(tests/helpers.py), on the whole output, and the same bits on a second call.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from helpers import TOL, as_f64, rel_fro, sample_rows, to_dev, to_host
+from helpers import TOL, as_f64, check_fwd_elements, rel_fro, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -48,10 +48,9 @@ def test_default_tile_boundaries(gpu_lib, shape):
     Y1 = to_host(gpu_lib.fwd(X, W, A, B, c.scale))
     Y2 = to_host(gpu_lib.fwd(X, W, A, B, c.scale))
     torch.cuda.synchronize()
-    rows = sample_rows(M, 16, seed=M + r)
-    ref = oracle.fwd(np.ascontiguousarray(t["X"][rows]), t["W"], t["A"], t["B"], c.scale)
-    err = rel_fro(as_f64(Y1[rows]), ref)
-    print(f"{c.name}: rows={len(rows)} rel_fro={err:.3e}")
+    ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)
+    err = rel_fro(as_f64(Y1), ref)
+    ratio = check_fwd_elements(Y1, ref, t["X"], t["W"], t["A"], t["B"], c.scale, "bf16", c.name)
+    print(f"{c.name}: rel_fro={err:.3e} worst/bound={ratio:.3f}")
     assert err <= TOL["bf16"]
-    assert np.isfinite(as_f64(Y1)).all()
     assert np.array_equal(Y1, Y2)

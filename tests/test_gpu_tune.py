@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import TOL, as_f64, rel_fro, to_dev, to_host
+from helpers import TOL, as_f64, check_fwd_elements, fwd_bound, rel_fro, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,7 @@ def test_every_tile_matches_oracle_and_default(gpu_lib, shape):
     t = c.make()
     X, W, A, B = (to_dev(t[k]) for k in "XWAB")
     ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)
+    bound = fwd_bound(ref, t["X"], t["W"], t["A"], t["B"], c.scale, "bf16")
     base = to_host(rg.fwd(X, W, A, B, c.scale))
     family = {}
     for tid in range(rg.TILE_COUNT):
@@ -41,8 +42,10 @@ def test_every_tile_matches_oracle_and_default(gpu_lib, shape):
         Y = to_host(rg.fwd(X, W, A, B, c.scale, tile=tid))
         torch.cuda.synchronize()
         err = rel_fro(as_f64(Y), ref)
-        print(f"{c.name} tile {tid}: rel_fro={err:.3e}")
+        bad = int((np.abs(as_f64(Y) - ref) > bound).sum())
+        print(f"{c.name} tile {tid}: rel_fro={err:.3e} outside_bound={bad}")
         assert err <= TOL["bf16"], (tid, err)
+        assert bad == 0, (tid, bad)
         key = "ksplit" if tid in KSPLIT else "in_order"
         if key in family:
             assert np.array_equal(Y, family[key]), tid
@@ -74,8 +77,8 @@ def test_tile_usage_and_limits(gpu_lib):
             assert u.blocks_per_cu >= (1 if info.lds_bytes <= lim.lds_per_block else 0)
             if u.scratch_bytes > 0:
                 spills.append((tid, r))
-    # The tiles lora_fwd picks by itself never spill.
-    assert all(tid == 5 for tid, _ in spills), spills
+    # No instantiated configuration spills (the one that did, id 5, is retired).
+    assert not spills, spills
 
 
 def test_tuner_end_to_end(gpu_lib, tmp_path):
@@ -87,7 +90,7 @@ def test_tuner_end_to_end(gpu_lib, tmp_path):
     assert set(cache.entries) == {"bf16:512:1024:512:16", "bf16:8:2048:1024:16"}
     for e in cache.entries.values():
         assert e["choice"] in e["us"] and e["us"][e["choice"]] == min(e["us"].values())
-        assert "tile:5" in e["pruned"] or "tile:5" in e["us"]
+        assert "tile:5" not in e["pruned"] and "tile:5" not in e["us"]   # retired id
     p = cache.save(str(tmp_path / "tiles.json"))
     loaded = tune.TileCache.load(p)
     # on a shape near a cached one the tuned forward runs the cached choice
@@ -103,4 +106,6 @@ def test_tuner_end_to_end(gpu_lib, tmp_path):
         Y0 = to_host(rg.fwd(X, W, A, B, c.scale, tile=int(choice.split(":")[1])))
     torch.cuda.synchronize()
     assert np.array_equal(Y1, Y0)
-    assert rel_fro(as_f64(Y1), oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)) <= TOL["bf16"]
+    ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)
+    assert rel_fro(as_f64(Y1), ref) <= TOL["bf16"]
+    check_fwd_elements(Y1, ref, t["X"], t["W"], t["A"], t["B"], c.scale, "bf16", "tuned")

@@ -261,6 +261,17 @@ def test_round_bf16_single_rounding_from_double():
     assert oracle.round_bf16(float("nan")) == 0x7FC0
 
 
+def test_round_bf16_array_equals_scalar_entry_point():
+    """The array form rounds each value exactly as the scalar entry point."""
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([rng.standard_normal(500) * 10.0 ** rng.integers(-40, 39, 500),
+                           [0.0, -0.0, np.inf, -np.inf, np.nan, 1.0 + 2.0 ** -8 + 2.0 ** -30]])
+    got = oracle.round_bf16(vals)
+    want = np.array([oracle.round_bf16_scalar(v) for v in vals], dtype=np.uint16)
+    np.testing.assert_array_equal(got, want)
+    assert oracle.round_bf16(vals.reshape(2, -1)).shape == (2, vals.size // 2)
+
+
 # ---------------------------------------------------------------- backward
 
 def _bwd_inputs(seed, M, N, K, r, dtype="f32"):
