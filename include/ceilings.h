@@ -33,15 +33,20 @@ int ceil_mfma(int workgroups, int waves, int iters, float *out, uint64_t *clocks
 double ceil_mfma_flops(int workgroups, int waves, int iters);
 
 /* dst[0, bytes) = src[0, bytes): a streaming copy, 16 B per lane, 256-lane
- * workgroups striding over the buffer.  bytes a multiple of 16, pointers
- * 16-byte aligned, buffers not overlapping. */
-int ceil_copy(const void *src, void *dst, int64_t bytes, int workgroups, void *stream);
+ * workgroups.  variant 0: every lane strides over the whole buffer, four
+ * loads in flight; 1: each workgroup streams one contiguous block, eight
+ * 4-KiB rounds in flight; 2: as 1 with non-temporal loads and stores.
+ * bytes a multiple of 16, pointers 16-byte aligned, buffers not
+ * overlapping. */
+int ceil_copy(const void *src, void *dst, int64_t bytes, int workgroups, int variant,
+              void *stream);
 
-/* Reads src[0, bytes) (16 B per lane, striding workgroups) and writes
+/* Reads src[0, bytes) (16 B per lane, variants as ceil_copy) and writes
  * nothing unless every word of a lane's XOR of its data is all ones; out:
  * `workgroups` uint32 the kernel may write in that case.  bytes a multiple
  * of 16, src 16-byte aligned. */
-int ceil_read(const void *src, int64_t bytes, void *out, int workgroups, void *stream);
+int ceil_read(const void *src, int64_t bytes, void *out, int workgroups, int variant,
+              void *stream);
 
 #ifdef __cplusplus
 }

@@ -60,35 +60,83 @@ __global__ __launch_bounds__(512) void ceil_mfma_kernel(int iters, float* out, u
   }
 }
 
-constexpr int kUnroll = 4;  // 16-B loads in flight per lane per iteration
+constexpr int kUnroll = 4;  // 16-B loads in flight per lane per iteration (grid stride)
+constexpr int kBlockU = 8;  // 16-B loads in flight per lane per step (blocked)
 
-__global__ __launch_bounds__(256) void ceil_copy_kernel(const u32x4* __restrict__ src,
-                                                        u32x4* __restrict__ dst, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
-    u32x4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = v[u];
-  }
-  for (; i < n16; i += stride) dst[i] = src[i];
+// Variant 0: every lane strides over the whole buffer, kUnroll loads at a time.
+// Variant 1: each workgroup streams one contiguous block, its 256 lanes
+// reading 4 KiB per load round, kBlockU rounds in flight.  Variant 2: as 1
+// with non-temporal loads and stores (streamed data bypasses cache retention).
+template <int V>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+  if constexpr (V == 2) return __builtin_nontemporal_load(p);
+  return *p;
+}
+template <int V>
+__device__ __forceinline__ void st(u32x4* p, u32x4 v) {
+  if constexpr (V == 2) __builtin_nontemporal_store(v, p);
+  else *p = v;
 }
 
+template <int V>
+__global__ __launch_bounds__(256) void ceil_copy_kernel(const u32x4* __restrict__ src,
+                                                        u32x4* __restrict__ dst, int64_t n16) {
+  if constexpr (V == 0) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = v[u];
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
+  } else {
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+    int64_t i = b0 + threadIdx.x;
+    for (; i + (kBlockU - 1) * 256 < b1; i += kBlockU * 256) {
+      u32x4 v[kBlockU];
+#pragma unroll
+      for (int u = 0; u < kBlockU; ++u) v[u] = ld<V>(src + i + u * 256);
+#pragma unroll
+      for (int u = 0; u < kBlockU; ++u) st<V>(dst + i + u * 256, v[u]);
+    }
+    for (; i < b1; i += 256) st<V>(dst + i, ld<V>(src + i));
+  }
+}
+
+template <int V>
 __global__ __launch_bounds__(256) void ceil_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                         uint32_t* __restrict__ out) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
-    u32x4 v[kUnroll];
+  if constexpr (V == 0) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+      u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+      for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+      for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+    }
+    for (; i < n16; i += stride) acc ^= src[i];
+  } else {
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+    int64_t i = b0 + threadIdx.x;
+    for (; i + (kBlockU - 1) * 256 < b1; i += kBlockU * 256) {
+      u32x4 v[kBlockU];
+#pragma unroll
+      for (int u = 0; u < kBlockU; ++u) v[u] = ld<V>(src + i + u * 256);
+#pragma unroll
+      for (int u = 0; u < kBlockU; ++u) acc ^= v[u];
+    }
+    for (; i < b1; i += 256) acc ^= ld<V>(src + i);
   }
-  for (; i < n16; i += stride) acc ^= src[i];
   // Never true for the benchmark's data (it reads a buffer of zeros): the
   // store keeps the loads alive without writing anything.
   if ((acc[0] & acc[1] & acc[2] & acc[3]) == 0xFFFFFFFFu) out[blockIdx.x] = acc[0];
@@ -109,23 +157,29 @@ double ceil_mfma_flops(int workgroups, int waves, int iters) {
   return (double)workgroups * waves * iters * kChains * (16.0 * 16.0 * 32.0 * 2.0);
 }
 
-int ceil_copy(const void* src, void* dst, int64_t bytes, int workgroups, void* stream) {
+int ceil_copy(const void* src, void* dst, int64_t bytes, int workgroups, int variant,
+              void* stream) {
   if (!src || !dst || bytes < 0 || (bytes & 15) || workgroups < 1) return 1;
+  if (variant < 0 || variant > 2) return 1;
   if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return 4;
   if (bytes == 0) return 0;
-  hipLaunchKernelGGL(ceil_copy_kernel, dim3(workgroups), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
-                     static_cast<u32x4*>(dst), bytes / 16);
+  auto k = variant == 0 ? ceil_copy_kernel<0> : variant == 1 ? ceil_copy_kernel<1>
+                                                              : ceil_copy_kernel<2>;
+  hipLaunchKernelGGL(k, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
   return hipGetLastError() == hipSuccess ? 0 : 8;
 }
 
-int ceil_read(const void* src, int64_t bytes, void* out, int workgroups, void* stream) {
+int ceil_read(const void* src, int64_t bytes, void* out, int workgroups, int variant,
+              void* stream) {
   if (!src || !out || bytes < 0 || (bytes & 15) || workgroups < 1) return 1;
+  if (variant < 0 || variant > 2) return 1;
   if ((uintptr_t)src & 15) return 4;
   if (bytes == 0) return 0;
-  hipLaunchKernelGGL(ceil_read_kernel, dim3(workgroups), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), bytes / 16,
-                     static_cast<uint32_t*>(out));
+  auto k = variant == 0 ? ceil_read_kernel<0> : variant == 1 ? ceil_read_kernel<1>
+                                                              : ceil_read_kernel<2>;
+  hipLaunchKernelGGL(k, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), bytes / 16, static_cast<uint32_t*>(out));
   return hipGetLastError() == hipSuccess ? 0 : 8;
 }
 
