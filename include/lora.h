@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 10
+#define LORA_ABI_VERSION 11
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -66,8 +66,10 @@ typedef enum lora_status {
                                  the limits below, or a forced variant that
                                  cannot run this shape */
     LORA_ERR_HIP = 8,         /* the HIP runtime reported a launch error */
-    LORA_ERR_WORKSPACE = 9    /* lora_bwd workspace NULL, smaller than
+    LORA_ERR_WORKSPACE = 9,   /* lora_bwd workspace NULL, smaller than
                                  lora_bwd_workspace_size or not 256-B aligned */
+    LORA_ERR_SCRATCH = 10     /* more forwards than the static scratch of
+                                 lora_fwd_batch_noalloc holds */
 } lora_status;
 
 #define LORA_MAX_LD ((1 << 22) - 8)
@@ -181,6 +183,33 @@ int lora_fwd_batch(int dtype, int count, const lora_fwd_desc *descs, void *works
 /* Workspace bytes lora_fwd_batch can use for count forwards (16 KiB each),
  * or -1 for count < 0. */
 int64_t lora_fwd_batch_workspace_size(int count);
+
+/*
+ * lora_fwd_batch_noalloc -- lora_fwd_batch with its workspace in the
+ * library's own static device memory, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing and calls no
+ * allocating routine; the caller still passes inputs and outputs.
+ *
+ * Arguments, validation and results as lora_fwd_batch called with a
+ * workspace (each Y bitwise the same), for at most LORA_NOALLOC_MAX_FORWARDS
+ * descriptors: more return LORA_ERR_SCRATCH and launch nothing.
+ *
+ * The scratch is one array of LORA_NOALLOC_MAX_FORWARDS x 16 KiB (1 MiB) per
+ * GPU, in the library's device data; each GPU holds it from the library's
+ * load until the process ends.  Its device address is looked up on the first
+ * call on a device, with that device current.  Every call on a GPU uses the
+ * same array and overwrites it, and the kernels read only what the same call
+ * wrote, so nothing needs clearing between calls; but calls that overlap in
+ * time on one GPU (other streams, other threads) race on the array and must
+ * be serialised by the caller.
+ *
+ *   dtype, count, descs, stream   as for lora_fwd_batch.
+ * Returns a lora_status (LORA_ERR_HIP if the scratch's address cannot be
+ * obtained).
+ */
+#define LORA_NOALLOC_MAX_FORWARDS 64
+int lora_fwd_batch_noalloc(int dtype, int count, const lora_fwd_desc *descs, void *stream);
 
 /*
  * lora_merge -- merge from pristine   [unsloth], addmm refresh entry.

@@ -39,6 +39,8 @@ LORA_ERR_ALIAS = 6
 LORA_ERR_UNSUPPORTED = 7
 LORA_ERR_HIP = 8
 LORA_ERR_WORKSPACE = 9
+LORA_ERR_SCRATCH = 10
+NOALLOC_MAX_FORWARDS = 64
 LORA_F32 = 0
 LORA_BF16 = 1
 VARIANTS = {"auto": 0, "tiled": 1, "decode": 2}
@@ -51,7 +53,7 @@ EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch",
            "lora_merge_inplace", "lora_status_str", "lora_abi_version", "lora_fwd_pick",
            "lora_bwd", "lora_bwd_workspace_size", "lora_tile_get_info", "lora_tile_get_usage",
            "lora_get_device_limits", "lora_fwd_tile", "lora_fwd_batch",
-           "lora_fwd_batch_workspace_size")
+           "lora_fwd_batch_workspace_size", "lora_fwd_batch_noalloc")
 
 
 class MergeDesc(ctypes.Structure):
@@ -153,6 +155,8 @@ def lib() -> ctypes.CDLL:
     L.lora_fwd_batch.restype = i32
     L.lora_fwd_batch_workspace_size.argtypes = [i32]
     L.lora_fwd_batch_workspace_size.restype = i64
+    L.lora_fwd_batch_noalloc.argtypes = [i32, i32, ctypes.POINTER(FwdDesc), vp]
+    L.lora_fwd_batch_noalloc.restype = i32
     _lib = L
     return L
 
@@ -212,6 +216,13 @@ def fwd_batch_raw(dtype: int, descs, stream: int = 0, ws: int = 0, ws_bytes: int
     if not isinstance(descs, ctypes.Array):
         descs = (FwdDesc * len(descs))(*descs)
     return int(lib().lora_fwd_batch(dtype, len(descs), descs, ws or None, ws_bytes, stream or None))
+
+
+def fwd_batch_noalloc_raw(dtype: int, descs, stream: int = 0) -> int:
+    """lora_fwd_batch_noalloc over a sequence of FwdDesc (or an array of them)."""
+    if not isinstance(descs, ctypes.Array):
+        descs = (FwdDesc * len(descs))(*descs)
+    return int(lib().lora_fwd_batch_noalloc(dtype, len(descs), descs, stream or None))
 
 
 def fwd_batch_workspace_size(count: int) -> int:

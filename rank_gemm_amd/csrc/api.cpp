@@ -167,6 +167,8 @@ const char* lora_status_str(int s) {
     case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED: rank or variant not supported";
     case LORA_ERR_HIP: return "LORA_ERR_HIP: HIP launch error";
     case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case LORA_ERR_SCRATCH:
+      return "LORA_ERR_SCRATCH: more forwards than the no-allocation scratch holds (64)";
     default: return "unknown lora_status";
   }
 }
@@ -372,40 +374,37 @@ int64_t lora_fwd_batch_workspace_size(int count) {
   return count < 0 ? -1 : (int64_t)count * lora::kDecTpBytes;
 }
 
-int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* workspace,
-                   int64_t workspace_bytes, void* stream) {
-  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
-  if (count < 0) return LORA_ERR_SHAPE;
-  if (count == 0) return LORA_OK;
-  if (descs == nullptr) return LORA_ERR_NULL;
-  if (workspace != nullptr && (workspace_bytes < (int64_t)count * lora::kDecTpBytes ||
-                               (reinterpret_cast<uintptr_t>(workspace) & 255)))
-    return LORA_ERR_WORKSPACE;
+}  // extern "C"
+
+namespace {
+
+// Validation of a batch of forward descriptors (into work, which holds at
+// least count entries; returns the number of non-empty forwards through n).
+int check_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, const void* workspace,
+                    int64_t ws_bytes, lora::FwdArgs* work, size_t* n) {
   const int64_t e = esize(dtype);
-  std::vector<lora::FwdArgs> work;
-  work.reserve(count);
+  size_t k = 0;
   for (int i = 0; i < count; ++i) {
     const lora_fwd_desc& d = descs[i];
     const int st = check_fwd(dtype, d.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda, d.B,
                              d.ldb, d.Y, d.ldy);
     if (st != LORA_OK) return st;
     if (d.M == 0 || d.N == 0) continue;
-    work.push_back({d.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda, d.B, d.ldb, d.scale,
-                    d.Y, d.ldy});
+    work[k++] = lora::FwdArgs{d.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda, d.B, d.ldb,
+                              d.scale, d.Y, d.ldy};
   }
   // Every output against every other forward's inputs and output, and the
   // workspace against every operand.
   const Range wsr{reinterpret_cast<uintptr_t>(workspace),
-                  reinterpret_cast<uintptr_t>(workspace) +
-                      (workspace ? (uintptr_t)count * lora::kDecTpBytes : 0)};
-  for (size_t i = 0; i < work.size(); ++i) {
+                  reinterpret_cast<uintptr_t>(workspace) + (workspace ? (uintptr_t)ws_bytes : 0)};
+  for (size_t i = 0; i < k; ++i) {
     const lora::FwdArgs& a = work[i];
     const Range y = span(a.Y, a.M, a.N, a.ldy, e);
     if (overlap(wsr, y) || overlap(wsr, span(a.X, a.M, a.K, a.ldx, e)) ||
         overlap(wsr, span(a.W, a.N, a.K, a.ldw, e)) || overlap(wsr, span(a.A, a.r, a.K, a.lda, e)) ||
         overlap(wsr, span(a.B, a.N, a.r, a.ldb, e)))
       return LORA_ERR_ALIAS;
-    for (size_t j = 0; j < work.size(); ++j) {
+    for (size_t j = 0; j < k; ++j) {
       if (j == i) continue;
       const lora::FwdArgs& b = work[j];
       if (overlap(y, span(b.X, b.M, b.K, b.ldx, e)) || overlap(y, span(b.W, b.N, b.K, b.ldw, e)) ||
@@ -414,14 +413,20 @@ int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* works
         return LORA_ERR_ALIAS;
     }
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  *n = k;
+  return LORA_OK;
+}
+
+// Launches of a validated batch (work[0, n)); workspace as lora_fwd_batch's.
+int run_fwd_batch(int dtype, const lora::FwdArgs* work, size_t n, void* workspace,
+                  hipStream_t s) {
   hipError_t err = hipSuccess;
   size_t i = 0;
-  while (i < work.size() && err == hipSuccess) {
+  while (i < n && err == hipSuccess) {
     const lora::FwdArgs& a = work[i];
     if (pick(dtype, a.M, a.r) == LORA_VARIANT_DECODE) {
       size_t j = i + 1;
-      while (j < work.size() && pick(dtype, work[j].M, work[j].r) == LORA_VARIANT_DECODE &&
+      while (j < n && pick(dtype, work[j].M, work[j].r) == LORA_VARIANT_DECODE &&
              work[j].M == a.M && (work[j].r <= 16) == (a.r <= 16))
         ++j;
       unsigned char* tws =
@@ -434,6 +439,45 @@ int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* works
     }
   }
   return err == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_fwd_batch(int dtype, int count, const lora_fwd_desc* descs, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (count < 0) return LORA_ERR_SHAPE;
+  if (count == 0) return LORA_OK;
+  if (descs == nullptr) return LORA_ERR_NULL;
+  if (workspace != nullptr && (workspace_bytes < (int64_t)count * lora::kDecTpBytes ||
+                               (reinterpret_cast<uintptr_t>(workspace) & 255)))
+    return LORA_ERR_WORKSPACE;
+  std::vector<lora::FwdArgs> work(count);
+  size_t n = 0;
+  const int st = check_fwd_batch(dtype, count, descs, workspace,
+                                 workspace ? (int64_t)count * lora::kDecTpBytes : 0, work.data(),
+                                 &n);
+  if (st != LORA_OK) return st;
+  return run_fwd_batch(dtype, work.data(), n, workspace, static_cast<hipStream_t>(stream));
+}
+
+int lora_fwd_batch_noalloc(int dtype, int count, const lora_fwd_desc* descs, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (count < 0) return LORA_ERR_SHAPE;
+  if (count == 0) return LORA_OK;
+  if (count > LORA_NOALLOC_MAX_FORWARDS) return LORA_ERR_SCRATCH;
+  if (descs == nullptr) return LORA_ERR_NULL;
+  static_assert(LORA_NOALLOC_MAX_FORWARDS == lora::kNoAllocForwards, "scratch size");
+  lora::FwdArgs work[LORA_NOALLOC_MAX_FORWARDS];  // host stack: nothing is allocated
+  size_t n = 0;
+  const int st = check_fwd_batch(dtype, count, descs, nullptr, 0, work, &n);
+  if (st != LORA_OK) return st;
+  if (n == 0) return LORA_OK;
+  void* scratch = nullptr;
+  if (lora::decode_scratch(&scratch) != hipSuccess) return LORA_ERR_HIP;
+  return run_fwd_batch(dtype, work, n, scratch, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -21,6 +21,8 @@
 // The waves' partial sums are added in a fixed order through LDS
 // (deterministic), then the epilogue adds scale * T B^T in fp32 on the VALU
 // and stores bf16 (one rounding).
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -480,6 +482,29 @@ hipError_t launch_dec_rb(const FwdArgs& a, const FwdArgs* batch, int i0, int i1,
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s) {
   return a.r <= 16 ? launch_dec_rb<1>(a, nullptr, 0, 0, nullptr, s)
                    : launch_dec_rb<2>(a, nullptr, 0, 0, nullptr, s);
+}
+
+// ---- Scratch of the no-allocation batch entry point: the T partial sums of
+// up to kNoAllocForwards forwards (kDecTpBytes each), one copy of the array
+// per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address is taken with
+// hipGetSymbolAddress once per device and only that address is used.
+static __device__ __align__(256) unsigned char scratch[kNoAllocForwards * kDecTpBytes];
+
+hipError_t decode_scratch(void** out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // With device `dev` current: the address of this device's copy.
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev].store(p, std::memory_order_release);  // concurrent first calls store the same value
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 // Forwards a[0, count): same M (<= LORA_DECODE_MAX_M) and the same rank class

@@ -100,6 +100,12 @@ hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s);
 // in a launch of its own instead of by every workgroup.
 constexpr int kDecTpBytes = 8 * 2 * 64 * 16;  // NW waves x rank blocks (<= 2) x 64 lanes x f32x4
 hipError_t launch_fwd_decode_bf16_batch(const FwdArgs* a, int count, void* tws, hipStream_t s);
+// The library's static scratch for lora_fwd_batch_noalloc: kNoAllocForwards
+// workspace slots of kDecTpBytes, one array per device (up to kMaxDevices),
+// its device address looked up once per device.
+constexpr int kNoAllocForwards = 64;
+constexpr int kMaxDevices = 64;
+hipError_t decode_scratch(void** out);
 hipError_t launch_merge_bf16(const MergeArgs& a, hipStream_t s);
 hipError_t launch_merge_f32(const MergeArgs& a, hipStream_t s);
 hipError_t launch_merge_bf16_batch(const MergeArgs* a, int count, hipStream_t s);

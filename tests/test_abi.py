@@ -33,8 +33,8 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 10
-    for s in range(10):
+    assert rg.abi_version() == 11
+    for s in range(11):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
 
@@ -385,3 +385,18 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1", out.stdout
+
+
+def test_fwd_batch_noalloc_rejects_before_any_hip_call():
+    """The no-allocation batch entry point validates like lora_fwd_batch and
+    refuses more forwards than its static scratch holds."""
+    d = _fdesc()
+    assert rg.fwd_batch_noalloc_raw(rg.LORA_BF16, [d] * (rg.NOALLOC_MAX_FORWARDS + 1)) == \
+        rg.LORA_ERR_SCRATCH
+    assert rg.fwd_batch_noalloc_raw(7, [d]) == rg.LORA_ERR_DTYPE
+    assert rg.fwd_batch_noalloc_raw(rg.LORA_BF16, []) == rg.LORA_OK
+    assert rg.lib().lora_fwd_batch_noalloc(rg.LORA_BF16, -1, None, None) == rg.LORA_ERR_SHAPE
+    assert rg.lib().lora_fwd_batch_noalloc(rg.LORA_BF16, 2, None, None) == rg.LORA_ERR_NULL
+    assert rg.fwd_batch_noalloc_raw(rg.LORA_BF16, [_fdesc(r=0)]) == rg.LORA_ERR_SHAPE
+    assert rg.fwd_batch_noalloc_raw(rg.LORA_BF16, [_fdesc(Y=PX)]) == rg.LORA_ERR_ALIAS
+    assert rg.fwd_batch_noalloc_raw(rg.LORA_BF16, [_fdesc(M=0)]) == rg.LORA_OK
