@@ -800,11 +800,10 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 // whole 128-B lines per row.
 template <int RP>
 using Big = Cfg<256, 256, 2, 4, RP, 2, 64>;
-// 256 x 256 with 4 waves (2 x 2) of 128 x 128, one per SIMD, accumulators in
-// the AGPRs: a third fewer LDS fragment bytes per MFMA than 8 waves of
-// 128 x 64 (each wave reads (128 + 128) rows per k for 128 x 128 outputs).
-template <int RP>
-using Big4 = Cfg<256, 256, 2, 2, RP, 2, 64>;
+// (Measured and dropped: the same tile as 4 waves of 128 x 128, one per
+// SIMD with the accumulators in AGPRs, reads a third fewer LDS bytes per
+// MFMA but ran 1.48x slower on 16384 x 8192 x 8192 r16 (2621 vs 1768 us) and
+// 1.55x on 8192 x 4096 x 2560: one wave per SIMD cannot hide its own loads.)
 // Tall: 64 x 32, 4 waves (4 x 1), eight 64-deep stages in flight, for few
 // tokens (M <= 64): the cost is streaming W and re-reading X from L2, so the
 // tile is narrow and the ring deep.
@@ -984,12 +983,6 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 32) {
         if (props) return tile_fill<WideL<RP>, 1>(props), hipSuccess;
         return launch<WideL<RP>>(*a, s);
-      }
-      break;
-    case kTileBig4:
-      if constexpr (RP <= 16) {  // rank 32 spills (27 registers)
-        if (props) return tile_fill<Big4<RP>, 1>(props), hipSuccess;
-        return launch<Big4<RP>>(*a, s);
       }
       break;
     case kTileBigNL:
