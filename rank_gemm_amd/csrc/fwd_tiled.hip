@@ -64,7 +64,12 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // at a load issue when the memory pipeline is backed up, and a multiplying
 // wave stalled there cannot issue its MFMAs either: with separate loaders the
 // loads and the MFMAs overlap.
-template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1, int PW_ = 0>
+//
+// TS = 1 stores the epilogue's T tile unpadded (rows of RP elements) with its
+// 16-B chunks XOR-swizzled by row, so that a tile keeping T across several N
+// tiles fits T after a ring that fills all but RP x BM x 2 bytes of the LDS.
+template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1, int PW_ = 0,
+          int TS_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_, BK = BK_;
   static constexpr int KS = KS_, PW = PW_;
@@ -89,7 +94,17 @@ struct Cfg {
   static constexpr int kLoadsLo = kXL + kWL + kAN / LW;
   static constexpr int kLoadsHi = kLoadsLo + (kAN % LW != 0 ? 1 : 0);
   static constexpr int kTS = RP + 8;                // epilogue T / B row stride (elements)
-  static constexpr int kEpiB = (BM + BN) * kTS * 2;
+  static constexpr bool kTSw = TS_ == 1;
+  static constexpr int kTRow = kTSw ? RP : kTS;     // T row stride (elements)
+  // Element index of T[row][col] in the epilogue's T tile.  Swizzled: chunk
+  // c = col / 8 of a row sits at c ^ (row mod RP / 8), so 16 rows read at one
+  // logical chunk (an MFMA operand fragment) hit distinct banks (RP = 128).
+  __device__ static __forceinline__ int t_idx(int row, int col) {
+    if constexpr (kTSw)
+      return row * RP + ((((col >> 3) ^ (row & (RP / 8 - 1))) << 3) | (col & 7));
+    return row * kTS + col;
+  }
+  static constexpr int kEpiB = (BM * kTRow + BN * kTS) * 2;
   static constexpr int kYS = BN + 8;                // output staging row stride (elements)
   static constexpr int kYB = BM * kYS * 2;
   // K split: after the loop each wave sends the half of its accumulators that
@@ -101,8 +116,9 @@ struct Cfg {
   // With T kept across the N tiles of a group: T after the ring, the B tile
   // and the output staging inside it.
   static constexpr int kTOffG = STAGES * kStageB;
-  static constexpr int kLdsG = kTOffG + BM * kTS * 2;
-  static_assert(BN * kTS * 2 <= kTOffG && kYB <= kTOffG, "group epilogue fits in the ring");
+  static constexpr int kLdsG = kTOffG + BM * kTRow * 2;
+  // (only then can a workgroup take several N tiles: see the kernel)
+  static constexpr bool kGroupFits = BN * kTS * 2 <= kTOffG && kYB <= kTOffG;
   // B tile elements per thread, fetched into registers at kernel start when
   // few enough (the epilogue's gather would otherwise put a memory round trip
   // after the K loop).  Not for 256 x 256 tiles: their main loop already
@@ -128,6 +144,7 @@ struct Cfg {
   static_assert(BM % (kRowsPerLoad * LW) == 0 && BN % (kRowsPerLoad * LW) == 0,
                 "X/W loads split evenly over the loaders");
   static_assert(kLds <= 160 * 1024, "LDS budget");
+  static_assert(!kTSw || (RP >= 64 && RP % 8 == 0), "swizzled T: at least 8 chunks per row");
   static_assert(STAGES >= 2, "ring: one stage being read, at least one in flight");
   static_assert(KS == 1 || (KS == 2 && BK == 64 && TM % 2 == 0), "k split: one k32 half per group");
   static_assert(BK == 32 || BK == 64, "one or two k32 substeps per stage");
@@ -262,6 +279,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   static_assert(C::KS == 1 || G == 1, "k split: one tile per workgroup");
+  static_assert(G == 1 || C::kGroupFits, "group epilogue fits in the ring");
   // With loader waves: waves [0, NWC) multiply, waves [NWC, NW) load.
   const bool mul = C::PW == 0 || wave < C::NWC;
   const int lw = C::PW == 0 ? wave : wave - C::NWC;  // loader index (loaders only)
@@ -584,7 +602,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // ---- epilogue 1: scaled T (bf16) and the B tile into LDS.  With G > 1,
   // T lives past the stage ring and is written by the first tile only.
   uint16_t* ts = reinterpret_cast<uint16_t*>(smem + (G > 1 ? C::kTOffG : 0));
-  uint16_t* bs = G > 1 ? reinterpret_cast<uint16_t*>(smem) : ts + BM * C::kTS;
+  uint16_t* bs = G > 1 ? reinterpret_cast<uint16_t*>(smem) : ts + BM * C::kTRow;
   if (g == 0 && kg == 0 && mul) {
 #pragma unroll
   for (int sl = 0; sl < C::kTSlots; ++sl) {
@@ -593,7 +611,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = wm * TM * 16 + i * 16 + lk * 4 + q;
-      ts[row * C::kTS + j] = j < r ? f2bf(scale * tacc[sl][q]) : uint16_t(0);
+      ts[C::t_idx(row, j)] = j < r ? f2bf(scale * tacc[sl][q]) : uint16_t(0);
     }
   }
   }
@@ -626,7 +644,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     const int nrow = rend - m0;
     for (int e = tid; e < nrow * r; e += C::NT) {
       const int row = e % nrow, j = e / nrow;
-      tout[(int64_t)j * ldt + m0 + row] = row < BM ? ts[row * C::kTS + j] : uint16_t(0);
+      tout[(int64_t)j * ldt + m0 + row] = row < BM ? ts[C::t_idx(row, j)] : uint16_t(0);
     }
   }
 
@@ -641,7 +659,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < TM; ++i)
         a[i] = *reinterpret_cast<const u32x4*>(
-            ts + (wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow) * C::kTS + kk * 32 + lk * 8);
+            ts + C::t_idx(wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow, kk * 32 + lk * 8));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS +
@@ -656,7 +674,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       a[i] = *reinterpret_cast<const u32x2*>(
-          ts + (wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow) * C::kTS + lk * 4);
+          ts + C::t_idx(wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow, lk * 4));
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       b[j] = *reinterpret_cast<const u32x2*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS + lk * 4);
@@ -692,8 +710,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < TH; ++i)
           a[i] = *reinterpret_cast<const u32x4*>(
-              ts + (wm * TM * 16 + ring_row_block<C>(S0 + i, rot) * 16 + lrow) * C::kTS + kk * 32 +
-              lk * 8);
+              ts + C::t_idx(wm * TM * 16 + ring_row_block<C>(S0 + i, rot) * 16 + lrow,
+                            kk * 32 + lk * 8));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS +
@@ -708,7 +726,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < TH; ++i)
         a[i] = *reinterpret_cast<const u32x2*>(
-            ts + (wm * TM * 16 + ring_row_block<C>(S0 + i, rot) * 16 + lrow) * C::kTS + lk * 4);
+            ts + C::t_idx(wm * TM * 16 + ring_row_block<C>(S0 + i, rot) * 16 + lrow, lk * 4));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         b[j] = *reinterpret_cast<const u32x2*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS + lk * 4);
@@ -840,6 +858,13 @@ using WideL = Cfg<128, 256, 2, 4, RP, 3, 64, 1, 4>;
 // against 183.5 us on 640 tiles of 128 x 256 (2.5 rounds).
 template <int RP>
 using BigNL = Cfg<256, 160, 4, 2, RP, 2, 64, 1, 4>;
+// Ranks 33-128 on large grids: 128 x 256 tiles (8 waves of 64 x 64, two
+// stages) where a workgroup walks 8 consecutive N tiles of one row block and
+// computes T = X A^T with the first only; s T (bf16) stays in the last
+// BM x RP x 2 bytes of the LDS (unpadded, swizzled), after the ring.
+template <int RP>
+using WideT = Cfg<128, 256, 2, 4, RP, 2, 64, 1, 0, 1>;
+constexpr int kWideTGroup = 8;
 // Small tiles with four loaders and four stages, for grids that the 128 x
 // 128 tile would leave under-filled: the smaller the tile, the more
 // workgroups share the streaming of W (tall-skinny and decode-like shapes).
@@ -859,8 +884,10 @@ using SmallL = Cfg<32, 32, 2, 1, RP, 4, 64, 1, 4>;
 //  * 256 x 256 (r <= 64) when there are >= 256 such tiles and the last round
 //    of them is at least 80 % full (q_proj, 512 tiles: 160 vs 202 us; the
 //    q_proj backward's dX product, 320 tiles: 211 us vs 191 us on 128 x 128);
-//  * rank 128 with >= 512 128 x 128 tiles: T shared over 2 N tiles (square
-//    16384 x 8192 x 8192: 3.27 ms; over 4 tiles 3.73 ms; unshared 3.87 ms);
+//  * rank 128 with >= 512 128 x 128 tiles: 128 x 256 tiles keeping T over 8
+//    N tiles when that grid has >= 256 workgroups (the 16384 x 8192 x 8192
+//    square: 2.73 ms), else 128 x 128 tiles sharing T over 2 N tiles (square:
+//    3.27-3.53 ms; over 4 tiles 3.73 ms; unshared 3.87 ms);
 //  * at most 256 tiles of 128 x 128: the largest loader tile (128 x 128,
 //    64 x 64, 64 x 32, 32 x 32) whose grid has at least 160 workgroups, else
 //    32 x 32.  128 x 128 keeps the work at 192 tiles (3072 x 1024 x 1024:
@@ -881,7 +908,14 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
     if (big_tiles >= 256 && big_tiles * 5 >= rounds * 256 * 4) return launch<Big<RP>>(a, s);
   }
   if constexpr (RP == 128) {
-    if (a.N > 128 && mid_tiles >= 512) return launch<Mid<RP>, 2>(a, s);
+    if (a.N > 128 && mid_tiles >= 512) {
+      // T kept over 8 N tiles of 128 x 256 when that grid still fills a round
+      // of 256 workgroups (16384 x 8192 x 8192: 2.73 ms against 3.53 ms on
+      // 128 x 128 tiles sharing T over 2; on 8192 x 4096 x 2560, 128
+      // workgroups, 442 against 368 us)
+      if (grid(128, 256 * kWideTGroup) >= 256) return launch<WideT<RP>, kWideTGroup>(a, s);
+      return launch<Mid<RP>, 2>(a, s);
+    }
   }
   if constexpr (RP <= 128) {
     if (mid_tiles <= 256) {
@@ -983,6 +1017,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 32) {
         if (props) return tile_fill<WideL<RP>, 1>(props), hipSuccess;
         return launch<WideL<RP>>(*a, s);
+      }
+      break;
+    case kTileWideT:
+      if constexpr (RP >= 64 && RP <= 128) {
+        if (props) return tile_fill<WideT<RP>, kWideTGroup>(props), hipSuccess;
+        return launch<WideT<RP>, kWideTGroup>(*a, s);
       }
       break;
     case kTileBigNL:

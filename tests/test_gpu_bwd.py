@@ -80,12 +80,14 @@ def test_bwd_mid_full(gpu_lib):
 
 
 @pytest.mark.parametrize("c", [synth.QPROJ, _case("b_m4096_n512_k4096_r16", 20, 4096, 512, 4096, 16),
-                               _case("b_m4096_n256_k4096_r128", 21, 4096, 256, 4096, 128)],
+                               _case("b_m4096_n256_k4096_r128", 21, 4096, 256, 4096, 128),
+                               _case("b_m8192_n256_k8192_r128", 22, 8192, 256, 8192, 128)],
                          ids=lambda c: c.name)
 def test_bwd_large_full(gpu_lib, c):
     """256 x 160 (rank <= 32) and grouped rank-128 dX tiles at full size
-    (the q_proj shape and two 4096-token shapes): every element of dX, dA
-    and dB."""
+    (the q_proj shape, two 4096-token shapes, and an 8192 x 8192 dX product
+    on the 128 x 256 tile that keeps s G after its ring): every element of
+    dX, dA and dB."""
     t = c.make("XWABD")
     got = _run(gpu_lib, t, c.scale)
     ref = oracle.bwd(t["X"], t["W"], t["A"], t["B"], t["dY"], c.scale)
