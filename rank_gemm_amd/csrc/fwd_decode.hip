@@ -265,6 +265,10 @@ __device__ __forceinline__ void dec_body(
   // L[m, n] = sum_j T[m, j] B[n, j]; Y = Ybase + scale * L, rounded once.
   const int n = n0 + lrow;
   if (n >= N) return;
+  // Branch-free: every load below is issued before any is waited on (a
+  // branch per rank element serialised one memory round trip each).  B is
+  // read at indices clamped into the row and zeroed past r; T's columns past
+  // r are zero (A rows past r read as zeros), so all RP terms can be summed.
   float bn[RP];
   if (b_vec) {
 #pragma unroll
@@ -273,18 +277,20 @@ __device__ __forceinline__ void dec_body(
       bn[j] = j < r ? bf2f((uint16_t)h) : 0.f;
     }
   } else {
+    uint16_t bh[RP];
 #pragma unroll
-    for (int j = 0; j < RP; ++j) bn[j] = j < r ? bf2f(B[brow * ldb + j]) : 0.f;
+    for (int j = 0; j < RP; ++j) bh[j] = B[brow * ldb + min(j, r - 1)];
+#pragma unroll
+    for (int j = 0; j < RP; ++j) bn[j] = j < r ? bf2f(bh[j]) : 0.f;
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int m = mb * 16 + lg * 4 + q;
-    if (m >= M) break;
+    const float* trow = tl + (lg * 4 + q) * C::kTS;
     float l = 0.f;
 #pragma unroll
-    for (int j = 0; j < RP; ++j)
-      if (j < r) l += tl[(lg * 4 + q) * C::kTS + j] * bn[j];
-    Y[(int64_t)m * ldy + n] = f2bf(y[q] + scale * l);
+    for (int j = 0; j < RP; ++j) l += trow[j] * bn[j];
+    if (m < M) Y[(int64_t)m * ldy + n] = f2bf(y[q] + scale * l);
   }
 }
 
