@@ -30,7 +30,8 @@ Printed: one JSON line.  Besides the headline it carries
 
 --only NAME runs just one kernel a few times (for rocprofv3); NAME is one of
 tiny, mid, q, v, sq8, sq16, sq64, sq128, dec1, dec8, dec64, decstep, merge,
-copy, bwd_mid, bwd_q, ceil_mfma, ceil_copy, ceil_read.
+copy, bwd_mid, bwd_q, ceil_mfma (all ceilings), and clock (the shader clock
+under sustained loads: the fused square, the MFMA loop, the library GEMM).
 """
 from __future__ import annotations
 
@@ -206,9 +207,13 @@ class ClockSampler:
         if not self.samples:
             return {"source": self.source, "samples": 0, "error": self.error or "no reading"}
         p10, med, p90 = pct(self.samples)
+        late = self.samples[len(self.samples) // 4:]
         return {"source": self.source, "samples": len(self.samples), "median_mhz": med,
                 "p10_mhz": p10, "p90_mhz": p90, "min_mhz": min(self.samples),
-                "max_mhz": max(self.samples)}
+                "max_mhz": max(self.samples),
+                "median_mhz_after_first_quarter": pct(late)[1] if late else None,
+                "note": "the driver's current shader-clock level, read by a host thread; "
+                        "the first samples lag the ramp from idle"}
 
 
 # ------------------------------------------------------------- ceilings
@@ -316,6 +321,57 @@ def run_ceilings(steps=20):
     return out
 
 
+def run_clock_phases(seconds=0.6):
+    """The shader clock under sustained loads, sampled every 5 ms: the fused
+    forward on the square (headline) workload, the dense MFMA loop, and the
+    library's plain bf16 GEMM (hipBLASLt via torch.matmul, no LoRA term) on
+    the same X and W, for reference.  Each phase runs about `seconds`."""
+    import torch
+    import rank_gemm_amd as rg
+    import synth
+    c = synth.SQUARE[1]
+    t = synth.fwd_case_on_device(c)
+    Y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+    L = ceil_lib()
+    wg, waves, iters = 512, 8, 5000
+    buf = torch.empty(wg * waves * 64, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(wg * 4, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    phases = [
+        ("fused_forward_square_r16", lambda i: rg.fwd(t["X"], t["W"], t["A"], t["B"], c.scale, out=Y),
+         c.flops()),
+        ("mfma_loop", lambda i: L.ceil_mfma(wg, waves, iters, buf.data_ptr(), clk.data_ptr(), st),
+         L.ceil_mfma_flops(wg, waves, iters)),
+        ("hipblaslt_plain_gemm_same_x_w", lambda i: torch.matmul(t["X"], t["W"].t(), out=Y),
+         2.0 * c.M * c.N * c.K)]
+    out = []
+    for rep in range(2):
+        for name, fn, flops in phases:
+            fn(0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(0)
+            e1.record()
+            torch.cuda.synchronize()
+            n = max(5, int(seconds / (e0.elapsed_time(e1) * 1e-3)))
+            sampler = ClockSampler(period_s=0.005)
+            with sampler:
+                e0.record()
+                for i in range(n):
+                    fn(i)
+                e1.record()
+                torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+            smp = sampler.samples[len(sampler.samples) // 4:]   # after the ramp
+            p10, med, p90 = pct(smp) if smp else (None, None, None)
+            out.append({"phase": name, "repeat": rep, "launches": n, "ms_per_launch": round(ms, 4),
+                        "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                        "clock_mhz_p10_median_p90": [p10, med, p90], "samples": len(smp),
+                        "source": sampler.source})
+    return out
+
+
 # ------------------------------------------------------------------ workloads
 
 def _fwd_line(c, ms_list, per=1, timing="", variant="tiled", ceil=None, bound="mfma"):
@@ -356,9 +412,16 @@ def run_fwd_case(rg, c, steps, warmup, rotate=1, variant="auto", graph=False, ce
         bound = "hbm" if c.M <= 64 else "mfma"
     if graph:
         reps = graph_replays(fn, steps, 10)
-        return _fwd_line(c, reps, per=steps, variant=vname, ceil=ceil, bound=bound,
-                         timing=f"HIP graph of {steps} launches over {rotate} operand sets; "
-                                "statistics over replays, per launch")
+        d = _fwd_line(c, reps, per=steps, variant=vname, ceil=ceil, bound=bound,
+                      timing=f"HIP graph of {steps} launches over {rotate} operand sets; "
+                             "statistics over replays, per launch")
+        key = {1: ("fwd_decode_m1_w4096_r16", "fwd_decode.hip"),
+               8: ("fwd_decode_m8_w4096_r16", "fwd_decode.hip"),
+               64: ("fwd_tiled_decode_m64_w4096_r16", "fwd_tiled.hip")}.get(c.M)
+        if key and c.N == 4096 and c.K == 4096 and c.r == 16:
+            tr = _traffic(key[0], [key[1], "common.h"])
+            d["traffic_bytes_per_launch"] = tr["hbm_bytes_per_launch"] if tr else None
+        return d
     times, _, _ = per_launch(fn, steps, warmup)
     return _fwd_line(c, times, variant=vname, ceil=ceil, bound=bound,
                      timing="back-to-back launches, HIP events around each")
@@ -414,6 +477,8 @@ def run_merge_pass(rg, steps, warmup, layers=36, ceil=None):
          "bytes_per_pass": int(total_bytes), "per_target_shape": shape_ms}
     if ceil and ceil.get("copy_1gib"):
         d["pct_measured_copy_ceiling"] = round(100 * gbs / ceil["copy_1gib"]["gbs_median"], 2)
+    tr = _traffic("merge_batch_36x7_r32_pass", ["merge.hip", "common.h"])
+    d["traffic_bytes_per_pass"] = tr["hbm_bytes_per_launch"] if tr else None
     return d
 
 
@@ -672,7 +737,7 @@ def main():
     def step(_):
         rg.fwd(t["X"], t["W"], t["A"], t["B"], head.scale, out=Y)
 
-    with ClockSampler() as clk:
+    with ClockSampler(period_s=0.005) as clk:
         times, region_ms, wall = per_launch(step, args.steps, args.warmup)
     ms_per_step = region_ms / args.steps
     value = head.flops() / (ms_per_step * 1e-3) / 1e12
@@ -782,6 +847,8 @@ def only(rg, name, steps, warmup):
                "gbs": 2 * n / (ms * 1e-3) / 1e9}
     elif name.startswith("ceil_"):
         res = run_ceilings(steps)
+    elif name == "clock":
+        res = run_clock_phases()
     else:
         raise SystemExit(f"unknown --only {name}")
     print(json.dumps(res), flush=True)
