@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 13
+#define LORA_ABI_VERSION 14
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -358,16 +358,20 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *  13   256 x 160   12    1               r <= 32    (two stages, 4 loaders)
  *  14   128 x 256    8    8 N tiles       64 < r <= 128 (two stages; T kept
  *                                         unpadded after the ring)
+ *  15   256 x 256    8    1               r <= 64    (four 32-deep stages,
+ *                                         ping-pong: two groups of four waves
+ *                                         alternate between multiplying and
+ *                                         reading)
  * ("T shared over g N tiles": a workgroup computes g consecutive output
  * tiles of one row block and the down-projection T only once.  Every id
- * stages 64 k per stage; the stage counts not given are two.  0 keeps
+ * but 15 stages 64 k per stage; the stage counts not given are two.  0 keeps
  * eight stages.  "k split": two groups of eight waves compute the same tile,
  * each from one 32-wide half of every stage, and their sums are added before
  * the up-projection; its results differ from the other ids' in rounding,
  * which all agree bit for bit with each other.  "4 loaders": four of the
  * waves only issue the stage loads, the other eight only multiply.)
  */
-#define LORA_TILE_COUNT 15
+#define LORA_TILE_COUNT 16
 
 typedef struct lora_tile_info {
     int32_t tile;        /* id */

@@ -19,12 +19,14 @@
 //     valid row, so rows past M, N or r and the K tail read as zeros.
 //     16-B chunks are XOR-swizzled per row so that MFMA operand reads
 //     (16 rows x one chunk per instruction) hit distinct banks.
-//     acc[BM x BN] += X W^T          (MFMA)
+//     acc[BM x BN] += X W^T          (MFMA with W as the first operand: each
+//                                     lane accumulates 4 consecutive output
+//                                     columns of one row)
 //     T[BM x RP]   += X A^T          (MFMA, reusing the X operand registers)
 //   epilogue:
 //     T -> scale * T -> bf16 -> LDS; B[BN x RP] -> LDS (zero padded)
 //     acc += (s T) B^T               (MFMA over the rank)
-//     acc -> bf16 -> LDS -> coalesced 16-B stores of Y.
+//     acc -> bf16 -> LDS (8 B per lane and block) -> coalesced 16-B stores of Y.
 #include <type_traits>
 
 #include "common.h"
@@ -68,11 +70,17 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // TS = 1 stores the epilogue's T tile unpadded (rows of RP elements) with its
 // 16-B chunks XOR-swizzled by row, so that a tile keeping T across several N
 // tiles fits T after a ring that fills all but RP x BM x 2 bytes of the LDS.
+//
+// PP = 1 runs the K loop as a ping-pong between two groups of four waves
+// (see the kernel): the first group multiplies while the second reads its
+// next fragments from LDS and issues stage loads, then the roles swap.
 template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1, int PW_ = 0,
-          int TS_ = 0>
+          int TS_ = 0, int PP_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_, BK = BK_;
   static constexpr int KS = KS_, PW = PW_;
+  static constexpr bool kPP = PP_ >= 1;
+  static constexpr bool kPPSpread = PP_ == 2;  // X/W loads among the MFMAs of M
   static constexpr int kRowB = BK * 2;                // bytes per staged row
   static constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one 1-KiB wave load covers
   static constexpr int kChunks = BK / 8;              // 16-B chunks per row
@@ -112,7 +120,7 @@ struct Cfg {
   // sends its partial T; the area starts after the epilogue's T and B tiles.
   static constexpr int kXOff = kEpiB;
   static constexpr int kXchB = KS == 2 ? WM * WN * (TM * TN + (TM * RB + WN - 1) / WN) * 1024 : 0;
-  static constexpr int kLds = cmax(cmax(STAGES * kStageB, kXOff + kXchB), cmax(kEpiB, kYB));
+  static constexpr int kLds0 = cmax(cmax(STAGES * kStageB, kXOff + kXchB), cmax(kEpiB, kYB));
   // With T kept across the N tiles of a group: T after the ring, the B tile
   // and the output staging inside it.
   static constexpr int kTOffG = STAGES * kStageB;
@@ -129,6 +137,17 @@ struct Cfg {
   static constexpr int kBPre = BN * RP / (NWC * kWave);
   static constexpr bool kBEarly = BN * RP % (NWC * kWave) == 0 && kBPre <= 8 &&
                                   BM * BN <= 128 * 128 && (BM * BN > 64 * 32 || RP <= 16);
+  // Otherwise, where it fits after the ring and the output staging without
+  // costing a workgroup per CU, the B tile is fetched at kernel start by
+  // direct loads into LDS (unpadded rows of RP elements), landing with the
+  // first stage; tiles with loader waves and the k split keep the gather
+  // after the K loop.
+  static constexpr int kBDmaOff = cmax(STAGES * kStageB, kYB);
+  static constexpr int kBDmaB = BN * RP * 2;
+  static constexpr bool kBDma = !kBEarly && PW == 0 && KS == 1 && kBDmaB % 1024 == 0 &&
+                                kBDmaOff + kBDmaB <= 160 * 1024 &&
+                                (160 * 1024) / (kBDmaOff + kBDmaB) >= (160 * 1024) / kLds0;
+  static constexpr int kLds = kBDma ? cmax(kLds0, kBDmaOff + kBDmaB) : kLds0;
   static constexpr int kTSlots = (TM * RB + WN - 1) / WN;  // T accumulators per wave
   static constexpr int kGroup = 4;         // M tiles per group (XCD-contiguous ids)
   static constexpr int kGroupShared = 8;   // M tiles swept together by all XCDs (measured best)
@@ -147,6 +166,9 @@ struct Cfg {
   static_assert(!kTSw || (RP >= 64 && RP % 8 == 0), "swizzled T: at least 8 chunks per row");
   static_assert(STAGES >= 2, "ring: one stage being read, at least one in flight");
   static_assert(KS == 1 || (KS == 2 && BK == 64 && TM % 2 == 0), "k split: one k32 half per group");
+  static_assert(!kPP || (WM * WN == 8 && KS == 1 && PW == 0 && BK == 32 && STAGES >= 3 &&
+                         (STAGES & (STAGES - 1)) == 0),
+                "ping-pong: two groups of four waves, one k32 step per stage, a power-of-two ring");
   static_assert(BK == 32 || BK == 64, "one or two k32 substeps per stage");
 };
 
@@ -258,6 +280,21 @@ __device__ __forceinline__ void issue_stage(unsigned char* smem, int buf, int k0
           off_or_oob(kin, va + sgpr(s * sa + kb)), 0, 0, 0);
 }
 
+// The A loads of one stage alone (loaders below kAN).
+template <class C>
+__device__ __forceinline__ void issue_stage_a(unsigned char* smem, int buf, int k0, int K, int wave,
+                                              int lchunk, __amdgpu_buffer_rsrc_t ra, uint32_t va,
+                                              uint32_t sa) {
+  const bool kin = k0 + lchunk * 8 < K;
+  const uint32_t kb = (uint32_t)k0 * 2;
+  unsigned char* base = smem + buf * C::kStageB + (C::BM + C::BN) * C::kRowB;
+#pragma unroll
+  for (int s = 0; s < C::kAL; ++s)
+    if (wave + s * C::LW < C::kAN)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (wave + s * C::LW) * 1024), 16,
+                                               off_or_oob(kin, va + sgpr(s * sa + kb)), 0, 0, 0);
+}
+
 // G > 1: a workgroup computes G consecutive N tiles of one M tile.  The first
 // tile runs the fused K loop (base and T = X A^T); its epilogue keeps s T
 // (bf16) in an LDS region outside the stage ring, and the later tiles run
@@ -280,6 +317,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   static_assert(C::KS == 1 || G == 1, "k split: one tile per workgroup");
   static_assert(G == 1 || C::kGroupFits, "group epilogue fits in the ring");
+  static_assert(!C::kPP || G == 1, "ping-pong: one tile per workgroup");
   // With loader waves: waves [0, NWC) multiply, waves [NWC, NW) load.
   const bool mul = C::PW == 0 || wave < C::NWC;
   const int lw = C::PW == 0 ? wave : wave - C::NWC;  // loader index (loaders only)
@@ -366,6 +404,30 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     }
   }
 
+  // G == 1, no early B: the B tile by direct loads into LDS past the ring,
+  // when every 16-B chunk of a B row is aligned and wholly inside or wholly
+  // past the rank (else the gather after the K loop).  These loads are older
+  // than every stage load, so the K loop's waits cover them.
+  constexpr bool kBDma = C::kBDma && G == 1;
+  const bool bdma = kBDma && mul && r % 8 == 0 && ldb % 8 == 0 &&
+                    (reinterpret_cast<uintptr_t>(B) & 15) == 0;
+  if constexpr (kBDma) {
+    if (bdma) {
+      const int n0 = ng0 * BN;
+      const int brows = max(0, min(BN, N - n0));
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(B + (int64_t)n0 * ldb), 0, (int)(brows * ldb * 2), 0x00020000);
+      constexpr int kBL = C::kBDmaB / 1024;  // 1-KiB loads
+      for (int p = cw; p < kBL; p += C::NWC) {
+        const int byte = p * 1024 + lane * 16;
+        const int row = byte / (RP * 2), j0 = (byte % (RP * 2)) / 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (lds_void*)(smem + C::kBDmaOff + p * 1024), 16,
+            off_or_oob(j0 < r, (uint32_t)(row * ldb * 2 + j0 * 2)), 0, 0, 0);
+      }
+    }
+  }
+
   for (int g = 0; g < G; ++g) {
   const int n0 = (ng0 + g) * BN;
   if (n0 >= N) break;  // uniform: the group's last tiles may lie past N
@@ -393,6 +455,99 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // streams.
   constexpr int NSUB = BK / 32;
   const int nk = (K + BK - 1) / BK;
+  if constexpr (C::kPP) {
+    // Ping-pong.  Waves 0-3 (group 0) and 4-7 (group 1) sit in pairs on the
+    // four SIMDs (a wave's SIMD is its index mod 4).  Each k32 stage q is a
+    // read phase R(q) -- this wave's X, W and A fragments of stage q from
+    // LDS into registers, then its share of the loads of stage q + STAGES -
+    // 1 into the ring slot that stage q - 1 has left -- and a multiply
+    // phase M(q) on those registers.  Group 1 runs one phase behind group 0
+    // and every phase ends at a barrier of all eight waves, so on each SIMD
+    // one wave issues MFMAs while the other reads: the matrix pipe is fed
+    // by one wave at a time without the two competing for it, and one
+    // register set per wave suffices.  Order of the phases (barrier b_k
+    // between phases k - 1 and k of the sequence R(0) M(0) R(1) M(1) ...):
+    // group 0 runs phase k, group 1 phase k - 1, after b_k.
+    //  * Slot reuse: stage q - 1's slot is refilled in R(q) of either group,
+    //    after both groups' R(q - 1) have waited for their reads (lgkmcnt)
+    //    and passed a barrier.
+    //  * Arrival: stage q + 1 is read from R(q + 1) of group 0 on; every
+    //    wave waits for its own loads of that stage (vmcnt, two newer stages
+    //    in flight) before the barrier that precedes it: group 0 at the end
+    //    of M(q), group 1 at the end of R(q).
+    // Loads of stages past K read zeros; all of them have landed (vmcnt 0)
+    // before the epilogue reuses the LDS.
+    constexpr int S = STAGES;
+    const int grp = wave >> 2;
+    const int px0 = wm * TM * 16 + lrow;
+    const int pw0 = wn * TN * 16 + lrow;
+    Frags<C> f;
+    auto bar = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+      issue_stage<C, WT>(smem, st, st * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+    wait_stages<C, S - 2, WT>(wave);
+    bar();
+    if (grp == 1) bar();
+    for (int q = 0; q < nk; ++q) {
+      const unsigned char* xs = smem + (q & (S - 1)) * C::kStageB;
+      const unsigned char* ws = xs + BM * kRowB;
+      const unsigned char* as = ws + BN * kRowB;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        f.a[i] = *reinterpret_cast<const u32x4*>(
+            xs + stage_off<BK>(px0 + ring_row_block<C>(i, rot) * 16, lk));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        f.b[j] = *reinterpret_cast<const u32x4*>(ws + stage_off<BK>(pw0 + j * 16, lk));
+#pragma unroll
+      for (int u = 0; u < C::kTF; ++u)
+        f.t[u] = *reinterpret_cast<const u32x4*>(as + stage_off<BK>(t_block<C>(wn, u) * 16 + lrow, lk));
+      wait_lgkm0();
+      __builtin_amdgcn_sched_barrier(0);
+      const int ls = (q + S - 1) & (S - 1);
+      const int lk0 = (q + S - 1) * BK;
+      if constexpr (C::kPPSpread) {
+        issue_stage_a<C>(smem, ls, lk0, K, wave, lchunk, ra, va, sa);
+        // Newer than stage q + 1: stage q + 2 and the A load of q + 3.
+        if (grp == 1) {
+          if (wave < C::kAN) wait_vmcnt<C::kLoadsHi + 1>();
+          else wait_vmcnt<C::kLoadsLo>();
+        }
+      } else {
+        issue_stage<C, WT>(smem, ls, lk0, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+        if (grp == 1) wait_stages<C, S - 2, WT>(wave);
+      }
+      bar();
+      t_update_ab<C>(f.a, f.t, tacc);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(f.b[j], f.a[i], acc[i][j]);
+      if constexpr (C::kPPSpread) {
+        issue_stage<C, false>(smem, ls, lk0, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+        // One X or W load after every eighth MFMA.
+        constexpr int kXW = C::kXL + C::kWL;
+        constexpr int kM = C::kTSlots + TM * TN;
+        constexpr int kEvery = kM / (kXW + 1);
+#pragma unroll
+        for (int d = 0; d < kXW; ++d) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kEvery, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // VMEM (DMA) issue
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kM - kXW * kEvery, 0);
+      }
+      if (grp == 0) wait_stages<C, S - 2, WT>(wave);
+      bar();
+    }
+    if (grp == 0) bar();
+    wait_vmcnt<0>();
+    return;
+  } else {
   if constexpr (C::PW > 0) {
     if (!mul) {
       // Loader: the same barriers as the multiplying waves (one after stage
@@ -480,7 +635,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(cur.a[i], bc[j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(bc[j], cur.a[i], acc[i][j]);
       cur.a[i] = *reinterpret_cast<const u32x4*>(
           xs + stage_off<BK>(xrow0 + ring_row_block<C>(i, rot) * 16, cc));
     }
@@ -542,6 +697,7 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     rslot = nslot;
   }
   }
+  }  // not ping-pong
   };  // kloop
   if (g == 0) kloop(std::true_type{});
   else kloop(std::false_type{});
@@ -603,6 +759,13 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // T lives past the stage ring and is written by the first tile only.
   uint16_t* ts = reinterpret_cast<uint16_t*>(smem + (G > 1 ? C::kTOffG : 0));
   uint16_t* bs = G > 1 ? reinterpret_cast<uint16_t*>(smem) : ts + BM * C::kTRow;
+  int bst = C::kTS;  // B tile row stride (elements)
+  if constexpr (kBDma) {
+    if (bdma) {
+      bs = reinterpret_cast<uint16_t*>(smem + C::kBDmaOff);
+      bst = RP;
+    }
+  }
   if (g == 0 && kg == 0 && mul) {
 #pragma unroll
   for (int sl = 0; sl < C::kTSlots; ++sl) {
@@ -624,11 +787,13 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       }
     }
   } else {
-    for (int e = tid; e < BN * RP; e += C::NT) {
-      const int n = e / RP, j = e % RP;
-      uint16_t v = 0;
-      if (j < r && n0 + n < N) v = B[(int64_t)(n0 + n) * ldb + j];
-      bs[n * C::kTS + j] = v;
+    if (!bdma) {
+      for (int e = tid; e < BN * RP; e += C::NT) {
+        const int n = e / RP, j = e % RP;
+        uint16_t v = 0;
+        if (j < r && n0 + n < N) v = B[(int64_t)(n0 + n) * ldb + j];
+        bs[n * C::kTS + j] = v;
+      }
     }
   }
   __syncthreads();
@@ -662,12 +827,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
             ts + C::t_idx(wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow, kk * 32 + lk * 8));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS +
+        b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * bst +
                                                kk * 32 + lk * 8);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(b[j], a[i], acc[i][j]);
     }
   } else {
     u32x2 a[TM], b[TN];
@@ -677,11 +842,11 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
           ts + C::t_idx(wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow, lk * 4));
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      b[j] = *reinterpret_cast<const u32x2*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS + lk * 4);
+      b[j] = *reinterpret_cast<const u32x2*>(bs + (wn * TN * 16 + j * 16 + lrow) * bst + lk * 4);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x16(b[j], a[i], acc[i][j]);
   }
   __syncthreads();
 
@@ -690,12 +855,11 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lk * 4 + q;
-        ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
-      }
+    for (int j = 0; j < TN; ++j) {
+      const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow;
+      *reinterpret_cast<u32x2*>(ys + row * C::kYS + wn * TN * 16 + j * 16 + lk * 4) =
+          u32x2{pack_bf2(acc[i][j][0], acc[i][j][1]), pack_bf2(acc[i][j][2], acc[i][j][3])};
+    }
   }
   __syncthreads();
   } else {
@@ -714,12 +878,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
                             kk * 32 + lk * 8));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS +
+          b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * bst +
                                                  kk * 32 + lk * 8);
 #pragma unroll
         for (int i = 0; i < TH; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[S0 + i][j] = mfma16x16x32(a[i], b[j], acc[S0 + i][j]);
+          for (int j = 0; j < TN; ++j) acc[S0 + i][j] = mfma16x16x32(b[j], a[i], acc[S0 + i][j]);
       }
     } else {
       u32x2 a[TH], b[TN];
@@ -729,11 +893,11 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
             ts + C::t_idx(wm * TM * 16 + ring_row_block<C>(S0 + i, rot) * 16 + lrow, lk * 4));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const u32x2*>(bs + (wn * TN * 16 + j * 16 + lrow) * C::kTS + lk * 4);
+        b[j] = *reinterpret_cast<const u32x2*>(bs + (wn * TN * 16 + j * 16 + lrow) * bst + lk * 4);
 #pragma unroll
       for (int i = 0; i < TH; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[S0 + i][j] = mfma16x16x16(a[i], b[j], acc[S0 + i][j]);
+        for (int j = 0; j < TN; ++j) acc[S0 + i][j] = mfma16x16x16(b[j], a[i], acc[S0 + i][j]);
     }
   };
   if (mul) {
@@ -748,12 +912,11 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
     for (int i = S0; i < S0 + TH; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lk * 4 + q;
-          ys[row * C::kYS + wn * TN * 16 + j * 16 + lrow] = f2bf(acc[i][j][q]);
-        }
+      for (int j = 0; j < TN; ++j) {
+        const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow;
+        *reinterpret_cast<u32x2*>(ys + row * C::kYS + wn * TN * 16 + j * 16 + lk * 4) =
+            u32x2{pack_bf2(acc[i][j][0], acc[i][j][1]), pack_bf2(acc[i][j][2], acc[i][j][3])};
+      }
   };
   if (mul) {
     if (kg == 0) epi3(std::integral_constant<int, 0>{});
@@ -818,6 +981,11 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 // whole 128-B lines per row.
 template <int RP>
 using Big = Cfg<256, 256, 2, 4, RP, 2, 64>;
+// The same tile with the ping-pong K loop: 32-deep stages, four in flight.
+template <int RP>
+using BigPP = Cfg<256, 256, 2, 4, RP, 4, 32, 1, 0, 0, 1>;
+template <int RP>
+using BigPP2 = Cfg<256, 256, 2, 4, RP, 4, 32, 1, 0, 0, 2>;
 // (Measured and dropped: the same tile as 4 waves of 128 x 128, one per
 // SIMD with the accumulators in AGPRs, reads a third fewer LDS bytes per
 // MFMA but ran 1.48x slower on 16384 x 8192 x 8192 r16 (2621 vs 1768 us) and
@@ -881,9 +1049,10 @@ using SmallL = Cfg<32, 32, 2, 1, RP, 4, 64, 1, 4>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
 // measurements on the benchmark shapes and on rotating operand sets:
-//  * 256 x 256 (r <= 64) when there are >= 256 such tiles and the last round
-//    of them is at least 80 % full (q_proj, 512 tiles: 160 vs 202 us; the
-//    q_proj backward's dX product, 320 tiles: 211 us vs 191 us on 128 x 128);
+//  * 256 x 256 (r <= 64; the ping-pong K loop at rank 64) when there are
+//    >= 256 such tiles and the last round of them is at least 80 % full
+//    (q_proj, 512 tiles: 160 vs 202 us; the q_proj backward's dX product,
+//    320 tiles: 211 us vs 191 us on 128 x 128);
 //  * rank 128 with >= 512 128 x 128 tiles: 128 x 256 tiles keeping T over 8
 //    N tiles when that grid has >= 256 workgroups (the 16384 x 8192 x 8192
 //    square: 2.73 ms), else 128 x 128 tiles sharing T over 2 N tiles (square:
@@ -905,7 +1074,12 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
   if constexpr (RP <= 64) {
     const int64_t big_tiles = grid(256, 256);
     const int64_t rounds = (big_tiles + 255) / 256;
-    if (big_tiles >= 256 && big_tiles * 5 >= rounds * 256 * 4) return launch<Big<RP>>(a, s);
+    if (big_tiles >= 256 && big_tiles * 5 >= rounds * 256 * 4) {
+      // rank 64: the ping-pong K loop (16384 x 8192 x 8192: 1.96-2.00 ms
+      // against 1.99-2.05 on the two-stage ring; the ring is ahead at rank 16)
+      if constexpr (RP == 64) return launch<BigPP<RP>>(a, s);
+      return launch<Big<RP>>(a, s);
+    }
   }
   if constexpr (RP == 128) {
     if (a.N > 128 && mid_tiles >= 512) {
@@ -1029,6 +1203,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 32) {
         if (props) return tile_fill<BigNL<RP>, 1>(props), hipSuccess;
         return launch<BigNL<RP>>(*a, s);
+      }
+      break;
+    case kTileBigPP:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<BigPP<RP>, 1>(props), hipSuccess;
+        return launch<BigPP<RP>>(*a, s);
       }
       break;
     case kTileSqL:
