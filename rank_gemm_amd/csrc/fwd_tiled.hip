@@ -1046,6 +1046,15 @@ template <int RP>
 using TallL = Cfg<64, 32, 4, 1, RP, 4, 64, 1, 4>;
 template <int RP>
 using SmallL = Cfg<32, 32, 2, 1, RP, 4, 64, 1, 4>;
+// The same two tiles with eight stages in flight, for grids of at most one
+// workgroup per CU, where the LDS that a second workgroup would have used
+// holds more of the W stream in flight instead (64 x 4096 x 4096 r16 on
+// 32 x 32: 15.1-15.3 against 17.6-17.8 us; 128 x 4096 x 4096 on 64 x 32:
+// 19.1 against 20.1 us; twelve stages no better than eight).
+template <int RP>
+using TallL8 = Cfg<64, 32, 4, 1, RP, 8, 64, 1, 4>;
+template <int RP>
+using SmallL8 = Cfg<32, 32, 2, 1, RP, 8, 64, 1, 4>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
 // measurements on the benchmark shapes and on rotating operand sets:
@@ -1059,7 +1068,8 @@ using SmallL = Cfg<32, 32, 2, 1, RP, 4, 64, 1, 4>;
 //    3.27-3.53 ms; over 4 tiles 3.73 ms; unshared 3.87 ms);
 //  * at most 256 tiles of 128 x 128: the largest loader tile (128 x 128,
 //    64 x 64, 64 x 32, 32 x 32) whose grid has at least 160 workgroups, else
-//    32 x 32.  128 x 128 keeps the work at 192 tiles (3072 x 1024 x 1024:
+//    32 x 32; 64 x 32 and 32 x 32 with eight stages when their grid is at
+//    most 256 workgroups.  128 x 128 keeps the work at 192 tiles (3072 x 1024 x 1024:
 //    12.6 vs 16.7 us on 64 x 64) and gives it up at 128 (2048 x 1024 x 4096:
 //    40.1 vs 38.4 us);
 //  * rank <= 32 past that: 128 x 256 with loaders (8192 x 1024 x 2560 r32:
@@ -1097,7 +1107,11 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
       if (mid_tiles >= kFill) return launch<Mid3L<RP>>(a, s);
       if constexpr (RP <= 64) {
         if (grid(64, 64) >= kFill) return launch<SqL<RP>>(a, s);
-        if (grid(64, 32) >= kFill) return launch<TallL<RP>>(a, s);
+        if (grid(64, 32) >= kFill) {
+          if (grid(64, 32) <= 256) return launch<TallL8<RP>>(a, s);
+          return launch<TallL<RP>>(a, s);
+        }
+        if (grid(32, 32) <= 256) return launch<SmallL8<RP>>(a, s);
         return launch<SmallL<RP>>(a, s);
       }
       return launch<Mid3L<RP>>(a, s);
@@ -1221,6 +1235,18 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 64) {
         if (props) return tile_fill<TallL<RP>, 1>(props), hipSuccess;
         return launch<TallL<RP>>(*a, s);
+      }
+      break;
+    case kTileTallL8:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<TallL8<RP>, 1>(props), hipSuccess;
+        return launch<TallL8<RP>>(*a, s);
+      }
+      break;
+    case kTileSmallL8:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<SmallL8<RP>, 1>(props), hipSuccess;
+        return launch<SmallL8<RP>>(*a, s);
       }
       break;
     case kTileSmallL:

@@ -84,7 +84,8 @@ enum TileId { kTileTall = 0, kTileMid = 1, kTileMidG2 = 2, kTileMidG4 = 3, kTile
               kTileBigG2 = 5, kTileMid3 = 6, kTileMidK2 = 7,
               kTileMid3L = 8, kTileWideL = 9,
               kTileSqL = 10, kTileTallL = 11, kTileSmallL = 12, kTileBigNL = 13,
-              kTileWideT = 14, kTileBigPP = 15, kTileCount = 16 };
+              kTileWideT = 14, kTileBigPP = 15, kTileTallL8 = 16, kTileSmallL8 = 17,
+              kTileCount = 18 };
 struct TileProps {
   int bm, bn, waves, stages, bk, group, rank_pad, lds_bytes, k_split;
   const void* kernel;
