@@ -305,6 +305,171 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
                                   blockIdx.x * 16, smem);
 }
 
+// One token (M = 1): the same workgroup partition (16 rows of W per
+// workgroup, 8 waves splitting K), but every operand is loaded as whole 128-B
+// lines -- lane l reads row 8 h + l / 8 of a 16-row block at k = 64 s +
+// 8 (l % 8), so one 16-B-per-lane load covers 8 rows x 128 B -- and the dot
+// products run on the VALU (v_dot2_f32_bf16): with one token the MFMA's 16
+// token rows would be 15/16 idle anyway, and its operand layout needs 16 rows
+// x 64 B per load.  A load's cost in the load pipe follows the cache lines it
+// touches, and each workgroup re-reads all of A next to its share of W, so
+// whole-line loads of both cut the lines per byte in half (measured with a
+// W-and-A stream alone: 7.9 against 10.1 us per launch for 32 MiB of W).
+// Each lane accumulates its 8-element pieces of rows (8 h + l / 8) of Ybase
+// and of T; the 8 lanes of a row are added by a fixed butterfly, the waves
+// in wave order through LDS, and the epilogue is the decode kernel's.
+template <int RB, int R>
+__global__ __launch_bounds__(512) void fwd_decode_row_kernel(
+    int N, int K, int r, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    int64_t ldw, const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+    int64_t ldb, float scale, uint16_t* __restrict__ Y, int b_vec) {
+  constexpr int NW = 8, RP = RB * 16;
+  static_assert(R <= 8 && 2 * RB * R + 2 * R < 64, "one 1-KiB X piece per wave and round");
+  __shared__ float red[NW][16 + RP];
+  __shared__ __attribute__((aligned(16))) unsigned char xsh[NW][1024];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 3, c = lane & 7;
+  const int n0 = blockIdx.x * 16;
+  const int wrows = min(16, N - n0);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * ldw), 0, (int)(wrows * ldw * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(r * lda * 2), 0x00020000);
+  // Rows 8 h + g of the 16-row W block and of the rank blocks.
+  const uint32_t wrow[2] = {(uint32_t)g * (uint32_t)ldw * 2, (uint32_t)(8 + g) * (uint32_t)ldw * 2};
+  uint32_t arow[2 * RB];
+#pragma unroll
+  for (int q = 0; q < 2 * RB; ++q) arow[q] = (uint32_t)(8 * q + g) * (uint32_t)lda * 2;
+
+  // The epilogue's B row (lane < 16: row n0 + lane), as in the decode kernel.
+  u32x4 bv[RP / 8];
+  const int64_t brow = min(n0 + (lane & 15), N - 1);
+  if (b_vec && wave == 0 && lane < 16) {
+#pragma unroll
+    for (int q = 0; q < RP / 8; ++q)
+      bv[q] = *reinterpret_cast<const u32x4*>(B + brow * ldb + min(q * 8, (r - 1) & ~7));
+  }
+
+  float yacc[2] = {0.f, 0.f};
+  float tacc[2 * RB];
+#pragma unroll
+  for (int q = 0; q < 2 * RB; ++q) tacc[q] = 0.f;
+  // acc + sum of the 8 products, in element-pair order.  (The pairs are
+  // taken as swizzles of the 8-wide vector: a dynamically indexed dword
+  // bit-cast to a pair miscompiled here to the first dword every time.)
+  auto dot8 = [](const u32x4& p, const u32x4& q, float acc) {
+    const bf16x8 pv = __builtin_bit_cast(bf16x8, p), qv = __builtin_bit_cast(bf16x8, q);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s01, qv.s01, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s23, qv.s23, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s45, qv.s45, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s67, qv.s67, acc, false);
+    return acc;
+  };
+  // Wave w takes R consecutive 64-deep segments per round.
+  const int nseg = (K + 63) >> 6;
+  for (int s0 = wave * R; s0 < nseg; s0 += NW * R) {
+    u32x4 x[R], w[R][2], a[R][2 * RB];
+    // The round's X piece (R segments of 128 B) by one DMA into this wave's
+    // LDS slot, lane i chunk i; lanes past the round read zeros.
+    {
+      const int k = (s0 + (lane >> 3)) * 64 + c * 8;
+      const uint32_t ko = (lane >> 3) < R && k < K ? (uint32_t)k * 2 : kDecOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)xsh[wave], 16, ko, 0, 0, 0);
+    }
+    // The DMA must stay the oldest load of the round (the wait below counts
+    // on it).
+    __builtin_amdgcn_sched_barrier(0);
+    // Rank 16: W (from HBM) and A (from L2) segment by segment, W first
+    // (1 x 4096 x 4096: 9.2 us against 10.0 with all A loads first).  Rank
+    // 32, where A is twice W: all A loads first (1 x 9728 x 2560: 19.3
+    // against 20.7 us interleaved).
+    auto wload = [&](int u) {
+      const int k = (s0 + u) * 64 + c * 8;
+      const uint32_t ko = k < K ? (uint32_t)k * 2 : kDecOob;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) w[u][h] = bload(rw, k < K ? wrow[h] + ko : kDecOob);
+    };
+    auto aload = [&](int u) {
+      const int k = (s0 + u) * 64 + c * 8;
+      const uint32_t ko = k < K ? (uint32_t)k * 2 : kDecOob;
+#pragma unroll
+      for (int q = 0; q < 2 * RB; ++q) a[u][q] = bload(ra, k < K ? arow[q] + ko : kDecOob);
+    };
+    if constexpr (RB == 1) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        wload(u);
+        aload(u);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < R; ++u) aload(u);
+#pragma unroll
+      for (int u = 0; u < R; ++u) wload(u);
+    }
+    // Every load of the round in flight before the first product; then the
+    // X piece (all later loads may still be in flight) from LDS.
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 * RB * R + 2 * R>();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < R; ++u) x[u] = *reinterpret_cast<const u32x4*>(&xsh[wave][u * 128 + c * 16]);
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+#pragma unroll
+      for (int q = 0; q < 2 * RB; ++q) tacc[q] = dot8(a[u][q], x[u], tacc[q]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) yacc[h] = dot8(w[u][h], x[u], yacc[h]);
+    }
+  }
+  // The 8 lanes of a row: a fixed butterfly (every lane ends with the same
+  // sum), then lane c == 0 of each row group publishes the wave's partials.
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) yacc[h] += __shfl_xor(yacc[h], m);
+#pragma unroll
+    for (int q = 0; q < 2 * RB; ++q) tacc[q] += __shfl_xor(tacc[q], m);
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) red[wave][8 * h + g] = yacc[h];
+#pragma unroll
+    for (int q = 0; q < 2 * RB; ++q) red[wave][16 + 8 * q + g] = tacc[q];
+  }
+  __syncthreads();
+  if (wave != 0 || lane >= 16) return;
+  const int n = n0 + lane;
+  if (n >= N) return;
+  float y = 0.f;
+  for (int v = 0; v < NW; ++v) y += red[v][lane];
+  // T[j] summed over the waves in wave order, then the rank sum in j order;
+  // branch-free as in the decode kernel: T's columns past r are zero (A rows
+  // past r read as zeros) and B is zeroed past r.
+  auto tcol = [&](int j) {
+    float tj = 0.f;
+    for (int v = 0; v < NW; ++v) tj += red[v][16 + j];
+    return tj;
+  };
+  float l = 0.f;
+  if (b_vec) {
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+      const uint32_t hw = (bv[j >> 3][(j >> 1) & 3] >> ((j & 1) * 16)) & 0xFFFFu;
+      l += tcol(j) * (j < r ? bf2f((uint16_t)hw) : 0.f);
+    }
+  } else {
+    uint16_t bh[RP];
+#pragma unroll
+    for (int j = 0; j < RP; ++j) bh[j] = B[brow * ldb + min(j, r - 1)];
+#pragma unroll
+    for (int j = 0; j < RP; ++j) l += tcol(j) * (j < r ? bf2f(bh[j]) : 0.f);
+  }
+  Y[n] = f2bf(y + scale * l);
+}
+
 // Batched decode: up to kDecBatch forwards with the same M and rank class per
 // launch, their descriptors in the kernel arguments (no device memory).
 // Workgroups [first[t], first[t + 1]) belong to forward t; a workgroup finds
@@ -485,7 +650,20 @@ hipError_t launch_dec_rb(const FwdArgs& a, const FwdArgs* batch, int i0, int i1,
 
 }  // namespace
 
+// One token: whole-line loads and VALU dot products (fwd_decode_row_kernel).
+template <int RB, int R>
+hipError_t launch_dec_row(const FwdArgs& a, hipStream_t s) {
+  const int blocks = (int)((a.N + 15) / 16);
+  hipLaunchKernelGGL((fwd_decode_row_kernel<RB, R>), dim3(blocks), dim3(512), 0, s, (int)a.N,
+                     (int)a.K, (int)a.r, static_cast<const uint16_t*>(a.X),
+                     static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
+                     a.lda, static_cast<const uint16_t*>(a.B), a.ldb, a.scale,
+                     static_cast<uint16_t*>(a.Y), dec_b_vec(a));
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s) {
+  if (a.M == 1) return a.r <= 16 ? launch_dec_row<1, 8>(a, s) : launch_dec_row<2, 4>(a, s);
   return a.r <= 16 ? launch_dec_rb<1>(a, nullptr, 0, 0, nullptr, s)
                    : launch_dec_rb<2>(a, nullptr, 0, 0, nullptr, s);
 }

@@ -154,6 +154,9 @@ EDGE = [
     (33, 4100, 2056, 16, "bf16", "decode"),
     (64, 513, 4104, 32, "bf16", "decode"),
     (17, 513, 4104, 20, "bf16", "decode"),
+    (1, 4100, 2056, 32, "bf16", "decode"),      # one token: ragged N, K not a multiple of 64
+    (1, 33, 520, 17, "bf16", "decode"),
+    (1, 17, 8, 9, "bf16", "decode"),
     (5, 7, 12, 3, "f32", "tiled"),
     (65, 70, 516, 20, "f32", "tiled"),
     (130, 129, 64, 256, "f32", "tiled"),
@@ -240,6 +243,8 @@ INT_CASES = [
     (64, 70, 136, 1, 1.0, "bf16", "decode"),
     (61, 70, 136, 2, 2.0, "bf16", "tiled"),
     (9, 33, 256, 3, 2.0, "bf16", "decode"),
+    (1, 70, 200, 3, 2.0, "bf16", "decode"),
+    (1, 33, 256, 20, 0.5, "bf16", "decode"),
     (67, 130, 200, 2, 2.0, "f32", "tiled"),
 ]
 
