@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 15
+#define LORA_ABI_VERSION 16
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -364,6 +364,8 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *                                         reading)
  *  16   64 x 32      8    1               r <= 64    (eight stages, 4 loaders)
  *  17   32 x 32      6    1               r <= 64    (eight stages, 4 loaders)
+ *  18   256 x 256    8    1               r <= 64    (two stages; waves 0-3
+ *                                         issue all stage loads)
  * ("T shared over g N tiles": a workgroup computes g consecutive output
  * tiles of one row block and the down-projection T only once.  Every id
  * but 15 stages 64 k per stage; the stage counts not given are two.  0 keeps
@@ -373,7 +375,7 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  * which all agree bit for bit with each other.  "4 loaders": four of the
  * waves only issue the stage loads, the other eight only multiply.)
  */
-#define LORA_TILE_COUNT 18
+#define LORA_TILE_COUNT 19
 
 typedef struct lora_tile_info {
     int32_t tile;        /* id */

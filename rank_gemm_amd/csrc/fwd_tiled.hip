@@ -71,11 +71,17 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // 16-B chunks XOR-swizzled by row, so that a tile keeping T across several N
 // tiles fits T after a ring that fills all but RP x BM x 2 bytes of the LDS.
 //
+// LD > 0 (without loader waves): only multiplying waves [0, LD) issue the
+// stage loads, each LD-th load of every stage.  In the 256 x 256 tile the
+// first four waves reach each stage's barrier well ahead of the other four
+// (they win the SIMD's issue arbitration); giving them the loads evens the
+// two out.
+//
 // PP = 1 runs the K loop as a ping-pong between two groups of four waves
 // (see the kernel): the first group multiplies while the second reads its
 // next fragments from LDS and issues stage loads, then the roles swap.
 template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1, int PW_ = 0,
-          int TS_ = 0, int PP_ = 0>
+          int TS_ = 0, int PP_ = 0, int LD_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_, BK = BK_;
   static constexpr int KS = KS_, PW = PW_;
@@ -86,7 +92,7 @@ struct Cfg {
   static constexpr int kChunks = BK / 8;              // 16-B chunks per row
   static constexpr int NWC = WM * WN * KS;          // multiplying waves
   static constexpr int NW = NWC + PW;               // all waves
-  static constexpr int LW = PW > 0 ? PW : NWC;      // waves that issue the stage loads
+  static constexpr int LW = PW > 0 ? PW : (LD_ > 0 ? LD_ : NWC);  // waves that issue the stage loads
   static constexpr int NT = NW * kWave;
   static constexpr int TM = BM / WM / 16;
   static constexpr int TN = BN / WN / 16;
@@ -166,6 +172,7 @@ struct Cfg {
   static_assert(!kTSw || (RP >= 64 && RP % 8 == 0), "swizzled T: at least 8 chunks per row");
   static_assert(STAGES >= 2, "ring: one stage being read, at least one in flight");
   static_assert(KS == 1 || (KS == 2 && BK == 64 && TM % 2 == 0), "k split: one k32 half per group");
+  static_assert(LD_ == 0 || (PW == 0 && KS == 1 && PP_ == 0 && LD_ <= NWC), "load subset");
   static_assert(!kPP || (WM * WN == 8 && KS == 1 && PW == 0 && BK == 32 && STAGES >= 3 &&
                          (STAGES & (STAGES - 1)) == 0),
                 "ping-pong: two groups of four waves, one k32 step per stage, a power-of-two ring");
@@ -321,6 +328,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   // With loader waves: waves [0, NWC) multiply, waves [NWC, NW) load.
   const bool mul = C::PW == 0 || wave < C::NWC;
   const int lw = C::PW == 0 ? wave : wave - C::NWC;  // loader index (loaders only)
+  // Without loader waves: does this wave issue stage loads (all do unless LD)?
+  const bool ldr = C::PW > 0 || C::LW == C::NWC || wave < C::LW;
   const int cw = C::PW == 0 ? wave : (mul ? wave : 0);
   const int wgi = C::KS == 1 ? cw : cw % (C::WM * WN);  // wave within its k group
   const int kg = C::KS == 1 ? 0 : cw / (C::WM * WN);     // k group (KS = 2: its k32 half)
@@ -572,14 +581,16 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   } else {
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
-      issue_stage<C, WT>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
+      if (ldr) issue_stage<C, WT>(smem, s, s * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va, sx, sw, sa);
   }
 
   const int xrow0 = wm * TM * 16 + lrow;  // + 16 * ring_row_block(k) for ring slot k
   const int wrow0 = wn * TN * 16 + lrow;
   Frags<C> cur;
   const int lk0 = C::KS == 2 ? kg * 4 + lk : lk;  // logical chunk of this wave's first k32
-  if constexpr (C::PW == 0) wait_stages<C, STAGES - 1, WT>(wave);
+  if constexpr (C::PW == 0) {
+    if (ldr) wait_stages<C, STAGES - 1, WT>(wave);
+  }
   __builtin_amdgcn_s_barrier();
   {
     const unsigned char* xs = smem;
@@ -611,12 +622,16 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       // flight; this wave's reads of stage kt are complete.  After the
       // barrier every wave is past both.  A bare s_barrier: a fence would
       // drain every stage in flight.
-      if constexpr (C::PW == 0) wait_stages<C, STAGES - 2, WT>(wave);
+      if constexpr (C::PW == 0) {
+        if (ldr) wait_stages<C, STAGES - 2, WT>(wave);
+      }
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      if constexpr (C::PW == 0)
-        issue_stage<C, WT>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw, va,
-                           sx, sw, sa);
+      if constexpr (C::PW == 0) {
+        if (ldr)
+          issue_stage<C, WT>(smem, rslot, (kt + STAGES) * BK, K, wave, lchunk, rx, rw, ra, vx, vw,
+                             va, sx, sw, sa);
+      }
     }
     const unsigned char* xs = smem + (sync ? nslot : rslot) * C::kStageB;
     const unsigned char* ws = xs + BM * kRowB;
@@ -986,6 +1001,13 @@ template <int RP>
 using BigPP = Cfg<256, 256, 2, 4, RP, 4, 32, 1, 0, 0, 1>;
 template <int RP>
 using BigPP2 = Cfg<256, 256, 2, 4, RP, 4, 32, 1, 0, 0, 2>;
+// The two-stage 256 x 256 tile with the stage loads issued by waves 0-3 only
+// (see LD): 16384 x 8192 x 8192 r16 1.57-1.60 ms against 1.64-1.69, r64
+// 1.84 against 2.01 (and 1.96 on the ping-pong tile), q_proj 145-150 against
+// 158-163 us; with waves 0-1 only 1.66 ms.  A single round of tiles (4096^3)
+// runs 5 % slower: four waves fill the first two stages alone.
+template <int RP>
+using BigL4 = Cfg<256, 256, 2, 4, RP, 2, 64, 1, 0, 0, 0, 4>;
 // (Measured and dropped: the same tile as 4 waves of 128 x 128, one per
 // SIMD with the accumulators in AGPRs, reads a third fewer LDS bytes per
 // MFMA but ran 1.48x slower on 16384 x 8192 x 8192 r16 (2621 vs 1768 us) and
@@ -1058,8 +1080,9 @@ using SmallL8 = Cfg<32, 32, 2, 1, RP, 8, 64, 1, 4>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
 // measurements on the benchmark shapes and on rotating operand sets:
-//  * 256 x 256 (r <= 64; the ping-pong K loop at rank 64) when there are
-//    >= 256 such tiles and the last round of them is at least 80 % full
+//  * 256 x 256 (r <= 64; its stage loads from four of the eight waves when
+//    there is more than one round) when there are >= 256 such tiles and the
+//    last round of them is at least 80 % full
 //    (q_proj, 512 tiles: 160 vs 202 us; the q_proj backward's dX product,
 //    320 tiles: 211 us vs 191 us on 128 x 128);
 //  * rank 128 with >= 512 128 x 128 tiles: 128 x 256 tiles keeping T over 8
@@ -1085,9 +1108,8 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
     const int64_t big_tiles = grid(256, 256);
     const int64_t rounds = (big_tiles + 255) / 256;
     if (big_tiles >= 256 && big_tiles * 5 >= rounds * 256 * 4) {
-      // rank 64: the ping-pong K loop (16384 x 8192 x 8192: 1.96-2.00 ms
-      // against 1.99-2.05 on the two-stage ring; the ring is ahead at rank 16)
-      if constexpr (RP == 64) return launch<BigPP<RP>>(a, s);
+      // two or more rounds: stage loads from waves 0-3 only
+      if (big_tiles > 256) return launch<BigL4<RP>>(a, s);
       return launch<Big<RP>>(a, s);
     }
   }
@@ -1223,6 +1245,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 64) {
         if (props) return tile_fill<BigPP<RP>, 1>(props), hipSuccess;
         return launch<BigPP<RP>>(*a, s);
+      }
+      break;
+    case kTileBigL4:
+      if constexpr (RP <= 64) {
+        if (props) return tile_fill<BigL4<RP>, 1>(props), hipSuccess;
+        return launch<BigL4<RP>>(*a, s);
       }
       break;
     case kTileSqL:
