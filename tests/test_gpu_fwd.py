@@ -160,6 +160,7 @@ EDGE = [
     (5, 7, 12, 3, "f32", "tiled"),
     (65, 70, 516, 20, "f32", "tiled"),
     (130, 129, 64, 256, "f32", "tiled"),
+    (1030, 1030, 72, 20, "f32", "tiled"),       # 64 x 64 fp32 tiles (>= 128 of them), ragged
 ]
 
 
