@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 16
+#define LORA_ABI_VERSION 17
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -366,16 +366,21 @@ int64_t lora_bwd_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, int6
  *  17   32 x 32      6    1               r <= 64    (eight stages, 4 loaders)
  *  18   256 x 256    8    1               r <= 64    (two stages; waves 0-3
  *                                         issue all stage loads)
+ *  19   256 x 256    8    8 N tiles       32 < r <= 128 (T computed once, in
+ *                                         a prologue, and kept in LDS after
+ *                                         the ring; stages hold X and W only:
+ *                                         two 64-deep for r <= 64, three
+ *                                         32-deep above; waves 0-3 load)
  * ("T shared over g N tiles": a workgroup computes g consecutive output
  * tiles of one row block and the down-projection T only once.  Every id
- * but 15 stages 64 k per stage; the stage counts not given are two.  0 keeps
+ * but 15 and 19 above rank 64 stages 64 k per stage; the stage counts not given are two.  0 keeps
  * eight stages.  "k split": two groups of eight waves compute the same tile,
  * each from one 32-wide half of every stage, and their sums are added before
  * the up-projection; its results differ from the other ids' in rounding,
  * which all agree bit for bit with each other.  "4 loaders": four of the
  * waves only issue the stage loads, the other eight only multiply.)
  */
-#define LORA_TILE_COUNT 19
+#define LORA_TILE_COUNT 20
 
 typedef struct lora_tile_info {
     int32_t tile;        /* id */

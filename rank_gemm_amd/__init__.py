@@ -47,7 +47,7 @@ VARIANTS = {"auto": 0, "tiled": 1, "decode": 2}
 MAX_RANK = 256
 DECODE_MAX_M = 64
 
-TILE_COUNT = 19
+TILE_COUNT = 20
 
 EXPORTS = ("lora_fwd", "lora_fwd_variant", "lora_merge", "lora_merge_batch",
            "lora_merge_inplace", "lora_status_str", "lora_abi_version", "lora_fwd_pick",

@@ -80,12 +80,18 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // PP = 1 runs the K loop as a ping-pong between two groups of four waves
 // (see the kernel): the first group multiplies while the second reads its
 // next fragments from LDS and issues stage loads, then the roles swap.
+//
+// TP = 1 (with a group of N tiles, TS = 1) computes the group's s T in a
+// prologue of its own before the first tile (t_prologue) and keeps it in LDS
+// past the ring; the stages then hold only X and W rows, and no tile of the
+// group runs the down-projection in its K loop.
 template <int BM_, int BN_, int WM_, int WN_, int RP_, int ST_, int BK_, int KS_ = 1, int PW_ = 0,
-          int TS_ = 0, int PP_ = 0, int LD_ = 0>
+          int TS_ = 0, int PP_ = 0, int LD_ = 0, int TP_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RP = RP_, STAGES = ST_, BK = BK_;
   static constexpr int KS = KS_, PW = PW_;
   static constexpr bool kPP = PP_ >= 1;
+  static constexpr bool kTP = TP_ == 1;
   static constexpr bool kPPSpread = PP_ == 2;  // X/W loads among the MFMAs of M
   static constexpr int kRowB = BK * 2;                // bytes per staged row
   static constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one 1-KiB wave load covers
@@ -97,7 +103,7 @@ struct Cfg {
   static constexpr int TM = BM / WM / 16;
   static constexpr int TN = BN / WN / 16;
   static constexpr int RB = RP / 16;
-  static constexpr int ROWS = BM + BN + RP;         // staged rows per stage
+  static constexpr int ROWS = BM + BN + (kTP ? 0 : RP);  // staged rows per stage
   static constexpr int kStageB = ROWS * kRowB;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static constexpr int kXL = BM / kRowsPerLoad / LW;  // X loads (1 KiB each) per loader per stage
@@ -131,8 +137,18 @@ struct Cfg {
   // and the output staging inside it.
   static constexpr int kTOffG = STAGES * kStageB;
   static constexpr int kLdsG = kTOffG + BM * kTRow * 2;
+  // The output staging of a group tile goes in two halves of BM / 2 rows
+  // (one wave row each) when the whole tile does not fit in the ring.
+  static constexpr bool kYSplit = kYB > kTOffG;
   // (only then can a workgroup take several N tiles: see the kernel)
-  static constexpr bool kGroupFits = BN * kTS * 2 <= kTOffG && kYB <= kTOffG;
+  static constexpr bool kGroupFits =
+      BN * kTS * 2 <= kTOffG && (kYB <= kTOffG || (WM == 2 && KS == 1 && kYB / 2 <= kTOffG));
+  // T prologue: its own ring in the stage ring's LDS, 64-deep stages of BM X
+  // rows then RP A rows, 8 rows per 1-KiB load, every wave an equal share.
+  static constexpr int kPRows = BM + RP;
+  static constexpr int kPStageB = kPRows * 128;
+  static constexpr int kPStages = kTP ? (STAGES * kStageB / kPStageB < 4 ? STAGES * kStageB / kPStageB : 4) : 2;
+  static constexpr int kPLoads = kPRows / 8 / (WM * WN);
   // B tile elements per thread, fetched into registers at kernel start when
   // few enough (the epilogue's gather would otherwise put a memory round trip
   // after the K loop).  Not for 256 x 256 tiles: their main loop already
@@ -177,6 +193,9 @@ struct Cfg {
                          (STAGES & (STAGES - 1)) == 0),
                 "ping-pong: two groups of four waves, one k32 step per stage, a power-of-two ring");
   static_assert(BK == 32 || BK == 64, "one or two k32 substeps per stage");
+  static_assert(!kTP || (kTSw && PW == 0 && KS == 1 && !kPP && BM == 256 && WM * WN == 8 &&
+                         RP % 32 == 0 && kPRows % 64 == 0 && kPStages >= 2),
+                "T prologue: 4 x 2 waves over T, equal load shares, two stages at least");
 };
 
 
@@ -300,6 +319,107 @@ __device__ __forceinline__ void issue_stage_a(unsigned char* smem, int buf, int 
     if (wave + s * C::LW < C::kAN)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (wave + s * C::LW) * 1024), 16,
                                                off_or_oob(kin, va + sgpr(s * sa + kb)), 0, 0, 0);
+}
+
+// The group's down-projection ahead of its first tile (TP = 1): s T =
+// s X_tile A^T, BM x RP, rounded once to bf16 into the LDS region `ts` past
+// the stage ring, where every N tile of the group reads it.  A ring of
+// kPStages 64-deep stages (BM X rows, then RP A rows) in the stage ring's
+// LDS; every wave issues kPLoads 1-KiB loads per stage and owns a
+// (BM / 4) x (RP / 2) block of T (4 x 2 waves).  The accumulation runs over
+// k32 steps in ascending k on the same MFMA as the fused K loop, so T is the
+// one that loop would produce.  Loads past K or past the last row read
+// zeros; all of them have landed and every wave is past its reads when this
+// returns.
+template <class C>
+__device__ __forceinline__ void t_prologue(unsigned char* smem, uint16_t* ts, int K, int r,
+                                           float scale, __amdgpu_buffer_rsrc_t rx,
+                                           __amdgpu_buffer_rsrc_t ra, int64_t ldx, int64_t lda,
+                                           int wave, int lane) {
+  constexpr int BM = C::BM, RP = C::RP, S = C::kPStages, NWP = C::WM * C::WN;
+  constexpr int kPL = C::kPLoads;
+  constexpr int kXQ = BM / 8;           // X loads per stage
+  constexpr int PTM = BM / 4 / 16;      // row blocks per wave
+  constexpr int PTN = RP / 2 / 16;      // rank blocks per wave
+  static_assert(kXQ % NWP == 0, "X loads: the same count for every wave");
+  const int lrow = lane & 15, lk = lane >> 4;
+  const int pm = wave >> 1, pn = wave & 1;
+  // Lane l of a load writes staged row 8 q + l / 8 at physical chunk l % 8,
+  // so it fetches logical chunk (l % 8) ^ (row & 7) (the 64-deep swizzle).
+  const int lr = lane >> 3;
+  const int lc = (lane & 7) ^ lr;
+  const uint32_t vx = (uint32_t)((wave * 8 + lr) * ldx * 2 + lc * 16);
+  const uint32_t va = (uint32_t)((wave * 8 + lr) * lda * 2 + lc * 16);  // A load s - kXQ / NWP
+  const uint32_t sx = (uint32_t)(NWP * 8 * ldx * 2);
+  const uint32_t sa = (uint32_t)(NWP * 8 * lda * 2);
+  auto issue = [&](int slot, int kt) {
+    const uint32_t kb = (uint32_t)kt * 128;
+    const bool kin = kt * 64 + lc * 8 < K;
+    unsigned char* base = smem + slot * C::kPStageB;
+#pragma unroll
+    for (int s = 0; s < kPL; ++s) {
+      const int q = wave + s * NWP;  // load index in the stage (wave-uniform)
+      if (s < kXQ / NWP)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(base + q * 1024), 16,
+                                                 off_or_oob(kin, vx + sgpr(s * sx + kb)), 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (lds_void*)(base + q * 1024), 16,
+            off_or_oob(kin, va + sgpr((s - kXQ / NWP) * sa + kb)), 0, 0, 0);
+    }
+  };
+  f32x4 tacc[PTM][PTN];
+#pragma unroll
+  for (int i = 0; i < PTM; ++i)
+#pragma unroll
+    for (int j = 0; j < PTN; ++j) tacc[i][j] = zero4();
+  const int nk = (K + 63) / 64;
+#pragma unroll
+  for (int st = 0; st < S; ++st) issue(st, st);
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt has landed once at most S - 1 newer stages are in flight.
+    wait_vmcnt<(S - 1) * kPL>();
+    __builtin_amdgcn_s_barrier();
+    const unsigned char* xs = smem + slot * C::kPStageB;
+    const unsigned char* as = xs + BM * 128;
+    u32x4 xa[2][PTM], ta[2][PTN];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < PTM; ++i)
+        xa[h][i] = *reinterpret_cast<const u32x4*>(
+            xs + stage_off<64>(pm * PTM * 16 + i * 16 + lrow, h * 4 + lk));
+#pragma unroll
+      for (int j = 0; j < PTN; ++j)
+        ta[h][j] = *reinterpret_cast<const u32x4*>(
+            as + stage_off<64>(pn * PTN * 16 + j * 16 + lrow, h * 4 + lk));
+    }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();  // every wave's reads of this slot are done
+    issue(slot, kt + S);
+    slot = slot + 1 == S ? 0 : slot + 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < PTM; ++i)
+#pragma unroll
+        for (int j = 0; j < PTN; ++j) tacc[i][j] = mfma16x16x32(xa[h][i], ta[h][j], tacc[i][j]);
+  }
+  wait_vmcnt<0>();
+  // Lane: T rows lk * 4 + q of its row block, rank column lrow of its block.
+#pragma unroll
+  for (int i = 0; i < PTM; ++i)
+#pragma unroll
+    for (int j = 0; j < PTN; ++j) {
+      const int col = pn * PTN * 16 + j * 16 + lrow;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = pm * PTM * 16 + i * 16 + lk * 4 + q;
+        ts[C::t_idx(row, col)] = col < r ? f2bf(scale * tacc[i][j][q]) : uint16_t(0);
+      }
+    }
+  __syncthreads();  // T complete; the ring is free for the first tile's stages
 }
 
 // G > 1: a workgroup computes G consecutive N tiles of one M tile.  The first
@@ -435,6 +555,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
             off_or_oob(j0 < r, (uint32_t)(row * ldb * 2 + j0 * 2)), 0, 0, 0);
       }
     }
+  }
+
+  if constexpr (C::kTP) {
+    static_assert(G > 1, "T prologue: a group of N tiles");
+    t_prologue<C>(smem, reinterpret_cast<uint16_t*>(smem + C::kTOffG), K, r, scale, rx, ra, ldx,
+                  lda, wave, lane);
   }
 
   for (int g = 0; g < G; ++g) {
@@ -714,8 +840,12 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
   }  // not ping-pong
   };  // kloop
-  if (g == 0) kloop(std::true_type{});
-  else kloop(std::false_type{});
+  if constexpr (C::kTP) {
+    kloop(std::false_type{});  // T from the prologue
+  } else {
+    if (g == 0) kloop(std::true_type{});
+    else kloop(std::false_type{});
+  }
   __syncthreads();
 
   // ---- k split: add the two groups' partial sums.  Group g keeps ring slots
@@ -775,13 +905,19 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   uint16_t* ts = reinterpret_cast<uint16_t*>(smem + (G > 1 ? C::kTOffG : 0));
   uint16_t* bs = G > 1 ? reinterpret_cast<uint16_t*>(smem) : ts + BM * C::kTRow;
   int bst = C::kTS;  // B tile row stride (elements)
+  // A group tile with the swizzled T keeps its B tile in the same layout
+  // (unpadded rows of RP, 16-B chunks XOR-swizzled by row), filled by direct
+  // 16-B loads where every chunk of a B row is aligned and wholly inside or
+  // wholly past the rank, else gathered element by element.
+  constexpr bool kBSw = G > 1 && C::kTSw;
+  auto bidx = [&](int n, int col) { return kBSw ? C::t_idx(n, col) : n * bst + col; };
   if constexpr (kBDma) {
     if (bdma) {
       bs = reinterpret_cast<uint16_t*>(smem + C::kBDmaOff);
       bst = RP;
     }
   }
-  if (g == 0 && kg == 0 && mul) {
+  if (!C::kTP && g == 0 && kg == 0 && mul) {
 #pragma unroll
   for (int sl = 0; sl < C::kTSlots; ++sl) {
     const int i = ring_row_block<C>(t_ring_slot<C>(sl), rot);
@@ -799,6 +935,31 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       for (int i = 0; i < C::kBPre; ++i) {
         const int e = tid + i * C::NWC * kWave;
         bs[(e / RP) * C::kTS + e % RP] = bpre[i];
+      }
+    }
+  } else if constexpr (kBSw) {
+    if (r % 8 == 0 && ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0) {
+      const int brows = max(0, min(BN, N - n0));
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(B + (int64_t)n0 * ldb), 0, (int)(brows * ldb * 2), 0x00020000);
+      constexpr int kBL = BN * RP * 2 / 1024;  // 1-KiB loads
+      static_assert(kBL % C::NW == 0, "B tile loads: the same count for every wave");
+      for (int p = wave; p < kBL; p += C::NW) {
+        // lane: row n, physical chunk pc; it fetches logical chunk pc ^ (n mod RP / 8)
+        const int byte = p * 1024 + lane * 16;
+        const int n = byte / (RP * 2), pc = (byte % (RP * 2)) / 16;
+        const int j0 = (pc ^ (n & (RP / 8 - 1))) * 8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (lds_void*)(smem + p * 1024), 16,
+            off_or_oob(j0 < r, (uint32_t)(n * ldb * 2 + j0 * 2)), 0, 0, 0);
+      }
+      wait_vmcnt<0>();
+    } else {
+      for (int e = tid; e < BN * RP; e += C::NT) {
+        const int n = e / RP, j = e % RP;
+        uint16_t v = 0;
+        if (j < r && n0 + n < N) v = B[(int64_t)(n0 + n) * ldb + j];
+        bs[C::t_idx(n, j)] = v;
       }
     }
   } else {
@@ -829,6 +990,24 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
 
   uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
+  constexpr bool kYHalves = G > 1 && C::kYSplit;
+  static_assert(!kYHalves || (C::WM == 2 && C::KS == 1), "output halves: one wave row each");
+  // Output rows [r0, r0 + nr) of the tile from staging row 0 on, 16 B per lane.
+  auto store_y = [&](int r0, int nr) {
+    constexpr int kCPR = BN / 8;  // 16-B chunks per output row
+    for (int e = tid; e < nr * kCPR; e += C::NT) {
+      const int row = e / kCPR, c = e % kCPR;
+      const int gm = m0 + r0 + row, gn = n0 + c * 8;
+      if (gm >= M || gn >= N) continue;
+      const uint16_t* src = ys + row * C::kYS + c * 8;
+      uint16_t* dst = Y + (int64_t)gm * ldy + gn;
+      if (y_vec && gn + 8 <= N) {
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        for (int q = 0; q < 8 && gn + q < N; ++q) dst[q] = src[q];
+      }
+    }
+  };
   if constexpr (C::KS == 1) {
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank.
   if (!mul) {
@@ -842,8 +1021,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
             ts + C::t_idx(wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow, kk * 32 + lk * 8));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * bst +
-                                               kk * 32 + lk * 8);
+        b[j] = *reinterpret_cast<const u32x4*>(
+            bs + bidx(wn * TN * 16 + j * 16 + lrow, kk * 32 + lk * 8));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -865,18 +1044,26 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
   __syncthreads();
 
-  // ---- epilogue 3: round once to bf16, stage, store coalesced.
-  if (mul) {
+  // ---- epilogue 3: round once to bf16, stage, store coalesced (a group
+  // tile too large for the ring: wave row 0's half first, then wave row 1's).
+  auto stage_y = [&](int rsub) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow;
-      *reinterpret_cast<u32x2*>(ys + row * C::kYS + wn * TN * 16 + j * 16 + lk * 4) =
-          u32x2{pack_bf2(acc[i][j][0], acc[i][j][1]), pack_bf2(acc[i][j][2], acc[i][j][3])};
-    }
-  }
+      for (int j = 0; j < TN; ++j) {
+        const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow - rsub;
+        *reinterpret_cast<u32x2*>(ys + row * C::kYS + wn * TN * 16 + j * 16 + lk * 4) =
+            u32x2{pack_bf2(acc[i][j][0], acc[i][j][1]), pack_bf2(acc[i][j][2], acc[i][j][3])};
+      }
+  };
+  if (mul && (!kYHalves || wm == 0)) stage_y(0);
   __syncthreads();
+  if constexpr (kYHalves) {
+    store_y(0, BM / 2);
+    __syncthreads();
+    if (mul && wm == 1) stage_y(BM / 2);
+    __syncthreads();
+  }
   } else {
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank, for
   // the ring slots [S0, S0 + TH) this wave keeps.
@@ -893,8 +1080,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
                             kk * 32 + lk * 8));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          b[j] = *reinterpret_cast<const u32x4*>(bs + (wn * TN * 16 + j * 16 + lrow) * bst +
-                                                 kk * 32 + lk * 8);
+          b[j] = *reinterpret_cast<const u32x4*>(
+              bs + bidx(wn * TN * 16 + j * 16 + lrow, kk * 32 + lk * 8));
 #pragma unroll
         for (int i = 0; i < TH; ++i)
 #pragma unroll
@@ -939,19 +1126,8 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
   __syncthreads();
   }
-  constexpr int kCPR = BN / 8;  // 16-B chunks per output row
-  for (int e = tid; e < BM * kCPR; e += C::NT) {
-    const int row = e / kCPR, c = e % kCPR;
-    const int gm = m0 + row, gn = n0 + c * 8;
-    if (gm >= M || gn >= N) continue;
-    const uint16_t* src = ys + row * C::kYS + c * 8;
-    uint16_t* dst = Y + (int64_t)gm * ldy + gn;
-    if (y_vec && gn + 8 <= N) {
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-    } else {
-      for (int q = 0; q < 8 && gn + q < N; ++q) dst[q] = src[q];
-    }
-  }
+  if constexpr (kYHalves) store_y(BM / 2, BM / 2);
+  else store_y(0, BM);
   if (G > 1) __syncthreads();  // the next tile's loads reuse the staging area
   }  // tiles of the group
 }
@@ -1055,6 +1231,13 @@ using BigNL = Cfg<256, 160, 4, 2, RP, 2, 64, 1, 4>;
 template <int RP>
 using WideT = Cfg<128, 256, 2, 4, RP, 2, 64, 1, 0, 1>;
 constexpr int kWideTGroup = 8;
+// 256 x 256 keeping T over 8 N tiles, T from a prologue (ranks 33-128): s T
+// (BM x RP bf16) stays in LDS past the ring, so rank 128 leaves 96 KiB for
+// three 32-deep stages and rank 64 128 KiB for two 64-deep ones; stage loads
+// from waves 0-3.
+template <int RP>
+using BigT = std::conditional_t<(RP <= 64), Cfg<256, 256, 2, 4, RP, 2, 64, 1, 0, 1, 0, 4, 1>,
+                                Cfg<256, 256, 2, 4, RP, 3, 32, 1, 0, 1, 0, 4, 1>>;
 // Small tiles with four loaders and four stages, for grids that the 128 x
 // 128 tile would leave under-filled: the smaller the tile, the more
 // workgroups share the streaming of W (tall-skinny and decode-like shapes).
@@ -1080,6 +1263,11 @@ using SmallL8 = Cfg<32, 32, 2, 1, RP, 8, 64, 1, 4>;
 
 // The built-in choice (lora_fwd's default), from the tile tuner's
 // measurements on the benchmark shapes and on rotating operand sets:
+//  * ranks 33-128: 256 x 256 keeping T over 8 N tiles (T from a prologue)
+//    when its grid has >= 256 workgroups and its rounds are at least 80 %
+//    filled with whole tiles (the 16384 x 8192 x 8192 square: r128 1.90 ms
+//    against 2.26 on 128 x 256 keeping T; r64 1.70 against 1.81 on 256 x 256
+//    recomputing T);
 //  * 256 x 256 (r <= 64; its stage loads from four of the eight waves when
 //    there is more than one round) when there are >= 256 such tiles and the
 //    last round of them is at least 80 % full
@@ -1104,6 +1292,13 @@ template <int RP>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t s) {
   auto grid = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   const int64_t mid_tiles = grid(128, 128);
+  if constexpr (RP == 64 || RP == 128) {
+    const int64_t tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
+    const int64_t wgs = tm * ((tn + kWideTGroup - 1) / kWideTGroup);
+    const int64_t rounds = (wgs + 255) / 256;
+    if (wgs >= 256 && tm * tn * 5 >= rounds * 256 * kWideTGroup * 4)
+      return launch<BigT<RP>, kWideTGroup>(a, s);
+  }
   if constexpr (RP <= 64) {
     const int64_t big_tiles = grid(256, 256);
     const int64_t rounds = (big_tiles + 255) / 256;
@@ -1251,6 +1446,12 @@ hipError_t tile_rp(int id, TileProps* props, const FwdArgs* a, hipStream_t s) {
       if constexpr (RP <= 64) {
         if (props) return tile_fill<BigL4<RP>, 1>(props), hipSuccess;
         return launch<BigL4<RP>>(*a, s);
+      }
+      break;
+    case kTileBigT:
+      if constexpr (RP >= 64 && RP <= 128) {
+        if (props) return tile_fill<BigT<RP>, kWideTGroup>(props), hipSuccess;
+        return launch<BigT<RP>, kWideTGroup>(*a, s);
       }
       break;
     case kTileSqL:

@@ -85,7 +85,7 @@ enum TileId { kTileTall = 0, kTileMid = 1, kTileMidG2 = 2, kTileMidG4 = 3, kTile
               kTileMid3L = 8, kTileWideL = 9,
               kTileSqL = 10, kTileTallL = 11, kTileSmallL = 12, kTileBigNL = 13,
               kTileWideT = 14, kTileBigPP = 15, kTileTallL8 = 16, kTileSmallL8 = 17,
-              kTileBigL4 = 18, kTileCount = 19 };
+              kTileBigL4 = 18, kTileBigT = 19, kTileCount = 20 };
 struct TileProps {
   int bm, bn, waves, stages, bk, group, rank_pad, lds_bytes, k_split;
   const void* kernel;

@@ -8,7 +8,7 @@ fastest is cached per shape in a JSON file.  A shape missing from the cache
 takes the choice of the nearest cached shape; with no usable entry the
 library's own choice (lora_fwd) is used.
 
-Candidates are the tiled configurations of lora_fwd_tile (ids 0-18 except
+Candidates are the tiled configurations of lora_fwd_tile (ids 0-19 except
 the retired id 5, each at the ranks it is instantiated for; see
 include/lora.h) and, for bf16 with M <= 64 and r <= 32, the weight-streaming
 decode kernel ("decode").  Pruning rules, in order:
@@ -177,10 +177,12 @@ def valid_for(choice: str, dtype: str, M: int, r: int) -> bool:
 
 def _tile_ranks(tid: int, r: int) -> bool:
     # Same table as include/lora.h (checked against lora_tile_get_info by the
-    # tests); id 5 is retired (never instantiated); id 14 starts at rank 64.
+    # tests); id 5 is retired (never instantiated); ids 14 and 19 start at
+    # rank 64.
     limit = {0: 32, 1: 256, 2: 128, 3: 128, 4: 64, 6: 128, 7: 64, 8: 128, 9: 32,
-             10: 64, 11: 64, 12: 64, 13: 32, 14: 128, 15: 64, 16: 64, 17: 64, 18: 64}.get(tid)
-    low = {14: 64}.get(tid, 16)
+             10: 64, 11: 64, 12: 64, 13: 32, 14: 128, 15: 64, 16: 64, 17: 64, 18: 64,
+             19: 128}.get(tid)
+    low = {14: 64, 19: 64}.get(tid, 16)
     return limit is not None and low <= pad_rank(r) <= limit
 
 

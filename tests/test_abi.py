@@ -33,7 +33,7 @@ def test_header_exports_match_library():
 
 
 def test_version_and_status_strings():
-    assert rg.abi_version() == 16
+    assert rg.abi_version() == 17
     for s in range(11):
         assert rg.status_str(s).startswith("LORA_")
     assert "unknown" in rg.status_str(99)
@@ -281,7 +281,9 @@ def test_bwd_workspace_size():
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(tile=19), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=20), rg.LORA_ERR_UNSUPPORTED),
+    (dict(tile=19, r=32, ldb=32), rg.LORA_ERR_UNSUPPORTED),   # T-prologue 256 x 256: 32 < r
+    (dict(tile=19, r=200, ldb=200), rg.LORA_ERR_UNSUPPORTED), # ... r <= 128
     (dict(tile=15, r=100, ldb=100), rg.LORA_ERR_UNSUPPORTED), # ping-pong 256 x 256: r <= 64
     (dict(tile=5), rg.LORA_ERR_UNSUPPORTED),                    # retired id
     (dict(tile=14, r=32, ldb=32), rg.LORA_ERR_UNSUPPORTED),   # T-keeping 128 x 256: 32 < r

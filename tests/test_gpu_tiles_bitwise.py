@@ -27,12 +27,16 @@ def _tiles():
     import rank_gemm_amd as rg
     out = []
     for tid in range(rg.TILE_COUNT):
-        for r in (5, 100, 200):
+        for r in (5, 40, 100, 200):
             info = rg.tile_info(tid, r)
             if info is None:
                 continue
-            # rank 200 only where the tile reaches it; 100 where 128 is the cap
+            # rank 200 only where the tile reaches it; 100 where 128 is the
+            # cap; 40 (padded to 64) only where it is the tile's lowest rank
+            # class (the T-keeping tiles, whose rank-64 form differs)
             if r == 200 and info.rank_pad != 256:
+                continue
+            if r == 40 and rg.tile_info(tid, 5) is not None:
                 continue
             out.append((tid, r, info.bm, info.bn, info.group))
     return out
