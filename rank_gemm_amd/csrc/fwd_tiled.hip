@@ -137,12 +137,13 @@ struct Cfg {
   // and the output staging inside it.
   static constexpr int kTOffG = STAGES * kStageB;
   static constexpr int kLdsG = kTOffG + BM * kTRow * 2;
-  // The output staging of a group tile goes in two halves of BM / 2 rows
-  // (one wave row each) when the whole tile does not fit in the ring.
+  // A group tile's output staging that does not fit in the ring also covers
+  // s T, which the threads then hold in registers meanwhile (see the kernel).
   static constexpr bool kYSplit = kYB > kTOffG;
   // (only then can a workgroup take several N tiles: see the kernel)
   static constexpr bool kGroupFits =
-      BN * kTS * 2 <= kTOffG && (kYB <= kTOffG || (WM == 2 && KS == 1 && kYB / 2 <= kTOffG));
+      BN * kTS * 2 <= kTOffG &&
+      (kYB <= kTOffG || (kYB <= kLdsG && (BM * kTRow * 2) % (16 * NT) == 0));
   // T prologue: its own ring in the stage ring's LDS, 64-deep stages of BM X
   // rows then RP A rows, 8 rows per 1-KiB load, every wave an equal share.
   static constexpr int kPRows = BM + RP;
@@ -990,24 +991,14 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
 
   uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
-  constexpr bool kYHalves = G > 1 && C::kYSplit;
-  static_assert(!kYHalves || (C::WM == 2 && C::KS == 1), "output halves: one wave row each");
-  // Output rows [r0, r0 + nr) of the tile from staging row 0 on, 16 B per lane.
-  auto store_y = [&](int r0, int nr) {
-    constexpr int kCPR = BN / 8;  // 16-B chunks per output row
-    for (int e = tid; e < nr * kCPR; e += C::NT) {
-      const int row = e / kCPR, c = e % kCPR;
-      const int gm = m0 + r0 + row, gn = n0 + c * 8;
-      if (gm >= M || gn >= N) continue;
-      const uint16_t* src = ys + row * C::kYS + c * 8;
-      uint16_t* dst = Y + (int64_t)gm * ldy + gn;
-      if (y_vec && gn + 8 <= N) {
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        for (int q = 0; q < 8 && gn + q < N; ++q) dst[q] = src[q];
-      }
-    }
-  };
+  // A group tile whose output staging does not fit in the ring stages it
+  // over s T as well: from the up-projection until the stores have read the
+  // staging area each thread holds 16-B chunks tid, tid + NT, ... of s T in
+  // registers (which the K loop's operands have left free), then writes
+  // them back for the next tile.
+  constexpr bool kTPark = G > 1 && C::kYSplit;
+  constexpr int kTParkN = kTPark ? BM * C::kTRow * 2 / 16 / C::NT : 1;
+  u32x4 tpark[kTParkN];
   if constexpr (C::KS == 1) {
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank.
   if (!mul) {
@@ -1042,28 +1033,25 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x16(b[j], a[i], acc[i][j]);
   }
+  if constexpr (kTPark) {
+#pragma unroll
+    for (int i = 0; i < kTParkN; ++i)
+      tpark[i] = reinterpret_cast<const u32x4*>(ts)[i * C::NT + tid];
+  }
   __syncthreads();
 
-  // ---- epilogue 3: round once to bf16, stage, store coalesced (a group
-  // tile too large for the ring: wave row 0's half first, then wave row 1's).
-  auto stage_y = [&](int rsub) {
+  // ---- epilogue 3: round once to bf16, stage, store coalesced.
+  if (mul) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow - rsub;
-        *reinterpret_cast<u32x2*>(ys + row * C::kYS + wn * TN * 16 + j * 16 + lk * 4) =
-            u32x2{pack_bf2(acc[i][j][0], acc[i][j][1]), pack_bf2(acc[i][j][2], acc[i][j][3])};
-      }
-  };
-  if (mul && (!kYHalves || wm == 0)) stage_y(0);
-  __syncthreads();
-  if constexpr (kYHalves) {
-    store_y(0, BM / 2);
-    __syncthreads();
-    if (mul && wm == 1) stage_y(BM / 2);
-    __syncthreads();
+    for (int j = 0; j < TN; ++j) {
+      const int row = wm * TM * 16 + ring_row_block<C>(i, rot) * 16 + lrow;
+      *reinterpret_cast<u32x2*>(ys + row * C::kYS + wn * TN * 16 + j * 16 + lk * 4) =
+          u32x2{pack_bf2(acc[i][j][0], acc[i][j][1]), pack_bf2(acc[i][j][2], acc[i][j][3])};
+    }
   }
+  __syncthreads();
   } else {
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank, for
   // the ring slots [S0, S0 + TH) this wave keeps.
@@ -1126,9 +1114,24 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   }
   __syncthreads();
   }
-  if constexpr (kYHalves) store_y(BM / 2, BM / 2);
-  else store_y(0, BM);
+  constexpr int kCPR = BN / 8;  // 16-B chunks per output row
+  for (int e = tid; e < BM * kCPR; e += C::NT) {
+    const int row = e / kCPR, c = e % kCPR;
+    const int gm = m0 + row, gn = n0 + c * 8;
+    if (gm >= M || gn >= N) continue;
+    const uint16_t* src = ys + row * C::kYS + c * 8;
+    uint16_t* dst = Y + (int64_t)gm * ldy + gn;
+    if (y_vec && gn + 8 <= N) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int q = 0; q < 8 && gn + q < N; ++q) dst[q] = src[q];
+    }
+  }
   if (G > 1) __syncthreads();  // the next tile's loads reuse the staging area
+  if constexpr (kTPark) {
+#pragma unroll
+    for (int i = 0; i < kTParkN; ++i) reinterpret_cast<u32x4*>(ts)[i * C::NT + tid] = tpark[i];
+  }
   }  // tiles of the group
 }
 
