@@ -32,26 +32,24 @@ namespace {
 constexpr uint32_t kDecOob = 0x80000000u;  // offset past any resource's range
 
 
-// AL: A (and, with XL, the single X row) reach the waves through LDS: each
+// AL: A reaches the waves through LDS: each
 // wave stages the rows of its own K range with 16-B-per-lane DMA loads
 // (buffer_load ... lds), whole 128-B lines per instruction, instead of
 // 16-row x 64-B register loads; the MFMA fragments are then read from LDS.
-template <int MB, int RB, int U, int NW, bool AL, bool XL, bool TP = false>
+template <int MB, int RB, int U, int NW, bool AL, bool TP = false>
 struct Dec {
   static constexpr int RP = RB * 16;
   static constexpr int kRowB = U * 256;                   // bytes of a staged row per round
   static constexpr int kChunks = U * 16;                  // 16-B chunks per staged row
   static constexpr int kAB = AL && !TP ? NW * RP * kRowB : 0;  // per-wave A regions
-  static constexpr int kXB = XL ? NW * kRowB : 0;         // per-wave X row
   static constexpr int kSlots = MB * (1 + RB);            // f32x4 partials per lane
   static constexpr int kRedB = NW * kSlots * kWave * 16;  // LDS for the reduction
   static constexpr int kTS = RP + 1;                      // T row stride (floats)
   static constexpr int kTB = MB * 16 * kTS * 4;           // T rows for the epilogue
-  static constexpr int kRedOff = kAB + kXB;
+  static constexpr int kRedOff = kAB;
   static constexpr int kLds = kRedOff + kRedB + kTB;
   static_assert(kLds <= 160 * 1024, "LDS budget");
   static_assert(!AL || (MB == 1 && (kRowB == 512 || kRowB == 1024)), "LDS staging shape");
-  static_assert(!XL || (AL && kRowB == 1024), "X staging: one full 1-KiB DMA per round");
 };
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -61,14 +59,14 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // One workgroup's work: output columns [n0, n0 + 16) of one forward.
 // TP: T = X A^T was computed beforehand (tp: the NW per-wave partial sums,
 // as dec_t_kernel writes them); A is neither loaded nor multiplied here.
-template <int MB, int RB, int U, int NW, bool AL, bool XL, bool TP = false>
+template <int MB, int RB, int U, int NW, bool AL, bool TP = false>
 __device__ __forceinline__ void dec_body(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
     int64_t ldy, int b_vec, int n0, unsigned char* smem, const f32x4* __restrict__ tp = nullptr) {
   static_assert(!TP || MB == 1, "precomputed T: one 16-row block of tokens");
-  using C = Dec<MB, RB, U, NW, AL, XL, TP>;
+  using C = Dec<MB, RB, U, NW, AL, TP>;
   constexpr int RP = C::RP;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -120,7 +118,6 @@ __device__ __forceinline__ void dec_body(
   // [128 kbw, 128 (kbw + U)) with kbw = (round NW + w) U.
   const int nkb = (K + 127) >> 7;
   unsigned char* as = smem + wave * (RP * C::kRowB);            // AL: this wave's A rows
-  unsigned char* xs = smem + C::kAB + wave * C::kRowB;          // XL: this wave's X row
   for (int kbw = wave * U; kbw < nkb; kbw += NW * U) {
     // Byte offset of each (block, substep) chunk within a row, or past the
     // range when the 8-element chunk lies beyond K.
@@ -150,22 +147,13 @@ __device__ __forceinline__ void dec_body(
         const uint32_t vo = k < K ? (uint32_t)j * (uint32_t)lda * 2 + (uint32_t)k * 2 : kDecOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(as + d * 1024), 16, vo, 0, 0, 0);
       }
-      if constexpr (XL) {
-        // The X row (M == 1): one 1-KiB DMA, lane i chunk i, unswizzled (all
-        // sixteen row lanes read the same chunk: a broadcast).
-        const int k = kbw * 128 + lane * 8;
-        const uint32_t vo = k < K ? (uint32_t)k * 2 : kDecOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)xs, 16, vo, 0, 0, 0);
-      }
       // Nothing below may be scheduled before the DMAs: the wait further
       // down counts on them being the oldest loads of the round.
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!XL) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) x[u][0][q] = bload(rx, xbase[0] + off[u][q]);
-      }
+        for (int q = 0; q < 4; ++q) x[u][0][q] = bload(rx, xbase[0] + off[u][q]);
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -188,8 +176,8 @@ __device__ __forceinline__ void dec_body(
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (AL) {
       // The DMAs were issued first: waiting until only the later register
-      // loads (W, and X unless staged) are outstanding completes them.
-      wait_vmcnt<U * 4 * (XL ? 1 : 2)>();
+      // loads (X and W) are outstanding completes them.
+      wait_vmcnt<U * 4 * 2>();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -201,7 +189,6 @@ __device__ __forceinline__ void dec_body(
             const int j = jb * 16 + lrow;
             a[u][jb][q] = *reinterpret_cast<const u32x4*>(as + j * C::kRowB + ((c ^ lrow) << 4));
           }
-          if constexpr (XL) x[u][0][q] = *reinterpret_cast<const u32x4*>(xs + (c << 4));
         }
     }
     if constexpr (!TP) {
@@ -294,14 +281,14 @@ __device__ __forceinline__ void dec_body(
   }
 }
 
-template <int MB, int RB, int U, int NW, bool AL, bool XL>
+template <int MB, int RB, int U, int NW, bool AL>
 __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
     int M, int N, int K, int r, const uint16_t* __restrict__ X, int64_t ldx,
     const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ B, int64_t ldb, float scale, uint16_t* __restrict__ Y,
     int64_t ldy, int b_vec) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  dec_body<MB, RB, U, NW, AL, XL>(M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, scale, Y, ldy, b_vec,
+  dec_body<MB, RB, U, NW, AL>(M, N, K, r, X, ldx, W, ldw, A, lda, B, ldb, scale, Y, ldy, b_vec,
                                   blockIdx.x * 16, smem);
 }
 
@@ -318,19 +305,36 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_kernel(
 // Each lane accumulates its 8-element pieces of rows (8 h + l / 8) of Ybase
 // and of T; the 8 lanes of a row are added by a fixed butterfly, the waves
 // in wave order through LDS, and the epilogue is the decode kernel's.
-template <int RB, int R>
-__global__ __launch_bounds__(512) void fwd_decode_row_kernel(
-    int N, int K, int r, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-    int64_t ldw, const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
-    int64_t ldb, float scale, uint16_t* __restrict__ Y, int b_vec) {
+//
+// acc + the 8 products of p and q, in element-pair order.  (The pairs are
+// taken as swizzles of the 8-wide vector: a dynamically indexed dword
+// bit-cast to a pair miscompiled here to the first dword every time.)
+__device__ __forceinline__ float dot8(const u32x4& p, const u32x4& q, float acc) {
+  const bf16x8 pv = __builtin_bit_cast(bf16x8, p), qv = __builtin_bit_cast(bf16x8, q);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s01, qv.s01, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s23, qv.s23, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s45, qv.s45, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s67, qv.s67, acc, false);
+  return acc;
+}
+
+// The 16 rows [n0, n0 + 16) of one forward.  TP: the T partial sums of the
+// NW waves come from `tp` (RP floats per wave, as dec_row_t_kernel writes
+// them) and A is neither loaded nor multiplied.
+template <int RB, int R, bool TP>
+__device__ __forceinline__ void dec_row_body(int N, int K, int r, const uint16_t* __restrict__ X,
+                                             const uint16_t* __restrict__ W, int64_t ldw,
+                                             const uint16_t* __restrict__ A, int64_t lda,
+                                             const uint16_t* __restrict__ B, int64_t ldb,
+                                             float scale, uint16_t* __restrict__ Y, int b_vec,
+                                             int n0, const float* __restrict__ tp) {
   constexpr int NW = 8, RP = RB * 16;
   static_assert(R <= 8 && 2 * RB * R + 2 * R < 64, "one 1-KiB X piece per wave and round");
-  __shared__ float red[NW][16 + RP];
+  __shared__ float red[NW][16 + (TP ? 0 : RP)];
   __shared__ __attribute__((aligned(16))) unsigned char xsh[NW][1024];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 3, c = lane & 7;
-  const int n0 = blockIdx.x * 16;
   const int wrows = min(16, N - n0);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(W + (int64_t)n0 * ldw), 0, (int)(wrows * ldw * 2), 0x00020000);
@@ -356,17 +360,6 @@ __global__ __launch_bounds__(512) void fwd_decode_row_kernel(
   float tacc[2 * RB];
 #pragma unroll
   for (int q = 0; q < 2 * RB; ++q) tacc[q] = 0.f;
-  // acc + sum of the 8 products, in element-pair order.  (The pairs are
-  // taken as swizzles of the 8-wide vector: a dynamically indexed dword
-  // bit-cast to a pair miscompiled here to the first dword every time.)
-  auto dot8 = [](const u32x4& p, const u32x4& q, float acc) {
-    const bf16x8 pv = __builtin_bit_cast(bf16x8, p), qv = __builtin_bit_cast(bf16x8, q);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s01, qv.s01, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s23, qv.s23, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s45, qv.s45, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(pv.s67, qv.s67, acc, false);
-    return acc;
-  };
   // Wave w takes R consecutive 64-deep segments per round.
   const int nseg = (K + 63) >> 6;
   for (int s0 = wave * R; s0 < nseg; s0 += NW * R) {
@@ -397,7 +390,10 @@ __global__ __launch_bounds__(512) void fwd_decode_row_kernel(
 #pragma unroll
       for (int q = 0; q < 2 * RB; ++q) a[u][q] = bload(ra, k < K ? arow[q] + ko : kDecOob);
     };
-    if constexpr (RB == 1) {
+    if constexpr (TP) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) wload(u);
+    } else if constexpr (RB == 1) {
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         wload(u);
@@ -412,14 +408,16 @@ __global__ __launch_bounds__(512) void fwd_decode_row_kernel(
     // Every load of the round in flight before the first product; then the
     // X piece (all later loads may still be in flight) from LDS.
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<2 * RB * R + 2 * R>();
+    wait_vmcnt<(TP ? 0 : 2 * RB * R) + 2 * R>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < R; ++u) x[u] = *reinterpret_cast<const u32x4*>(&xsh[wave][u * 128 + c * 16]);
 #pragma unroll
     for (int u = 0; u < R; ++u) {
+      if constexpr (!TP) {
 #pragma unroll
-      for (int q = 0; q < 2 * RB; ++q) tacc[q] = dot8(a[u][q], x[u], tacc[q]);
+        for (int q = 0; q < 2 * RB; ++q) tacc[q] = dot8(a[u][q], x[u], tacc[q]);
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) yacc[h] = dot8(w[u][h], x[u], yacc[h]);
     }
@@ -430,14 +428,18 @@ __global__ __launch_bounds__(512) void fwd_decode_row_kernel(
   for (int m = 1; m < 8; m <<= 1) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) yacc[h] += __shfl_xor(yacc[h], m);
+    if constexpr (!TP) {
 #pragma unroll
-    for (int q = 0; q < 2 * RB; ++q) tacc[q] += __shfl_xor(tacc[q], m);
+      for (int q = 0; q < 2 * RB; ++q) tacc[q] += __shfl_xor(tacc[q], m);
+    }
   }
   if (c == 0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) red[wave][8 * h + g] = yacc[h];
+    if constexpr (!TP) {
 #pragma unroll
-    for (int q = 0; q < 2 * RB; ++q) red[wave][16 + 8 * q + g] = tacc[q];
+      for (int q = 0; q < 2 * RB; ++q) red[wave][16 + 8 * q + g] = tacc[q];
+    }
   }
   __syncthreads();
   if (wave != 0 || lane >= 16) return;
@@ -450,7 +452,10 @@ __global__ __launch_bounds__(512) void fwd_decode_row_kernel(
   // past r read as zeros) and B is zeroed past r.
   auto tcol = [&](int j) {
     float tj = 0.f;
-    for (int v = 0; v < NW; ++v) tj += red[v][16 + j];
+    for (int v = 0; v < NW; ++v) {
+      if constexpr (TP) tj += tp[v * RP + j];
+      else tj += red[v][16 + j];
+    }
     return tj;
   };
   float l = 0.f;
@@ -468,6 +473,15 @@ __global__ __launch_bounds__(512) void fwd_decode_row_kernel(
     for (int j = 0; j < RP; ++j) l += tcol(j) * (j < r ? bf2f(bh[j]) : 0.f);
   }
   Y[n] = f2bf(y + scale * l);
+}
+
+template <int RB, int R>
+__global__ __launch_bounds__(512) void fwd_decode_row_kernel(
+    int N, int K, int r, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    int64_t ldw, const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+    int64_t ldb, float scale, uint16_t* __restrict__ Y, int b_vec) {
+  dec_row_body<RB, R, false>(N, K, r, X, W, ldw, A, lda, B, ldb, scale, Y, b_vec,
+                             blockIdx.x * 16, nullptr);
 }
 
 // Batched decode: up to kDecBatch forwards with the same M and rank class per
@@ -541,7 +555,7 @@ __global__ __launch_bounds__(64) void dec_t_kernel(const DecBatch args) {
   for (int jb = 0; jb < RB; ++jb) d.tp[(w * RB + jb) * kWave + lane] = tacc[jb];
 }
 
-template <int MB, int RB, int U, int NW, bool AL, bool XL, bool TP>
+template <int MB, int RB, int U, int NW, bool AL, bool TP>
 __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_batch_kernel(const DecBatch args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int b = blockIdx.x;
@@ -551,7 +565,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_decode_bf16_batch_kernel(const De
     if (args.first[mid] <= b) lo = mid; else hi = mid - 1;
   }
   const DecDesc& d = args.d[lo];
-  dec_body<MB, RB, U, NW, AL, XL, TP>(args.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda,
+  dec_body<MB, RB, U, NW, AL, TP>(args.M, d.N, d.K, d.r, d.X, d.ldx, d.W, d.ldw, d.A, d.lda,
                                       d.B, d.ldb, d.scale, d.Y, d.ldy, d.b_vec,
                                       (b - args.first[lo]) * 16, smem, d.tp);
 }
@@ -562,13 +576,10 @@ inline int dec_b_vec(const FwdArgs& a) {
   return ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0) && (a.ldb % 8 == 0) && (a.r % 8 == 0);
 }
 
-// The forwards a[i0, i1) (same M, same rank class) in one launch; with a
-// workspace (tws: kDecTpBytes per forward) T first, in a launch of its own.
-template <int MB, int RB, int U, bool AL, bool XL>
-hipError_t launch_dec_batch(const FwdArgs* a, int i0, int i1, unsigned char* tws, hipStream_t s) {
-  constexpr int NW = 8;
-  using C = Dec<MB, RB, U, NW, AL, XL>;
-  DecBatch bt{};
+// The descriptors of forwards a[i0, i1) (one workgroup per 16 rows of W);
+// tws (may be null): kDecTpBytes of T partial sums per forward.  Returns
+// the workgroup count.
+inline int dec_batch_fill(DecBatch& bt, const FwdArgs* a, int i0, int i1, unsigned char* tws) {
   bt.count = i1 - i0;
   bt.M = (int)a[i0].M;
   int blocks = 0;
@@ -583,6 +594,94 @@ hipError_t launch_dec_batch(const FwdArgs* a, int i0, int i1, unsigned char* tws
     blocks += (int)((f.N + 15) / 16);
   }
   bt.first[bt.count] = blocks;
+  return blocks;
+}
+
+// One-token forwards of a batch: dec_row_body per forward, so each output
+// is bitwise the one lora_fwd gives for it.  TP: T from the workspace.
+template <int RB, int R, bool TP>
+__global__ __launch_bounds__(512) void fwd_decode_row_batch_kernel(const DecBatch args) {
+  const int b = blockIdx.x;
+  int lo = 0, hi = args.count - 1;  // last t with first[t] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (args.first[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  const DecDesc& d = args.d[lo];
+  dec_row_body<RB, R, TP>(d.N, d.K, d.r, d.X, d.W, d.ldw, d.A, d.lda, d.B, d.ldb, d.scale, d.Y,
+                          d.b_vec, (b - args.first[lo]) * 16, reinterpret_cast<const float*>(d.tp));
+}
+
+// T of every one-token forward of a batch, wave partition by wave
+// partition: workgroup (t, w) is one wave doing for forward t exactly what
+// wave w of dec_row_body does for T -- the same segments, X piece, A loads,
+// dot8 chains and butterfly -- and it stores the RP partial sums
+// (tp[w * RP + j]).  The batch kernel adds them in wave order, as
+// dec_row_body's LDS reduction does, so T and Y are bitwise those of the
+// single forward; A is read once per forward, by 8 workgroups at once.
+template <int RB, int R>
+__global__ __launch_bounds__(64) void dec_row_t_kernel(const DecBatch args) {
+  constexpr int NW = 8, RP = RB * 16;
+  __shared__ __attribute__((aligned(16))) unsigned char xsh[1024];
+  const int t = blockIdx.x / NW, wave = blockIdx.x % NW;
+  const DecDesc& d = args.d[t];
+  const int lane = threadIdx.x, g = lane >> 3, c = lane & 7;
+  const int K = d.K, r = d.r;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)d.X, 0, K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)d.A, 0, (int)(r * d.lda * 2), 0x00020000);
+  uint32_t arow[2 * RB];
+#pragma unroll
+  for (int q = 0; q < 2 * RB; ++q) arow[q] = (uint32_t)(8 * q + g) * (uint32_t)d.lda * 2;
+  float tacc[2 * RB];
+#pragma unroll
+  for (int q = 0; q < 2 * RB; ++q) tacc[q] = 0.f;
+  const int nseg = (K + 63) >> 6;
+  for (int s0 = wave * R; s0 < nseg; s0 += NW * R) {
+    u32x4 x[R], a[R][2 * RB];
+    {
+      const int k = (s0 + (lane >> 3)) * 64 + c * 8;
+      const uint32_t ko = (lane >> 3) < R && k < K ? (uint32_t)k * 2 : kDecOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)xsh, 16, ko, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the DMA stays the oldest load
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int k = (s0 + u) * 64 + c * 8;
+      const uint32_t ko = k < K ? (uint32_t)k * 2 : kDecOob;
+#pragma unroll
+      for (int q = 0; q < 2 * RB; ++q) a[u][q] = bload(ra, k < K ? arow[q] + ko : kDecOob);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 * RB * R>();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < R; ++u) x[u] = *reinterpret_cast<const u32x4*>(&xsh[u * 128 + c * 16]);
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+#pragma unroll
+      for (int q = 0; q < 2 * RB; ++q) tacc[q] = dot8(a[u][q], x[u], tacc[q]);
+  }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+    for (int q = 0; q < 2 * RB; ++q) tacc[q] += __shfl_xor(tacc[q], m);
+  float* tp = reinterpret_cast<float*>(d.tp);
+  if (c == 0) {
+#pragma unroll
+    for (int q = 0; q < 2 * RB; ++q) tp[wave * RP + 8 * q + g] = tacc[q];
+  }
+}
+
+// The forwards a[i0, i1) (same M, same rank class) in one launch; with a
+// workspace (tws: kDecTpBytes per forward) T first, in a launch of its own.
+template <int MB, int RB, int U, bool AL>
+hipError_t launch_dec_batch(const FwdArgs* a, int i0, int i1, unsigned char* tws, hipStream_t s) {
+  constexpr int NW = 8;
+  using C = Dec<MB, RB, U, NW, AL>;
+  DecBatch bt{};
+  const int blocks = dec_batch_fill(bt, a, i0, i1, tws);
   if constexpr (MB == 1) {
     if (tws != nullptr) {
       // Without A the W stream has the registers of rank 16 at any rank:
@@ -590,29 +689,29 @@ hipError_t launch_dec_batch(const FwdArgs* a, int i0, int i1, unsigned char* tws
       // (With rank 16 this is the single-forward kernel's own partition, so
       // the outputs stay bitwise; above it Y differs from it by rounding.)
       constexpr int UT = 4;
-      using CT = Dec<1, RB, UT, NW, true, XL, true>;
+      using CT = Dec<1, RB, UT, NW, true, true>;
       static_assert(NW * RB * kWave * 16 <= kDecTpBytes, "T partials fit the workspace slot");
       hipLaunchKernelGGL((dec_t_kernel<RB, UT>), dim3(bt.count * NW), dim3(64), 0, s, bt);
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-      auto kern = fwd_decode_bf16_batch_kernel<1, RB, UT, NW, true, XL, true>;
+      auto kern = fwd_decode_bf16_batch_kernel<1, RB, UT, NW, true, true>;
       static std::atomic<uint64_t> attr_done{0};
       if (hipError_t e = ensure_lds(kern, CT::kLds, attr_done); e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), CT::kLds, s, bt);
       return hipGetLastError();
     }
   }
-  auto kern = fwd_decode_bf16_batch_kernel<MB, RB, U, NW, AL, XL, false>;
+  auto kern = fwd_decode_bf16_batch_kernel<MB, RB, U, NW, AL, false>;
   static std::atomic<uint64_t> attr_done{0};
   if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), C::kLds, s, bt);
   return hipGetLastError();
 }
 
-template <int MB, int RB, int U, bool AL = false, bool XL = false>
+template <int MB, int RB, int U, bool AL = false>
 hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = 8;
-  using C = Dec<MB, RB, U, NW, AL, XL>;
-  auto kern = fwd_decode_bf16_kernel<MB, RB, U, NW, AL, XL>;
+  using C = Dec<MB, RB, U, NW, AL>;
+  auto kern = fwd_decode_bf16_kernel<MB, RB, U, NW, AL>;
   static std::atomic<uint64_t> attr_done{0};
   if (hipError_t e = ensure_lds(kern, C::kLds, attr_done); e != hipSuccess) return e;
   const int blocks = (int)((a.N + 15) / 16);
@@ -632,18 +731,15 @@ hipError_t launch_dec(const FwdArgs& a, hipStream_t s) {
 template <int RB>
 hipError_t launch_dec_rb(const FwdArgs& a, const FwdArgs* batch, int i0, int i1,
                          unsigned char* tws, hipStream_t s) {
-#define LORA_DEC(MB, U, AL, XL)                                                    \
-  return batch ? launch_dec_batch<MB, RB, U, AL, XL>(batch, i0, i1, tws, s)        \
-               : launch_dec<MB, RB, U, AL, XL>(a, s)
+#define LORA_DEC(MB, U, AL)                                                        \
+  return batch ? launch_dec_batch<MB, RB, U, AL>(batch, i0, i1, tws, s)            \
+               : launch_dec<MB, RB, U, AL>(a, s)
   switch ((a.M + 15) / 16) {
     case 1:
-      if constexpr (RB == 1) {
-        if (a.M == 1) LORA_DEC(1, 4, true, true);
-      }
-      LORA_DEC(1, (RB == 1 ? 4 : 2), true, false);
-    case 2: LORA_DEC(2, 2, false, false);
-    case 3: LORA_DEC(3, (RB == 1 ? 2 : 1), false, false);
-    default: LORA_DEC(4, (RB == 1 ? 2 : 1), false, false);
+      LORA_DEC(1, (RB == 1 ? 4 : 2), true);
+    case 2: LORA_DEC(2, 2, false);
+    case 3: LORA_DEC(3, (RB == 1 ? 2 : 1), false);
+    default: LORA_DEC(4, (RB == 1 ? 2 : 1), false);
   }
 #undef LORA_DEC
 }
@@ -659,6 +755,26 @@ hipError_t launch_dec_row(const FwdArgs& a, hipStream_t s) {
                      static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.A),
                      a.lda, static_cast<const uint16_t*>(a.B), a.ldb, a.scale,
                      static_cast<uint16_t*>(a.Y), dec_b_vec(a));
+  return hipGetLastError();
+}
+
+// One-token forwards a[i0, i1) (same rank class) in one launch; with a
+// workspace (tws: kDecTpBytes per forward) T first, in a launch of its own.
+template <int RB, int R>
+hipError_t launch_dec_row_batch(const FwdArgs* a, int i0, int i1, unsigned char* tws,
+                                hipStream_t s) {
+  static_assert(8 * RB * 16 * 4 <= kDecTpBytes, "T partial sums fit the workspace slot");
+  DecBatch bt{};
+  const int blocks = dec_batch_fill(bt, a, i0, i1, tws);
+  if (tws != nullptr) {
+    hipLaunchKernelGGL((dec_row_t_kernel<RB, R>), dim3(bt.count * 8), dim3(64), 0, s, bt);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_decode_row_batch_kernel<RB, R, true>), dim3(blocks), dim3(512), 0, s,
+                       bt);
+  } else {
+    hipLaunchKernelGGL((fwd_decode_row_batch_kernel<RB, R, false>), dim3(blocks), dim3(512), 0,
+                       s, bt);
+  }
   return hipGetLastError();
 }
 
@@ -698,8 +814,13 @@ hipError_t launch_fwd_decode_bf16_batch(const FwdArgs* a, int count, void* tws, 
   for (int i = 0; i < count; i += kDecBatch) {
     const int j = i + kDecBatch < count ? i + kDecBatch : count;
     unsigned char* wi = w ? w + (size_t)i * kDecTpBytes : nullptr;
-    const hipError_t e = a[i].r <= 16 ? launch_dec_rb<1>(a[i], a, i, j, wi, s)
-                                      : launch_dec_rb<2>(a[i], a, i, j, wi, s);
+    hipError_t e;
+    if (a[i].M == 1)  // the one-token kernel of lora_fwd, per forward
+      e = a[i].r <= 16 ? launch_dec_row_batch<1, 8>(a, i, j, wi, s)
+                       : launch_dec_row_batch<2, 4>(a, i, j, wi, s);
+    else
+      e = a[i].r <= 16 ? launch_dec_rb<1>(a[i], a, i, j, wi, s)
+                       : launch_dec_rb<2>(a[i], a, i, j, wi, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
