@@ -141,9 +141,7 @@ struct Cfg {
   // s T, which the threads then hold in registers meanwhile (see the kernel).
   static constexpr bool kYSplit = kYB > kTOffG;
   // (only then can a workgroup take several N tiles: see the kernel)
-  static constexpr bool kGroupFits =
-      BN * kTS * 2 <= kTOffG &&
-      (kYB <= kTOffG || (kYB <= kLdsG && (BM * kTRow * 2) % (16 * NT) == 0));
+  static constexpr bool kGroupFits = BN * kTS * 2 <= kTOffG && kYB <= kLdsG;
   // T prologue: its own ring in the stage ring's LDS, 64-deep stages of BM X
   // rows then RP A rows, 8 rows per 1-KiB load, every wave an equal share.
   static constexpr int kPRows = BM + RP;
@@ -992,12 +990,13 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
 
   uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
   // A group tile whose output staging does not fit in the ring stages it
-  // over s T as well: from the up-projection until the stores have read the
-  // staging area each thread holds 16-B chunks tid, tid + NT, ... of s T in
-  // registers (which the K loop's operands have left free), then writes
-  // them back for the next tile.
+  // over the start of s T as well: from the up-projection until the stores
+  // have read the staging area each thread holds 16-B chunks tid, tid + NT,
+  // ... of the covered part of s T in registers (which the K loop's
+  // operands have left free), then writes them back for the next tile.
   constexpr bool kTPark = G > 1 && C::kYSplit;
-  constexpr int kTParkN = kTPark ? BM * C::kTRow * 2 / 16 / C::NT : 1;
+  constexpr int kTParkN = kTPark ? (C::kYB - C::kTOffG + 16 * C::NT - 1) / (16 * C::NT) : 1;
+  static_assert(!kTPark || kTParkN * 16 * C::NT <= BM * C::kTRow * 2, "parked chunks lie in s T");
   u32x4 tpark[kTParkN];
   if constexpr (C::KS == 1) {
   // ---- epilogue 2: acc += (s T) B^T on MFMA, contraction over the rank.
