@@ -442,37 +442,42 @@ __device__ __forceinline__ void dec_row_body(int N, int K, int r, const uint16_t
     }
   }
   __syncthreads();
-  if (wave != 0 || lane >= 16) return;
+  if (wave != 0) return;
+  // Wave 0, lane l < 16 + RP: partial l summed over the waves in wave order
+  // (l < 16: Ybase of row n0 + l; else T[l - 16]), each sum once; the row
+  // lanes then take T by shuffles and add the rank sum in j order.  T's
+  // columns past r are zero (A rows past r read as zeros) and B is zeroed
+  // past r, so the rank loop needs no branch.
+  float sl = 0.f;
+  if (lane < 16) {
+    for (int v = 0; v < NW; ++v) sl += red[v][lane];
+  } else if (lane < 16 + RP) {
+    for (int v = 0; v < NW; ++v) {
+      if constexpr (TP) sl += tp[v * RP + lane - 16];
+      else sl += red[v][lane];
+    }
+  }
+  float tv[RP];
+#pragma unroll
+  for (int j = 0; j < RP; ++j) tv[j] = __shfl(sl, 16 + j);
+  if (lane >= 16) return;
   const int n = n0 + lane;
   if (n >= N) return;
-  float y = 0.f;
-  for (int v = 0; v < NW; ++v) y += red[v][lane];
-  // T[j] summed over the waves in wave order, then the rank sum in j order;
-  // branch-free as in the decode kernel: T's columns past r are zero (A rows
-  // past r read as zeros) and B is zeroed past r.
-  auto tcol = [&](int j) {
-    float tj = 0.f;
-    for (int v = 0; v < NW; ++v) {
-      if constexpr (TP) tj += tp[v * RP + j];
-      else tj += red[v][16 + j];
-    }
-    return tj;
-  };
   float l = 0.f;
   if (b_vec) {
 #pragma unroll
     for (int j = 0; j < RP; ++j) {
       const uint32_t hw = (bv[j >> 3][(j >> 1) & 3] >> ((j & 1) * 16)) & 0xFFFFu;
-      l += tcol(j) * (j < r ? bf2f((uint16_t)hw) : 0.f);
+      l += tv[j] * (j < r ? bf2f((uint16_t)hw) : 0.f);
     }
   } else {
     uint16_t bh[RP];
 #pragma unroll
     for (int j = 0; j < RP; ++j) bh[j] = B[brow * ldb + min(j, r - 1)];
 #pragma unroll
-    for (int j = 0; j < RP; ++j) l += tcol(j) * (j < r ? bf2f(bh[j]) : 0.f);
+    for (int j = 0; j < RP; ++j) l += tv[j] * (j < r ? bf2f(bh[j]) : 0.f);
   }
-  Y[n] = f2bf(y + scale * l);
+  Y[n] = f2bf(sl + scale * l);
 }
 
 template <int RB, int R>
