@@ -20,7 +20,9 @@ pytestmark = pytest.mark.gpu
 MIX = [(1, 1024, 2560, 32, False), (1, 264, 2560, 32, True), (1, 4100, 2560, 24, True),
        (1, 520, 2560, 16, True), (1, 1032, 1024, 16, False), (8, 2048, 512, 16, False),
        (8, 136, 512, 32, True), (100, 512, 512, 16, False), (1, 200, 512, 8, False),
-       (16, 1040, 256, 32, False)]
+       (16, 1040, 256, 32, False),
+       # one-token forwards whose K ends inside a 64-deep segment
+       (1, 72, 1000, 20, False), (1, 48, 136, 8, False)]
 
 
 def _make(i, M, N, K, r):

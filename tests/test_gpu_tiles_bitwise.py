@@ -67,3 +67,35 @@ def test_tile_integer_inputs_bitwise(gpu_lib, tid, r, mode, M, N):
     want = oracle.round_bf16(oracle.fwd(t["X"], t["W"], t["A"], t["B"], s))
     bad = np.argwhere(Y != want)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {tuple(bad[0])}"
+
+
+_FIRST_RANK = {}
+for _tid, _r, *_ in _tiles():
+    _FIRST_RANK.setdefault(_tid, _r)
+SHORT_K = [(tid, r, k) for tid, r in _FIRST_RANK.items() for k in (8, 0)]
+
+
+@pytest.mark.parametrize("tid,r,K", SHORT_K, ids=[f"tile{c[0]}_r{c[1]}_k{c[2]}" for c in SHORT_K])
+def test_tile_short_k(gpu_lib, tid, r, K):
+    """K = 8 (one 16-B chunk per row, every stage but the first past K) and
+    K = 0 (no stage in range: the output is exactly zero) on every tile, at
+    its first rank class, on a grid that neither mapping divides."""
+    import torch
+    info = gpu_lib.tile_info(tid, r)
+    M, N = 3 * info.bm - 3, 5 * info.bn * info.group - 5
+    rng = np.random.default_rng(tid * 31 + K)
+    ints = {k: rng.integers(-1, 2, shp).astype(np.float32)
+            for k, shp in (("X", (M, K)), ("W", (N, K)), ("A", (r, K)), ("B", (N, r)))}
+    t = {k: synth.f32_to_bf16_bits(v) for k, v in ints.items()}
+    X, W, A, B = (to_dev(t[k]) for k in "XWAB")
+    Yt = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")  # must be overwritten
+    print(f"tile {tid} r {r}: M {M} N {N} K {K}", flush=True)
+    gpu_lib.fwd(X, W, A, B, 2.0, out=Yt, tile=tid)
+    torch.cuda.synchronize()
+    if K == 0:
+        assert (Yt == 0).all().item()
+        return
+    Y = to_host(Yt)
+    want = oracle.round_bf16(oracle.fwd(t["X"], t["W"], t["A"], t["B"], 2.0))
+    bad = np.argwhere(Y != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {tuple(bad[0])}"
