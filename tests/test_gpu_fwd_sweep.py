@@ -1,7 +1,8 @@
 """The forward's built-in tile choice across its boundaries: shapes picked so
 that every default configuration (decode kernel; 32 x 32, 64 x 32, 64 x 64,
 128 x 128 and 128 x 256 tiles with loader waves; 128 x 128 two-stage; 256 x
-256; 128 x 128 and 128 x 256 tiles keeping T over several N tiles) runs with ragged M, N and K tails and ranks below their padded rank.
+256; 128 x 128, 128 x 256 and 256 x 256 tiles keeping T over several N
+tiles) runs with ragged M, N and K tails and ranks below their padded rank.
 
 Bar: relative Frobenius error <= 1e-2 (bf16) against the fp64 oracle and
 every element within the per-element bound of the kernels' arithmetic
@@ -37,6 +38,8 @@ SHAPES = [
     (4100, 4100, 136, 128),  # 128 x 128 sharing T over 2 N tiles (too few 128 x 256 groups)
     (5000, 3000, 136, 200),  # 128 x 128, two stages, rank 256
     (4000, 4096, 96, 20),    # 256 x 256 (256 tiles, ragged M)
+    (16380, 8190, 136, 120), # 256 x 256 keeping T over 8 N tiles, T from a prologue, rank 128
+    (16380, 8190, 136, 40),  # the same tile, rank 64 (two 64-deep stages)
 ]
 
 
