@@ -783,8 +783,22 @@ hipError_t launch_dec_row_batch(const FwdArgs* a, int i0, int i1, unsigned char*
   return hipGetLastError();
 }
 
+// 64-deep segments per wave and round of the one-token kernel: eight at
+// rank 16; at rank 32, where the A rows take twice the registers, five when
+// that covers K in one round of the 8 waves (K <= 2560: a second round for
+// some waves would wait on the first one's products), else four.  The
+// single forward and the batched forms take the same choice, so their
+// partitions -- and outputs -- stay the same.
+inline int row_segments(const FwdArgs& a) { return a.r <= 16 ? 8 : (a.K <= 2560 ? 5 : 4); }
+
 hipError_t launch_fwd_decode_bf16(const FwdArgs& a, hipStream_t s) {
-  if (a.M == 1) return a.r <= 16 ? launch_dec_row<1, 8>(a, s) : launch_dec_row<2, 4>(a, s);
+  if (a.M == 1) {
+    switch (row_segments(a)) {
+      case 8: return launch_dec_row<1, 8>(a, s);
+      case 5: return launch_dec_row<2, 5>(a, s);
+      default: return launch_dec_row<2, 4>(a, s);
+    }
+  }
   return a.r <= 16 ? launch_dec_rb<1>(a, nullptr, 0, 0, nullptr, s)
                    : launch_dec_rb<2>(a, nullptr, 0, 0, nullptr, s);
 }
@@ -819,11 +833,22 @@ hipError_t launch_fwd_decode_bf16_batch(const FwdArgs* a, int count, void* tws, 
   for (int i = 0; i < count; i += kDecBatch) {
     const int j = i + kDecBatch < count ? i + kDecBatch : count;
     unsigned char* wi = w ? w + (size_t)i * kDecTpBytes : nullptr;
-    hipError_t e;
-    if (a[i].M == 1)  // the one-token kernel of lora_fwd, per forward
-      e = a[i].r <= 16 ? launch_dec_row_batch<1, 8>(a, i, j, wi, s)
-                       : launch_dec_row_batch<2, 4>(a, i, j, wi, s);
-    else
+    hipError_t e = hipSuccess;
+    if (a[i].M == 1) {
+      // the one-token kernel of lora_fwd, per forward: one launch per run of
+      // forwards with the same segment count
+      for (int k = i; k < j && e == hipSuccess;) {
+        int l = k + 1;
+        while (l < j && row_segments(a[l]) == row_segments(a[k])) ++l;
+        unsigned char* wk = w ? w + (size_t)k * kDecTpBytes : nullptr;
+        switch (row_segments(a[k])) {
+          case 8: e = launch_dec_row_batch<1, 8>(a, k, l, wk, s); break;
+          case 5: e = launch_dec_row_batch<2, 5>(a, k, l, wk, s); break;
+          default: e = launch_dec_row_batch<2, 4>(a, k, l, wk, s); break;
+        }
+        k = l;
+      }
+    } else
       e = a[i].r <= 16 ? launch_dec_rb<1>(a[i], a, i, j, wi, s)
                        : launch_dec_rb<2>(a[i], a, i, j, wi, s);
     if (e != hipSuccess) return e;
