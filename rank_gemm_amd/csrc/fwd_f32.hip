@@ -127,28 +127,44 @@ __global__ __launch_bounds__(kF32Threads) void fwd_tiled_f32_kernel(
     const unsigned char* xs = smem_raw + (kt % S) * C::kStageB;
     const unsigned char* ws = xs + BT * kF32BK * 4;
     const unsigned char* as = ws + BT * kF32BK * 4;
+    // The stage's fragments first (at ranks <= 32 the A ones too), then the
+    // MFMAs: read and multiplied in turn, each 4-deep k step waited for its
+    // LDS reads before its MFMAs (the T MFMAs sit behind a per-wave branch).
+    constexpr int KS = kF32BK / 4;
+    constexpr bool kPre = C::RB <= 2;
+    float a[KS][TW], b[KS][TW], bt[kPre ? KS : 1][kPre ? C::RB : 1];
 #pragma unroll
-    for (int ks = 0; ks < kF32BK / 4; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int kc = ks * 4 + lk;
-      float a[TW], b[TW];
 #pragma unroll
       for (int i = 0; i < TW; ++i)
-        a[i] = *reinterpret_cast<const float*>(xs + f32_off(wm * HB + i * 16 + lrow, kc));
+        a[ks][i] = *reinterpret_cast<const float*>(xs + f32_off(wm * HB + i * 16 + lrow, kc));
 #pragma unroll
       for (int j = 0; j < TW; ++j)
-        b[j] = *reinterpret_cast<const float*>(ws + f32_off(wn * HB + j * 16 + lrow, kc));
+        b[ks][j] = *reinterpret_cast<const float*>(ws + f32_off(wn * HB + j * 16 + lrow, kc));
+      if constexpr (kPre) {
+#pragma unroll
+        for (int tj = 0; tj < C::RB; ++tj)
+          bt[ks][tj] = *reinterpret_cast<const float*>(as + f32_off(tj * 16 + lrow, kc));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kc = ks * 4 + lk;
 #pragma unroll
       for (int i = 0; i < TW; ++i)
 #pragma unroll
-        for (int j = 0; j < TW; ++j) acc[i][j] = mfma16x16x4f32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < TW; ++j) acc[i][j] = mfma16x16x4f32(a[ks][i], b[ks][j], acc[i][j]);
 #pragma unroll
       for (int i = 0; i < TW; ++i)
 #pragma unroll
         for (int tj = 0; tj < C::RB; ++tj) {
           const int idx = i * C::RB + tj;
           if ((idx & 1) != wn) continue;
-          const float bt = *reinterpret_cast<const float*>(as + f32_off(tj * 16 + lrow, kc));
-          tacc[idx >> 1] = mfma16x16x4f32(a[i], bt, tacc[idx >> 1]);
+          float t;
+          if constexpr (kPre) t = bt[ks][tj];
+          else t = *reinterpret_cast<const float*>(as + f32_off(tj * 16 + lrow, kc));
+          tacc[idx >> 1] = mfma16x16x4f32(a[ks][i], t, tacc[idx >> 1]);
         }
     }
     // This wave's reads of stage kt are done before the next barrier.
