@@ -43,6 +43,12 @@ struct F32Cfg {
   static_assert(kLds <= 160 * 1024, "LDS budget");
   static constexpr int kTTiles = TW * RB;              // T tiles per wave row
   static constexpr int kTSlots = (kTTiles + 1) / 2;    // split over the 2 waves of a row
+  // T tile ownership within a wave row: with an even number of rank blocks,
+  // wave wn takes rank blocks [wn RB / 2, (wn + 1) RB / 2) of every row
+  // block (slot i RB / 2 + t), so its A fragments are the same for all row
+  // blocks; with one rank block, row block i goes to wave i % 2 (slot i / 2).
+  static constexpr bool kTHalf = RB % 2 == 0;
+  static constexpr int kTB = kTHalf ? RB / 2 : 1;      // A fragments per wave and k step
 };
 
 // Byte offset of float k of staged row `row`: 16-B chunk k / 4 sits at
@@ -127,12 +133,11 @@ __global__ __launch_bounds__(kF32Threads) void fwd_tiled_f32_kernel(
     const unsigned char* xs = smem_raw + (kt % S) * C::kStageB;
     const unsigned char* ws = xs + BT * kF32BK * 4;
     const unsigned char* as = ws + BT * kF32BK * 4;
-    // The stage's fragments first (at ranks <= 32 the A ones too), then the
+    // The stage's fragments first (X, W and this wave's A ones), then the
     // MFMAs: read and multiplied in turn, each 4-deep k step waited for its
-    // LDS reads before its MFMAs (the T MFMAs sit behind a per-wave branch).
+    // own LDS reads.
     constexpr int KS = kF32BK / 4;
-    constexpr bool kPre = C::RB <= 2;
-    float a[KS][TW], b[KS][TW], bt[kPre ? KS : 1][kPre ? C::RB : 1];
+    float a[KS][TW], b[KS][TW], bt[KS][C::kTB];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int kc = ks * 4 + lk;
@@ -142,12 +147,13 @@ __global__ __launch_bounds__(kF32Threads) void fwd_tiled_f32_kernel(
 #pragma unroll
       for (int j = 0; j < TW; ++j)
         b[ks][j] = *reinterpret_cast<const float*>(ws + f32_off(wn * HB + j * 16 + lrow, kc));
-      if constexpr (kPre) {
 #pragma unroll
-        for (int tj = 0; tj < C::RB; ++tj)
-          bt[ks][tj] = *reinterpret_cast<const float*>(as + f32_off(tj * 16 + lrow, kc));
+      for (int t = 0; t < C::kTB; ++t) {
+        const int tj = C::kTHalf ? wn * C::kTB + t : 0;
+        bt[ks][t] = *reinterpret_cast<const float*>(as + f32_off(tj * 16 + lrow, kc));
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep every read of the stage ahead of the MFMAs
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int kc = ks * 4 + lk;
@@ -155,17 +161,19 @@ __global__ __launch_bounds__(kF32Threads) void fwd_tiled_f32_kernel(
       for (int i = 0; i < TW; ++i)
 #pragma unroll
         for (int j = 0; j < TW; ++j) acc[i][j] = mfma16x16x4f32(a[ks][i], b[ks][j], acc[i][j]);
+      if constexpr (C::kTHalf) {
 #pragma unroll
-      for (int i = 0; i < TW; ++i)
+        for (int i = 0; i < TW; ++i)
 #pragma unroll
-        for (int tj = 0; tj < C::RB; ++tj) {
-          const int idx = i * C::RB + tj;
-          if ((idx & 1) != wn) continue;
-          float t;
-          if constexpr (kPre) t = bt[ks][tj];
-          else t = *reinterpret_cast<const float*>(as + f32_off(tj * 16 + lrow, kc));
-          tacc[idx >> 1] = mfma16x16x4f32(a[ks][i], t, tacc[idx >> 1]);
+          for (int t = 0; t < C::kTB; ++t)
+            tacc[i * C::kTB + t] = mfma16x16x4f32(a[ks][i], bt[ks][t], tacc[i * C::kTB + t]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          if ((i & 1) != wn) continue;
+          tacc[i >> 1] = mfma16x16x4f32(a[ks][i], bt[ks][0], tacc[i >> 1]);
         }
+      }
     }
     // This wave's reads of stage kt are done before the next barrier.
     wait_lgkm0();
@@ -180,13 +188,13 @@ __global__ __launch_bounds__(kF32Threads) void fwd_tiled_f32_kernel(
 #pragma unroll
   for (int i = 0; i < TW; ++i)
 #pragma unroll
-    for (int tj = 0; tj < C::RB; ++tj) {
-      const int idx = i * C::RB + tj;
-      if ((idx & 1) != wn) continue;
-      const int j = tj * 16 + lrow;
+    for (int t = 0; t < C::kTB; ++t) {
+      if (!C::kTHalf && (i & 1) != wn) continue;
+      const int sl = C::kTHalf ? i * C::kTB + t : i >> 1;
+      const int j = (C::kTHalf ? wn * C::kTB + t : 0) * 16 + lrow;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        ts[(wm * HB + i * 16 + lk * 4 + q) * C::kES + j] = j < r ? scale * tacc[idx >> 1][q] : 0.f;
+        ts[(wm * HB + i * 16 + lk * 4 + q) * C::kES + j] = j < r ? scale * tacc[sl][q] : 0.f;
     }
   for (int e = tid; e < BT * RP; e += kF32Threads) {
     const int n = e / RP, j = e % RP;
