@@ -144,12 +144,14 @@ int lora_fwd_variant(int variant, int dtype, int64_t M, int64_t N, int64_t K, in
  *
  * With a workspace, each launch of batched decode forwards is preceded by a
  * small launch that computes T = X A^T once per forward (A is then read once
- * instead of once per 16 output columns, and the weight stream keeps four
- * 128-deep K blocks per wave in flight at any rank).  For r <= 16 the results
- * are still bitwise lora_fwd's (same partition of K, same summation order);
- * for 16 < r <= 32 the weight stream is partitioned differently and Y
- * differs from lora_fwd's by fp32 rounding order only (deterministic all the
- * same).
+ * instead of once per 16 output columns, and the weight stream reads W
+ * alone).  One-token forwards (M = 1) stay bitwise lora_fwd's at every rank
+ * (the T launch repeats the one-token kernel's partial sums and the stream
+ * adds them in its order); for 2 <= M <= 16 the results are bitwise
+ * lora_fwd's for r <= 16 (same partition of K, same summation order), while
+ * for 16 < r <= 32 the weight stream keeps four 128-deep K blocks per wave in
+ * flight, is partitioned differently and Y differs from lora_fwd's by fp32
+ * rounding order only (deterministic all the same).
  *
  *   dtype         LORA_F32 or LORA_BF16, for every forward.
  *   count         number of descriptors, >= 0 (0: no-op).
