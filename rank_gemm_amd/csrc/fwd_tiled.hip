@@ -161,7 +161,8 @@ struct Cfg {
   // Otherwise, where it fits after the ring and the output staging without
   // costing a workgroup per CU, the B tile is fetched at kernel start by
   // direct loads into LDS (unpadded rows of RP elements), landing with the
-  // first stage; tiles with loader waves and the k split keep the gather
+  // first stage; in tiles with loader waves the loaders fetch it into
+  // registers instead (see the kernel), and the k split keeps the gather
   // after the K loop.
   static constexpr int kBDmaOff = cmax(STAGES * kStageB, kYB);
   static constexpr int kBDmaB = BN * RP * 2;
@@ -556,6 +557,30 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
     }
   }
 
+  // Tiles with loader waves: the loaders fetch the B tile into registers
+  // (16 B per load, before any stage load, so the stage waits' counts still
+  // hold: loads complete in order) and write it to LDS after the K loop,
+  // when every 16-B chunk of a B row is aligned and wholly inside or wholly
+  // past the rank (else the gather after the K loop).  Assigned only on the
+  // loaders' path, so the multiplying waves' loop does not hold it.  (Not
+  // for 256 x 160: its multiplying waves then spill.)
+  constexpr bool kBPf = C::PW > 0 && G == 1 && C::KS == 1 && C::BM * C::BN <= 128 * 256;
+  constexpr int kBChunks = C::BN * RP / 8;                        // 16-B chunks of the tile
+  constexpr int kBCh = kBPf ? (kBChunks + C::PW * kWave - 1) / (C::PW * kWave) : 1;
+  const bool bpf = kBPf && r % 8 == 0 && ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
+  u32x4 bpre16[kBCh];
+  auto fetch_b = [&](int nb0) {
+#pragma unroll
+    for (int i = 0; i < kBCh; ++i) {
+      const int cidx = lw * kWave + lane + i * C::PW * kWave;
+      const int n = cidx / (RP / 8), j0 = (cidx % (RP / 8)) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (cidx < kBChunks && nb0 + n < N && j0 < r)
+        v = *reinterpret_cast<const u32x4*>(B + (int64_t)(nb0 + n) * ldb + j0);
+      bpre16[i] = v;
+    }
+  };
+
   if constexpr (C::kTP) {
     static_assert(G > 1, "T prologue: a group of N tiles");
     t_prologue<C>(smem, reinterpret_cast<uint16_t*>(smem + C::kTOffG), K, r, scale, rx, ra, ldx,
@@ -684,6 +709,9 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
   } else {
   if constexpr (C::PW > 0) {
     if (!mul) {
+      if constexpr (kBPf) {
+        if (bpf) fetch_b(n0);
+      }
       // Loader: the same barriers as the multiplying waves (one after stage
       // 0 has landed, one per stage), each preceded by the wait for the
       // stage the multipliers read next; after the barrier of stage kt every
@@ -962,7 +990,18 @@ __global__ __launch_bounds__(C::NT) void fwd_tiled_bf16_kernel(
       }
     }
   } else {
-    if (!bdma) {
+    if (kBPf && bpf) {
+      if (!mul) {
+#pragma unroll
+        for (int i = 0; i < kBCh; ++i) {
+          const int cidx = lw * kWave + lane + i * C::PW * kWave;
+          if (cidx < kBChunks) {
+            const int n = cidx / (RP / 8), j0 = (cidx % (RP / 8)) * 8;
+            *reinterpret_cast<u32x4*>(bs + n * C::kTS + j0) = bpre16[i];
+          }
+        }
+      }
+    } else if (!bdma) {
       for (int e = tid; e < BN * RP; e += C::NT) {
         const int n = e / RP, j = e % RP;
         uint16_t v = 0;
