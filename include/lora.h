@@ -142,12 +142,16 @@ int lora_fwd_variant(int variant, int dtype, int64_t M, int64_t N, int64_t K, in
  * concurrently, so every Y must also not overlap any other forward's X, W,
  * A, B or Y (LORA_ERR_ALIAS); inputs may be shared.
  *
- * With a workspace, each launch of batched decode forwards is preceded by a
- * small launch that computes T = X A^T once per forward (A is then read once
- * instead of once per 16 output columns, and the weight stream reads W
- * alone).  One-token forwards (M = 1) stay bitwise lora_fwd's at every rank
- * (the T launch repeats the one-token kernel's partial sums and the stream
- * adds them in its order); for 2 <= M <= 16 the results are bitwise
+ * With a workspace, T = X A^T is computed once per forward (A is then read
+ * once instead of once per 16 output columns, and the weight stream reads W
+ * alone).  For one-token forwards (M = 1) the first workgroups of the same
+ * launch compute T into the workspace and set a flag there for each weight
+ * workgroup, which streams its W meanwhile and waits for its flag only
+ * before the epilogue (forwards with more than 30720 output columns take T
+ * from a launch of its own); for 2 <= M <= 16 a small launch computes T
+ * first.  One-token forwards stay bitwise lora_fwd's at every rank (T
+ * repeats the one-token kernel's partial sums and the stream adds them in
+ * its order); for 2 <= M <= 16 the results are bitwise
  * lora_fwd's for r <= 16 (same partition of K, same summation order), while
  * for 16 < r <= 32 the weight stream keeps four 128-deep K blocks per wave in
  * flight, is partitioned differently and Y differs from lora_fwd's by fp32
@@ -158,7 +162,9 @@ int lora_fwd_variant(int variant, int dtype, int64_t M, int64_t N, int64_t K, in
  *   descs         HOST array of count descriptors, read during the call only.
  *   workspace     NULL, or device scratch of workspace_bytes >=
  *                 lora_fwd_batch_workspace_size(count), 256-byte aligned,
- *                 not overlapping any operand; content ignored on entry,
+ *                 not overlapping any operand; content ignored on entry
+ *                 (each launch's flags carry a value of that launch, and
+ *                 every flag is cleared again before the launch ends),
  *                 unspecified on return; calls in flight at the same time
  *                 need separate workspaces.
  *   stream        hipStream_t as void*.

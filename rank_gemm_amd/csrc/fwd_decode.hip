@@ -21,6 +21,7 @@
 // The waves' partial sums are added in a fixed order through LDS
 // (deterministic), then the epilogue adds scale * T B^T in fp32 on the VALU
 // and stores bf16 (one rounding).
+#include <algorithm>
 #include <atomic>
 
 #include "common.h"
@@ -318,16 +319,46 @@ __device__ __forceinline__ float dot8(const u32x4& p, const u32x4& q, float acc)
   return acc;
 }
 
+// Device-scope (agent) accesses of the words one workgroup hands another
+// within a launch: each is coherent across the XCDs' L2s by itself, so the
+// hand-over needs no L2 write-back or invalidation, only completion order
+// (the writer waits for its stores before it sets the flag; the reader
+// issues its loads after the flag's value came back).
+__device__ __forceinline__ void dev_store(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float dev_load(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Wait (the calling wave) until *flag holds tok, then clear it.  The wait is
+// bounded (about 0.1 s): false if the value never came.
+__device__ __forceinline__ bool dec_wait_flag(uint64_t* flag, uint64_t tok) {
+  uint64_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0; v != tok && it < (1 << 20); ++it) {
+    __builtin_amdgcn_s_sleep(2);
+    v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __hip_atomic_store(flag, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v == tok;
+}
+
 // The 16 rows [n0, n0 + 16) of one forward.  TP: the T partial sums of the
-// NW waves come from `tp` (RP floats per wave, as dec_row_t_kernel writes
-// them) and A is neither loaded nor multiplied.
+// NW waves come from `tp` (RP floats per wave, as dec_row_t_wave writes
+// them) and A is neither loaded nor multiplied.  flag (TP only, may be
+// null): the partial sums are written by another workgroup of the same
+// launch, which then stores `tok` into *flag; wave 0 waits for that value
+// before it reads them, and sets the flag back to zero.
 template <int RB, int R, bool TP>
 __device__ __forceinline__ void dec_row_body(int N, int K, int r, const uint16_t* __restrict__ X,
                                              const uint16_t* __restrict__ W, int64_t ldw,
                                              const uint16_t* __restrict__ A, int64_t lda,
                                              const uint16_t* __restrict__ B, int64_t ldb,
                                              float scale, uint16_t* __restrict__ Y, int b_vec,
-                                             int n0, const float* __restrict__ tp) {
+                                             int n0, const float* tp,
+                                             uint64_t* flag = nullptr, uint64_t tok = 0) {
   constexpr int NW = 8, RP = RB * 16;
   static_assert(R <= 8 && 2 * RB * R + 2 * R < 64, "one 1-KiB X piece per wave and round");
   __shared__ float red[NW][16 + (TP ? 0 : RP)];
@@ -443,6 +474,10 @@ __device__ __forceinline__ void dec_row_body(int N, int K, int r, const uint16_t
   }
   __syncthreads();
   if (wave != 0) return;
+  bool ready = true;
+  if constexpr (TP) {
+    if (flag != nullptr) ready = dec_wait_flag(flag, tok);
+  }
   // Wave 0, lane l < 16 + RP: partial l summed over the waves in wave order
   // (l < 16: Ybase of row n0 + l; else T[l - 16]), each sum once; the row
   // lanes then take T by shuffles and add the rank sum in j order.  T's
@@ -453,7 +488,7 @@ __device__ __forceinline__ void dec_row_body(int N, int K, int r, const uint16_t
     for (int v = 0; v < NW; ++v) sl += red[v][lane];
   } else if (lane < 16 + RP) {
     for (int v = 0; v < NW; ++v) {
-      if constexpr (TP) sl += tp[v * RP + lane - 16];
+      if constexpr (TP) sl += dev_load(&tp[v * RP + lane - 16]);
       else sl += red[v][lane];
     }
   }
@@ -477,7 +512,8 @@ __device__ __forceinline__ void dec_row_body(int N, int K, int r, const uint16_t
 #pragma unroll
     for (int j = 0; j < RP; ++j) l += tv[j] * (j < r ? bf2f(bh[j]) : 0.f);
   }
-  Y[n] = f2bf(sl + scale * l);
+  // A partial sum that never arrived (a wait past its bound) shows as NaN.
+  Y[n] = ready ? f2bf(sl + scale * l) : (uint16_t)0x7FC0u;
 }
 
 template <int RB, int R>
@@ -617,20 +653,18 @@ __global__ __launch_bounds__(512) void fwd_decode_row_batch_kernel(const DecBatc
                           d.b_vec, (b - args.first[lo]) * 16, reinterpret_cast<const float*>(d.tp));
 }
 
-// T of every one-token forward of a batch, wave partition by wave
-// partition: workgroup (t, w) is one wave doing for forward t exactly what
-// wave w of dec_row_body does for T -- the same segments, X piece, A loads,
-// dot8 chains and butterfly -- and it stores the RP partial sums
-// (tp[w * RP + j]).  The batch kernel adds them in wave order, as
-// dec_row_body's LDS reduction does, so T and Y are bitwise those of the
-// single forward; A is read once per forward, by 8 workgroups at once.
+// T of one one-token forward, one wave's share: exactly what wave `wave`
+// of dec_row_body does for T -- the same segments, X piece (through this
+// wave's 1 KiB of LDS, xsh), A loads, dot8 chains and butterfly -- stored
+// as its RP partial sums (tp[wave * RP + j]).  The weight stream adds the
+// eight in wave order, as dec_row_body's LDS reduction does, so T and Y are
+// bitwise those of the single forward; A is read once per forward instead
+// of once per 16 rows of W.
 template <int RB, int R>
-__global__ __launch_bounds__(64) void dec_row_t_kernel(const DecBatch args) {
+__device__ __forceinline__ void dec_row_t_wave(const DecDesc& d, int wave, int lane,
+                                               unsigned char* xsh) {
   constexpr int NW = 8, RP = RB * 16;
-  __shared__ __attribute__((aligned(16))) unsigned char xsh[1024];
-  const int t = blockIdx.x / NW, wave = blockIdx.x % NW;
-  const DecDesc& d = args.d[t];
-  const int lane = threadIdx.x, g = lane >> 3, c = lane & 7;
+  const int g = lane >> 3, c = lane & 7;
   const int K = d.K, r = d.r;
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc((void*)d.X, 0, K * 2, 0x00020000);
@@ -675,8 +709,68 @@ __global__ __launch_bounds__(64) void dec_row_t_kernel(const DecBatch args) {
   float* tp = reinterpret_cast<float*>(d.tp);
   if (c == 0) {
 #pragma unroll
-    for (int q = 0; q < 2 * RB; ++q) tp[wave * RP + 8 * q + g] = tacc[q];
+    for (int q = 0; q < 2 * RB; ++q) dev_store(&tp[wave * RP + 8 * q + g], tacc[q]);
   }
+}
+
+// T of every one-token forward of a batch in a launch of its own: workgroup
+// (t, w) is one wave doing wave w's share of forward t.
+template <int RB, int R>
+__global__ __launch_bounds__(64) void dec_row_t_kernel(const DecBatch args) {
+  __shared__ __attribute__((aligned(16))) unsigned char xsh[1024];
+  dec_row_t_wave<RB, R>(args.d[blockIdx.x / 8], blockIdx.x % 8, threadIdx.x, xsh);
+}
+
+// The T partial sums and the weight stream of one-token forwards in one
+// launch.  Workgroups [0, count) compute T, one per forward (wave w doing
+// wave w's share), then store `tok` into the flag of every weight
+// workgroup of that forward (kDecFlagOff bytes into the forward's workspace
+// slot, one 8-byte flag per 16 rows of W).  The weight workgroups follow;
+// they stream W as in the two-launch form and wait for their flag only
+// before the epilogue reads T.  Workgroups are dispatched in id order, so
+// every T workgroup is running before any weight workgroup can wait on it.
+// Each weight workgroup clears its flag after the wait, which leaves every
+// flag zero at the end of a launch: a replayed graph reusing tok finds no
+// stale value.
+constexpr int kDecFlagOff = 1024;  // after the 8 x RP <= 256 partial sums
+constexpr int kDecMaxFlags = (kDecTpBytes - kDecFlagOff) / 8;
+template <int RB, int R>
+__global__ __launch_bounds__(512) void fwd_decode_row_fused_kernel(const DecBatch args,
+                                                                   uint64_t tok) {
+  static_assert(8 * RB * 16 * 4 <= kDecFlagOff, "T partial sums below the flags");
+  const int b = blockIdx.x;
+  if (b < args.count) {
+    __shared__ __attribute__((aligned(16))) unsigned char xsh[8][1024];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const DecDesc& d = args.d[b];
+    dec_row_t_wave<RB, R>(d, wave, lane, xsh[wave]);
+    // Every wave's partial sums (device-scope stores) complete before any
+    // flag is set.
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    uint64_t* flags = reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(d.tp) +
+                                                  kDecFlagOff);
+    const int nf = args.first[b + 1] - args.first[b];
+    for (int i = threadIdx.x; i < nf; i += 512)
+      __hip_atomic_store(&flags[i], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int bw = b - args.count;
+  int lo = 0, hi = args.count - 1;  // last t with first[t] <= bw
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (args.first[mid] <= bw) lo = mid; else hi = mid - 1;
+  }
+  const DecDesc& d = args.d[lo];
+  uint64_t* flags =
+      reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(d.tp) + kDecFlagOff);
+  const int wb = bw - args.first[lo];
+  dec_row_body<RB, R, true>(d.N, d.K, d.r, d.X, d.W, d.ldw, d.A, d.lda, d.B, d.ldb, d.scale, d.Y,
+                            d.b_vec, wb * 16, reinterpret_cast<const float*>(d.tp), flags + wb,
+                            tok);
 }
 
 // The forwards a[i0, i1) (same M, same rank class) in one launch; with a
@@ -764,14 +858,25 @@ hipError_t launch_dec_row(const FwdArgs& a, hipStream_t s) {
 }
 
 // One-token forwards a[i0, i1) (same rank class) in one launch; with a
-// workspace (tws: kDecTpBytes per forward) T first, in a launch of its own.
+// workspace (tws: kDecTpBytes per forward) T is computed once per forward,
+// by the first workgroups of the same launch (by a launch of its own when a
+// forward has more 16-row blocks than its slot has flags).
 template <int RB, int R>
 hipError_t launch_dec_row_batch(const FwdArgs* a, int i0, int i1, unsigned char* tws,
                                 hipStream_t s) {
   static_assert(8 * RB * 16 * 4 <= kDecTpBytes, "T partial sums fit the workspace slot");
   DecBatch bt{};
   const int blocks = dec_batch_fill(bt, a, i0, i1, tws);
-  if (tws != nullptr) {
+  int most = 0;  // weight workgroups of the largest forward
+  for (int t = 0; t < bt.count; ++t) most = std::max(most, bt.first[t + 1] - bt.first[t]);
+  if (tws != nullptr && most <= kDecMaxFlags) {
+    // A token per launch with the bit pattern of a signalling NaN (never a
+    // partial sum's bits) and a nonzero count below it.
+    static std::atomic<uint64_t> launches{0};
+    const uint64_t tok = 0x7FF4000000000000ull | ((launches.fetch_add(1) + 1) & 0xFFFFFFFFFFFull);
+    hipLaunchKernelGGL((fwd_decode_row_fused_kernel<RB, R>), dim3(bt.count + blocks), dim3(512),
+                       0, s, bt, tok);
+  } else if (tws != nullptr) {
     hipLaunchKernelGGL((dec_row_t_kernel<RB, R>), dim3(bt.count * 8), dim3(64), 0, s, bt);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_decode_row_batch_kernel<RB, R, true>), dim3(blocks), dim3(512), 0, s,

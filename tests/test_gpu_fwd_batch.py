@@ -1,7 +1,8 @@
 """lora_fwd_batch on the GPU: each output bitwise equal to lora_fwd's for the
 same forward (the batched decode launch runs the same kernel code per
-forward; one-token forwards with a workspace take T from a launch that
-reproduces the one-token kernel's own partial sums; with a workspace, 2 <= M
+forward; one-token forwards with a workspace take T from workgroups that
+reproduce the one-token kernel's own partial sums, in the same launch or,
+for very wide forwards, in a launch of their own; with a workspace, 2 <= M
 <= 16 and 16 < r <= 32, equal up to fp32 rounding order),
 over a mix that exercises the grouping: several decode-shaped
 forwards sharing X (different N and K), a change of rank class, a change of
@@ -22,7 +23,10 @@ MIX = [(1, 1024, 2560, 32, False), (1, 264, 2560, 32, True), (1, 4100, 2560, 24,
        (8, 136, 512, 32, True), (100, 512, 512, 16, False), (1, 200, 512, 8, False),
        (16, 1040, 256, 32, False),
        # one-token forwards whose K ends inside a 64-deep segment
-       (1, 72, 1000, 20, False), (1, 48, 136, 8, False)]
+       (1, 72, 1000, 20, False), (1, 48, 136, 8, False),
+       # more 16-row blocks than a workspace slot has flags: T by a launch
+       # of its own
+       (1, 30736, 64, 16, False)]
 
 
 def _make(i, M, N, K, r):
@@ -95,3 +99,48 @@ def test_fwd_batch_graph_replays(gpu_lib, with_ws):
         torch.cuda.synchronize()
         for e, Y in zip(eager, outs):
             assert np.array_equal(to_host(Y), e), rep
+
+
+def test_fwd_batch_graph_new_tokens(gpu_lib):
+    """One-token forwards with a workspace, captured once and replayed with a
+    new X before each replay (as a decode loop does): every replay equals
+    lora_fwd on that replay's X, so no replay reads the T partial sums or
+    flags a previous one left in the workspace."""
+    import torch
+    rg = gpu_lib
+    shapes = [(1, 1024, 2560, 32), (1, 264, 2560, 32), (1, 520, 1024, 16), (1, 200, 512, 8)]
+    items, outs, xs, ops = [], [], [], []
+    for i, (M, N, K, r) in enumerate(shapes):
+        c, t = _make(40 + i, M, N, K, r)
+        X, W, A, B = (to_dev(t[k]) for k in ("X", "W", "A", "B"))
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        items.append((X, W, A, B, c.scale, Y))
+        outs.append(Y)
+        xs.append(X)
+        ops.append((W, A, B, c.scale))
+    ws = torch.full((rg.fwd_batch_workspace_size(len(items)),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    rg.fwd_batch(items, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            rg.fwd_batch(items, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        fresh = []
+        for i, (X, (M, N, K, r)) in enumerate(zip(xs, shapes)):
+            new = synth.FwdCase(f"tok{rep}_{i}", 9, 100 * rep + i, M, N, K, r, 2.0 * r,
+                                "bf16").make("X")["X"]
+            X.copy_(to_dev(new))
+            fresh.append(X.clone())
+        for Y in outs:
+            Y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for X, (W, A, B, scale), Y in zip(fresh, ops, outs):
+            single = to_host(rg.fwd(X, W, A, B, scale))
+            assert np.array_equal(to_host(Y), single), rep
