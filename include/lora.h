@@ -144,12 +144,14 @@ int lora_fwd_variant(int variant, int dtype, int64_t M, int64_t N, int64_t K, in
  *
  * With a workspace, T = X A^T is computed once per forward (A is then read
  * once instead of once per 16 output columns, and the weight stream reads W
- * alone).  For one-token forwards (M = 1) the first workgroups of the same
+ * alone).  For one-token forwards (M = 1) whose launch has more than 256
+ * weight workgroups of 16 output columns, the first workgroups of the same
  * launch compute T into the workspace and set a flag there for each weight
  * workgroup, which streams its W meanwhile and waits for its flag only
  * before the epilogue (forwards with more than 30720 output columns take T
- * from a launch of its own); for 2 <= M <= 16 a small launch computes T
- * first.  One-token forwards stay bitwise lora_fwd's at every rank (T
+ * from a launch of its own); smaller one-token launches ignore the
+ * workspace (with one workgroup per CU or fewer, T's latency would add to
+ * the stream's).  For 2 <= M <= 16 a small launch computes T first.  One-token forwards stay bitwise lora_fwd's at every rank (T
  * repeats the one-token kernel's partial sums and the stream adds them in
  * its order); for 2 <= M <= 16 the results are bitwise
  * lora_fwd's for r <= 16 (same partition of K, same summation order), while

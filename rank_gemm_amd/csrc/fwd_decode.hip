@@ -734,6 +734,7 @@ __global__ __launch_bounds__(64) void dec_row_t_kernel(const DecBatch args) {
 // stale value.
 constexpr int kDecFlagOff = 1024;  // after the 8 x RP <= 256 partial sums
 constexpr int kDecMaxFlags = (kDecTpBytes - kDecFlagOff) / 8;
+constexpr int kDecFusedMinBlocks = 256;
 template <int RB, int R>
 __global__ __launch_bounds__(512) void fwd_decode_row_fused_kernel(const DecBatch args,
                                                                    uint64_t tok) {
@@ -869,6 +870,13 @@ hipError_t launch_dec_row_batch(const FwdArgs* a, int i0, int i1, unsigned char*
   const int blocks = dec_batch_fill(bt, a, i0, i1, tws);
   int most = 0;  // weight workgroups of the largest forward
   for (int t = 0; t < bt.count; ++t) most = std::max(most, bt.first[t + 1] - bt.first[t]);
+  // With at most one weight workgroup per CU (256 on this chip) the stream
+  // ends about when T does, and T's latency adds to it (1 x 4096 x 4096:
+  // 11.1 us against 9.2 us recomputing T per workgroup); with more, T is
+  // ready before the stream's last workgroups start (1 x 9728 x 2560 r16:
+  // 13.4 against 15.9 us; q/k/v r16: 9.9 against 11.7 us).  Both ways give
+  // the same bits.
+  if (blocks <= kDecFusedMinBlocks) tws = nullptr;
   if (tws != nullptr && most <= kDecMaxFlags) {
     // A token per launch with the bit pattern of a signalling NaN (never a
     // partial sum's bits) and a nonzero count below it.

@@ -108,7 +108,9 @@ def test_fwd_batch_graph_new_tokens(gpu_lib):
     flags a previous one left in the workspace."""
     import torch
     rg = gpu_lib
-    shapes = [(1, 1024, 2560, 32), (1, 264, 2560, 32), (1, 520, 1024, 16), (1, 200, 512, 8)]
+    # two launches, each with more weight workgroups than CUs (T computed in
+    # the weight stream's launch)
+    shapes = [(1, 4096, 2560, 32), (1, 1024, 2560, 32), (1, 4100, 1024, 16), (1, 200, 1024, 8)]
     items, outs, xs, ops = [], [], [], []
     for i, (M, N, K, r) in enumerate(shapes):
         c, t = _make(40 + i, M, N, K, r)
