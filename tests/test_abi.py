@@ -404,3 +404,18 @@ def test_fwd_batch_noalloc_rejects_before_any_hip_call():
     assert rg.fwd_batch_noalloc_raw(rg.LORA_BF16, [_fdesc(r=0)]) == rg.LORA_ERR_SHAPE
     assert rg.fwd_batch_noalloc_raw(rg.LORA_BF16, [_fdesc(Y=PX)]) == rg.LORA_ERR_ALIAS
     assert rg.fwd_batch_noalloc_raw(rg.LORA_BF16, [_fdesc(M=0)]) == rg.LORA_OK
+
+
+def test_ceilings_library_exports_its_header():
+    """libceilings.so (the benchmark's machine-ceiling kernels, not part of
+    the LoRA path) exports every function include/ceilings.h declares."""
+    from rank_gemm_amd import build as b
+    if not os.path.exists(b.CEIL_LIB):
+        pytest.skip("libceilings.so not built")
+    src = open(os.path.join(ROOT, "include", "ceilings.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    declared = set(re.findall(r"\b(ceil_\w+)\s*\(", src))
+    assert {"ceil_mfma", "ceil_copy", "ceil_read"} <= declared
+    out = os.popen(f"nm -D --defined-only {b.CEIL_LIB}").read()
+    exported = set(re.findall(r"\bT\s+(ceil_\w+)", out))
+    assert declared <= exported, declared - exported
