@@ -24,9 +24,13 @@
 // Without dX: prep_kernel (B^T), proj_kernel (s G and s T), tc_kernel,
 // red_kernel.  With no tokens, red_kernel alone writes dA = 0 and dB = 0.
 // (Folding the reduction into the token contraction, the last workgroup of
-// a column tile adding the others' partials, needs an agent-scope release
-// fence per workgroup; on gfx950 that writes back the XCD's L2 and made the
-// contraction 8x slower than the separate reduce launch.)
+// a column tile adding the others' partials: with an agent-scope release
+// fence per workgroup, which on gfx950 writes back the XCD's L2, the
+// contraction ran 8x slower than the separate reduce launch; with the
+// partials written and read by device-scope atomic stores and loads and a
+// per-tile counter instead, the pass took 29.9 against 27.6 us on
+// X[4096,1024] W[1024,1024] r16 and 206 against 196-202 us on
+// X[8192,2560] W[4096,2560] r32, graph replays.)
 // W^T is rewritten on every call (2 |W| bytes of traffic): the forward
 // kernel's contiguous-contraction operand reads run faster than reading W
 // as stored through transposing LDS reads, by more than the copy costs
