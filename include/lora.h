@@ -39,7 +39,9 @@
  *     ld multiples of 4.  N, r, ldb and ldy are unrestricted.
  *   - Limits (LORA_ERR_UNSUPPORTED beyond them): every size <= 2^30 - 1;
  *     for lora_fwd, ldx, ldw and lda <= LORA_MAX_LD elements (the kernels
- *     address a 256-row tile of X or W with signed 32-bit byte ranges).
+ *     address a 256-row tile of X or W with signed 32-bit byte ranges), and
+ *     r * lda * (element size) <= 2^31 - 1 (A as one such range; binding
+ *     only for fp32 above rank 128).
  *   - Outputs must not overlap any input (LORA_ERR_ALIAS).
  *   - NaN and Inf in the inputs propagate as IEEE arithmetic makes them.
  */

@@ -48,6 +48,9 @@ int check_fwd(int dtype, int64_t M, int64_t N, int64_t K, int64_t r, const void*
   if (ldx < K || ldw < K || lda < K || ldb < r || ldy < N) return LORA_ERR_STRIDE;
   if (ldx > LORA_MAX_LD || ldw > LORA_MAX_LD || lda > LORA_MAX_LD) return LORA_ERR_UNSUPPORTED;
   const int64_t e = esize(dtype);
+  // A is addressed as one signed 32-bit byte range of r rows (fp32 above
+  // rank 128 can exceed it at the largest lda).
+  if (r * lda * e > INT32_MAX) return LORA_ERR_UNSUPPORTED;
   const int64_t kal = dtype == LORA_BF16 ? 8 : 4;
   if (K > 0) {
     if (!aligned16(X) || !aligned16(W) || !aligned16(A)) return LORA_ERR_ALIGN;

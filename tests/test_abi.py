@@ -79,6 +79,9 @@ def _merge(**kw):
     (dict(ldx=1 << 22), rg.LORA_ERR_UNSUPPORTED),
     (dict(ldw=1 << 22), rg.LORA_ERR_UNSUPPORTED),
     (dict(lda=1 << 22), rg.LORA_ERR_UNSUPPORTED),
+    # fp32 A as one signed 32-bit byte range: r * lda * 4 > 2^31 - 1
+    (dict(dtype=rg.LORA_F32, r=129, ldb=129, lda=(1 << 22) - 8), rg.LORA_ERR_UNSUPPORTED),
+    (dict(dtype=rg.LORA_F32, r=256, ldb=256, lda=(1 << 21)), rg.LORA_ERR_UNSUPPORTED),
     (dict(M=1 << 30), rg.LORA_ERR_UNSUPPORTED),
     (dict(X=0), rg.LORA_ERR_NULL),
     (dict(W=0), rg.LORA_ERR_NULL),

@@ -334,3 +334,43 @@ def test_lora_fwd_entry_point_raw(gpu_lib, c):
     torch.cuda.synchronize()
     ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], c.scale)
     _check("lora_fwd raw " + c.name, to_host(Y), ref, t, c.scale, c.dtype)
+
+
+LORA_MAX_LD = (1 << 22) - 8   # include/lora.h
+
+
+@pytest.mark.parametrize("dtype,r,tile", [("bf16", 8, None), ("bf16", 8, 4), ("bf16", 8, 18),
+                                          ("bf16", 256, None), ("f32", 128, None)])
+def test_largest_leading_dimensions(gpu_lib, dtype, r, tile):
+    """ldx = ldw = lda = LORA_MAX_LD, the largest the C ABI accepts, where a
+    256-row tile of X or W (bf16) and r rows of A (bf16 at r 256, fp32 at r
+    128) each span 2^31 - 4096 or 2^31 - 16384 bytes: just inside the
+    kernels' signed 32-bit buffer ranges.  Ragged 300 x 300 output (two row
+    and two column tiles of 256), every element against the oracle; tiles 4
+    and 18 are the 256 x 256 configurations, forced through lora_fwd_tile."""
+    import torch
+    M, N, K = 300, 300, 64
+    t = _rand_case(8, M, N, K, r, dtype)
+    ld = LORA_MAX_LD
+    big = {}
+    for k in "XWA":
+        a = to_dev(t[k])
+        b = torch.zeros((a.shape[0], ld), dtype=a.dtype, device=a.device)
+        b[:, :K] = a
+        big[k] = b
+    B = to_dev(t["B"])
+    Y = torch.full((M, N), float("nan"), dtype=B.dtype, device=B.device)
+    scale = 2.0
+    if tile is None:
+        gpu_lib.fwd(big["X"][:, :K], big["W"][:, :K], big["A"][:, :K], B, scale, out=Y)
+    else:
+        st = gpu_lib.fwd_tile_raw(tile, gpu_lib.LORA_BF16, M, N, K, r, big["X"].data_ptr(), ld,
+                                  big["W"].data_ptr(), ld, big["A"].data_ptr(), ld, B.data_ptr(),
+                                  r, scale, Y.data_ptr(), N,
+                                  torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+    torch.cuda.synchronize()
+    del big
+    got = to_host(Y)
+    ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], scale)
+    _check(f"max ld {dtype} r{r} tile {tile}", got, ref, t, scale, dtype)
