@@ -374,3 +374,46 @@ def test_largest_leading_dimensions(gpu_lib, dtype, r, tile):
     got = to_host(Y)
     ref = oracle.fwd(t["X"], t["W"], t["A"], t["B"], scale)
     _check(f"max ld {dtype} r{r} tile {tile}", got, ref, t, scale, dtype)
+
+
+@pytest.mark.parametrize("M,N,K,r,dtype,variant", [(130, 200, 264, 20, "bf16", "tiled"),
+                                                   (4, 300, 136, 16, "bf16", "decode"),
+                                                   (1, 300, 136, 32, "bf16", "decode"),
+                                                   (70, 90, 100, 12, "f32", "tiled")])
+def test_nan_and_inf_propagate(gpu_lib, M, N, K, r, dtype, variant):
+    """A NaN in X[m0, k0], +Inf in W[n1, k1] and a NaN in B[n2, j2] (j2 < r)
+    give what the fp64 oracle gives: row m0 and column n2 NaN, column n1 +-Inf
+    with the oracle's signs (NaN at m0), and every other element within the
+    per-element bound of the arithmetic (those touch no special value)."""
+    import torch
+    t = _rand_case(9, M, N, K, r, dtype)
+    X, W, B = t["X"].copy(), t["W"].copy(), t["B"].copy()
+    m0, k0, n1, k1, n2, j2 = M // 2, K // 3, N // 4, K - 1, N - 2, r - 1
+    if dtype == "bf16":          # bf16 operands are held as their bit patterns
+        nan, inf = np.uint16(0x7FC0), np.uint16(0x7F80)
+    else:
+        nan, inf = np.float32(np.nan), np.float32(np.inf)
+    X[m0, k0] = nan
+    W[n1, k1] = inf
+    B[n2, j2] = nan
+    scale = 2.0
+    Xd, Wd, Ad, Bd = to_dev(X), to_dev(W), to_dev(t["A"]), to_dev(B)
+    Y = gpu_lib.fwd(Xd, Wd, Ad, Bd, scale, variant=variant)
+    torch.cuda.synchronize()
+    got = as_f64(to_host(Y))
+    ref = oracle.fwd(X, W, t["A"], B, scale)
+    assert np.isnan(ref[m0]).all() and np.isnan(ref[:, n2]).all()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    inf = np.isinf(ref)
+    assert inf[:, n1].sum() == M - 1
+    assert np.array_equal(np.sign(got[inf]), np.sign(ref[inf]))
+    rows = [m for m in range(M) if m != m0]
+    cols = [n for n in range(N) if n not in (n1, n2)]
+    g = np.ascontiguousarray(to_host(Y)[np.ix_(rows, cols)])
+    rs = np.ascontiguousarray(ref[np.ix_(rows, cols)])
+    ratio = check_fwd_elements(g, rs, np.ascontiguousarray(X[rows]), np.ascontiguousarray(W[cols]),
+                               t["A"], np.ascontiguousarray(B[cols]), scale, dtype,
+                               f"special {dtype} {variant}")
+    assert rel_fro(as_f64(g), rs) <= TOL[dtype]
+    print(f"special values {dtype} {variant}: worst/bound={ratio:.3f}")
